@@ -1,0 +1,141 @@
+/*
+ * mx.h - C ABI of the inline-quantized A4W4 MXFP4 GEMM library for MI355X (gfx950).
+ *
+ * The operation ("[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", Summary and
+ * Implementation): BF16 activations A[M,K] are quantized inside the GEMM to MXFP4
+ * (E2M1 elements, one E8M0 scale per 32 consecutive K) and multiplied against a
+ * weight W[N,K] that was quantized to MXFP4 and preshuffled once; the product is
+ * accumulated in FP32 and written as BF16 C[M,N]. Scope (same page, Scope): gfx950
+ * only, N divisible by 256, K divisible by 128; rows of C at or beyond M are never
+ * read or written (same page, Implementation: M-tail masking).
+ *
+ * Quantization rule (all entry points): for each 32-element block along K, the scale
+ * byte is s = max(E - 2, 0) where E is the exponent field of the block's largest
+ * magnitude (equivalently e = floor(log2 amax) - 2 clamped to [-127, 127], s = e + 127;
+ * an all-zero block gets 0); each element x becomes the E2M1 code nearest to
+ * x * 2^-e, ties to the even code, magnitudes >= 6 saturating to 6, with the sign bit
+ * of x kept (so -0.0 encodes as 0x8).
+ *
+ * Conventions shared by every entry point:
+ *  - All buffer pointers are device pointers, caller-allocated and caller-owned, and
+ *    16-byte aligned. The library allocates no device memory and keeps no per-call state.
+ *  - Matrices are dense row-major. bf16 values are raw 16-bit patterns.
+ *  - Argument errors are returned synchronously before any HIP call is made.
+ *  - Work is enqueued on `stream` (NULL = the default stream); no entry point
+ *    synchronizes the host. Faults inside a kernel surface at the caller's next sync.
+ *  - Inputs must be finite; NaN/Inf inputs give unspecified (but in-bounds) results.
+ *  - Output is bitwise reproducible for a given (M, N, K), device and library build.
+ *  - Entry points are thread-safe.
+ */
+#ifndef MX_H_
+#define MX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,      /* a required pointer is NULL */
+  MX_ERR_SHAPE = 2,     /* a size is negative or breaks a divisibility rule */
+  MX_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  MX_ERR_DEVICE = 4,    /* the current device is not gfx950 */
+  MX_ERR_WORKSPACE = 5, /* a required workspace is missing or too small */
+  MX_ERR_HIP = 6        /* a HIP runtime call or kernel launch failed */
+} mx_status;
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* mx_status_string(mx_status s);
+
+/* Version of the prepared-weight layout; a blob is only valid for the version that wrote it. */
+int mx_prepared_layout_version(void);
+
+/*
+ * Size in bytes of a prepared MXFP4 weight of shape [N, K]: N*K/2 bytes of packed E2M1
+ * payload followed by the E8M0 scales, N*16*ceil(K/512) bytes (the scales of four
+ * consecutive 128-wide K steps share one 32-bit word per lane; a K that is not a
+ * multiple of 512 pads its last word). For K a multiple of 512 this is N*K*17/32,
+ * e.g. 32,169,984 bytes for 8448 x 7168 ("[gfx950][FlyDSL] Add direct dense A4W4
+ * MXFP4 GEMM", Model validation). Returns 0 when N <= 0, K <= 0, N % 256 or K % 128.
+ */
+size_t mx_prepared_weight_bytes(int64_t N, int64_t K);
+
+/*
+ * One-time weight preparation ("prepare_gemm_a4w4_weight" of the page above,
+ * Implementation: one-time packed E2M1 weight and E8M0 scale preshuffle).
+ * w_bf16: [N, K] bf16 row-major (read only).
+ * w_prep: mx_prepared_weight_bytes(N, K) bytes, written completely (opaque layout).
+ * Requires N % 256 == 0, K % 128 == 0. Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN,
+ * MX_ERR_DEVICE, MX_ERR_HIP.
+ */
+mx_status mx_prepare_weight(const void* w_bf16, int64_t N, int64_t K, void* w_prep,
+                            hipStream_t stream);
+
+/*
+ * Test support: the inverse of the preshuffle. Writes the canonical MXFP4 form of a
+ * prepared weight: w_fp4 [N, K/2] (element at even k in the low nibble) and
+ * w_scale [N, K/32] (one E8M0 byte per 32-block). Same shape rules and errors as
+ * mx_prepare_weight.
+ */
+mx_status mx_unprepare_weight(const void* w_prep, int64_t N, int64_t K, void* w_fp4,
+                              void* w_scale, hipStream_t stream);
+
+/*
+ * Standalone activation quantizer: the same rule as the GEMM's inline quantization,
+ * written out in canonical layout ("[gfx1250] Fuse A4W4 stage1 FP4 quantization",
+ * Summary: the standalone quant path).
+ * a_bf16: [M, K] bf16. a_fp4: [M, K/2] bytes (low nibble = even k). a_scale: [M, K/32]
+ * bytes. Requires M >= 0, K > 0, K % 32 == 0. M == 0 is a no-op returning MX_OK.
+ */
+mx_status mx_quant_act(const void* a_bf16, int64_t M, int64_t K, void* a_fp4, void* a_scale,
+                       hipStream_t stream);
+
+/*
+ * Workspace the dense GEMM can use for a split-K reduction at this shape. It is
+ * always optional: with a NULL or smaller workspace the library picks a
+ * configuration that needs none.
+ */
+size_t mx_a4w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * The dense A4W4 GEMM ("flydsl_gemm_a4w4" of "[gfx950][FlyDSL] Add direct dense A4W4
+ * MXFP4 GEMM", Summary and Implementation): C = Q(A) * Q(W)^T with Q the MXFP4
+ * quantization above; A is quantized inside the kernel, never written to memory.
+ * a_bf16: [M, K] bf16. w_prep: prepared weight of shape [N, K]. c_bf16: [M, N] bf16,
+ * rows < M written with the FP32 sum rounded to nearest even. Requires M >= 0,
+ * N % 256 == 0, K % 128 == 0. M == 0 is a no-op. workspace may be NULL.
+ */
+mx_status mx_a4w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int64_t M,
+                       int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * Grouped MoE GEMM1 (expert-segmented dense GEMM, "[HIP] [CK] [FlyDSL] [Kernel] Extend
+ * MXFP4 GEMM1 replacement to A4W4", Summary; shape of "[gfx1250] Fuse A4W4 stage1 FP4
+ * quantization", Performance). Output row r (expert-sorted order) is
+ * Q(A[row_token[r]]) * Q(W_e)^T for the expert e with
+ * expert_offsets[e] <= r < expert_offsets[e+1].
+ * a_bf16: [T, K] bf16. row_token: [R_max] int32 device array; entries below R are token
+ * indices in [0, T) (an index outside that range reads as an all-zero row).
+ * expert_offsets: [E+1] int32 device array, non-decreasing, expert_offsets[0] == 0,
+ * expert_offsets[E] == R <= R_max (segments are clamped to [0, R_max]).
+ * w_prep_stacked: E prepared weights of shape [N, K],
+ * expert e at byte offset e * mx_prepared_weight_bytes(N, K) (64-bit addressing).
+ * c_bf16: [R_max, N] bf16; rows >= R are untouched. rows_hint: the expected rows per
+ * active expert (only a tiling hint; any value >= 1 is correct).
+ * Requires E >= 1, T >= 0, R_max >= 0, N % 256 == 0, K % 128 == 0.
+ */
+mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token,
+                               const int32_t* expert_offsets, int64_t E, int64_t R_max,
+                               const void* w_prep_stacked, void* c_bf16, int64_t T, int64_t N,
+                               int64_t K, int64_t rows_hint, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_H_ */

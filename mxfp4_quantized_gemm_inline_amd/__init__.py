@@ -1,0 +1,178 @@
+"""Inline-quantized A4W4 MXFP4 GEMM for MI355X (gfx950).
+
+A thin Python binding over the C ABI in ``include/mx.h`` (``libmxgemm.so``, built
+in-tree by ``python -m mxfp4_quantized_gemm_inline_amd.build``). Every function here
+only marshals arguments: torch supplies device memory and the current HIP stream, and
+all computation runs in the library's HIP kernels. There is no fallback: if the library
+is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxgemm.so")
+
+# Symbols declared in include/mx.h, with ctypes signatures.
+_c_i64, _c_sz, _vp, _c_int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+SIGNATURES = {
+    "mx_status_string": (ctypes.c_char_p, [_c_int]),
+    "mx_prepared_layout_version": (_c_int, []),
+    "mx_prepared_weight_bytes": (_c_sz, [_c_i64, _c_i64]),
+    "mx_prepare_weight": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp]),
+    "mx_unprepare_weight": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "mx_quant_act": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "mx_a4w4_gemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64]),
+    "mx_a4w4_gemm": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_sz, _vp]),
+    "mx_a4w4_gemm_grouped": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _c_i64,
+                                      _c_i64, _c_i64, _vp]),
+}
+
+MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE, MX_ERR_WORKSPACE, MX_ERR_HIP = range(7)
+
+_lib = None
+
+
+class MxError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with "
+                              "`python -m mxfp4_quantized_gemm_inline_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mx_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != MX_OK:
+        raise MxError(status, what)
+
+
+# ----------------------------------------------------------------------------- torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def mx_prepared_layout_version() -> int:
+    return int(lib().mx_prepared_layout_version())
+
+
+def mx_prepared_weight_bytes(N: int, K: int) -> int:
+    return int(lib().mx_prepared_weight_bytes(int(N), int(K)))
+
+
+def mx_a4w4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().mx_a4w4_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def mx_prepare_weight(w_bf16, out=None, stream=None):
+    """W [N, K] bf16 -> opaque prepared MXFP4 blob (uint8, mx_prepared_weight_bytes(N, K))."""
+    torch = _torch()
+    N, K = w_bf16.shape
+    nbytes = mx_prepared_weight_bytes(N, K)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w_bf16.device)
+    _check(lib().mx_prepare_weight(_dev(w_bf16, torch.bfloat16, "w_bf16"), N, K,
+                                   _dev(out, torch.uint8, "w_prep"), _stream_ptr(stream)),
+           "mx_prepare_weight")
+    return out
+
+
+def mx_unprepare_weight(w_prep, N: int, K: int, stream=None):
+    """Prepared blob -> canonical (payload uint8 [N, K/2], scales uint8 [N, K/32])."""
+    torch = _torch()
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=w_prep.device)
+    s = torch.empty((N, K // 32), dtype=torch.uint8, device=w_prep.device)
+    _check(lib().mx_unprepare_weight(_dev(w_prep, torch.uint8, "w_prep"), N, K,
+                                     _dev(q, None, "w_fp4"), _dev(s, None, "w_scale"),
+                                     _stream_ptr(stream)), "mx_unprepare_weight")
+    return q, s
+
+
+def mx_quant_act(a_bf16, q_out=None, s_out=None, stream=None):
+    """A [M, K] bf16 -> (payload uint8 [M, K/2], scales uint8 [M, K/32]), canonical layout."""
+    torch = _torch()
+    M, K = a_bf16.shape
+    q = q_out if q_out is not None else torch.empty((M, K // 2), dtype=torch.uint8, device=a_bf16.device)
+    s = s_out if s_out is not None else torch.empty((M, K // 32), dtype=torch.uint8, device=a_bf16.device)
+    if M == 0:
+        return q, s
+    _check(lib().mx_quant_act(_dev(a_bf16, torch.bfloat16, "a_bf16"), M, K, _dev(q, torch.uint8, "a_fp4"),
+                              _dev(s, torch.uint8, "a_scale"), _stream_ptr(stream)), "mx_quant_act")
+    return q, s
+
+
+def mx_a4w4_gemm(a_bf16, w_prep, N: int, out=None, workspace=None, stream=None):
+    """C [M, N] bf16 = Q(A) Q(W)^T with A [M, K] bf16 and a prepared weight of shape [N, K]."""
+    torch = _torch()
+    M, K = a_bf16.shape
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_bf16.device)
+    if M == 0:
+        return c
+    ws_ptr, ws_bytes = (None, 0)
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
+    _check(lib().mx_a4w4_gemm(_dev(a_bf16, torch.bfloat16, "a_bf16"), _dev(w_prep, torch.uint8, "w_prep"),
+                              _dev(c, torch.bfloat16, "c_bf16"), M, int(N), K, ws_ptr, ws_bytes,
+                              _stream_ptr(stream)), "mx_a4w4_gemm")
+    return c
+
+
+def mx_a4w4_gemm_grouped(a_bf16, row_token, expert_offsets, E: int, R_max: int, w_prep_stacked,
+                         N: int, rows_hint: int = 1, out=None, stream=None):
+    """Grouped GEMM1: C [R_max, N] bf16, rows in expert-sorted order (rows >= R untouched)."""
+    torch = _torch()
+    T, K = a_bf16.shape
+    c = out if out is not None else torch.empty((R_max, N), dtype=torch.bfloat16, device=a_bf16.device)
+    _check(lib().mx_a4w4_gemm_grouped(
+        _dev(a_bf16, torch.bfloat16, "a_bf16") if T > 0 else None,
+        _dev(row_token, torch.int32, "row_token") if R_max > 0 else None,
+        _dev(expert_offsets, torch.int32, "expert_offsets"), int(E), int(R_max),
+        _dev(w_prep_stacked, torch.uint8, "w_prep_stacked"), _dev(c, torch.bfloat16, "c_bf16") if R_max > 0 else None,
+        T, int(N), K, int(rows_hint), _stream_ptr(stream)), "mx_a4w4_gemm_grouped")
+    return c
+
+
+__all__ = [
+    "LIB_PATH", "MxError", "lib", "status_string", "mx_prepared_layout_version",
+    "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
+    "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
+]

@@ -1,0 +1,139 @@
+// mx_device.h - device-side building blocks for gfx950: the MXFP4 block quantizer,
+// the prepared-weight layout, and the block-scaled FP4 MFMA wrapper.
+//
+// MXFP4 (E2M1 elements, one E8M0 scale per 32 elements along K) as used by
+// "[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", Summary. The block exponent is
+// floor(log2 amax) - 2 clamped to [-127, 127] (OCP MX v1.0 conversion with the E2M1
+// maximum exponent 2); elements round to nearest even and saturate at 6.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 32;      // elements per E8M0 scale
+constexpr int kStepK = 128;     // K covered by one 16x16x128 MFMA
+constexpr int kFragBytes = 16;  // one lane's share of an MFMA operand: one 32-block
+constexpr int kLayoutVersion = 1;
+
+// ------------------------------------------------------------------ prepared weight layout
+//
+// Payload: for column group g (16 columns n = 16g..16g+15) and K step t (k = 128t..128t+127)
+// one 1 KiB tile; lane l = (n % 16) + 16 * ((k % 128) / 32) owns bytes [16l, 16l+16), which
+// are the 32-block (n, kb = 4t + l/16) in canonical order (element at even k in the low
+// nibble). This is exactly the operand layout of the 16x16x128 FP4 MFMA, so one
+// global_load_dwordx4 per lane fetches a whole operand and a wave's load is 1 KiB contiguous.
+// Tiles are ordered [g][t]: a column group's whole K range is contiguous.
+//
+// Scales: after the payload, for column group g and step quad t4 (steps 4t4..4t4+3) one
+// 32-bit word per lane whose byte j is the E8M0 scale of (n, kb = 4(4t4 + j) + l/16); the
+// byte index j is the MFMA's scale op_sel. A K that is not a multiple of 512 pads the last
+// word with zero bytes (ceil-sized scale region).
+__host__ __device__ inline int steps_of(int K) { return K / kStepK; }
+__host__ __device__ inline int quads_of(int K) { return (K / kStepK + 3) / 4; }
+__host__ __device__ inline size_t payload_bytes(int64_t N, int64_t K) { return (size_t)N * (size_t)K / 2; }
+__host__ __device__ inline size_t scale_region_bytes(int64_t N, int64_t K) {
+  return (size_t)(N / 16) * (size_t)quads_of((int)K) * 256;
+}
+__host__ __device__ inline size_t wp_payload_off(int g, int t, int lane, int T) {
+  return (((size_t)g * T + t) * 64 + lane) * 16;
+}
+__host__ __device__ inline size_t wp_scale_off(int g, int t4, int lane, int T4) {
+  return (((size_t)g * T4 + t4) * 64 + lane) * 4;
+}
+
+// ------------------------------------------------------------------ bf16 helpers
+
+// FP32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  uint2 r;
+  r.x = f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+  r.y = f32_to_bf16_rne(c) | (f32_to_bf16_rne(d) << 16);
+  return r;
+}
+
+// ------------------------------------------------------------------ the block quantizer
+
+// E8M0 scale byte of a 32-element bf16 block held as 16 words of bf16 pairs.
+// For a finite block, floor(log2 amax) is (E - 127) with E the largest exponent field, so
+// s = e + 127 = max(E - 2, 0); subnormal and zero blocks (E = 0) give 0.
+__device__ __forceinline__ uint32_t block_scale_byte(const uint32_t (&x)[16]) {
+  u16x2 m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u16x2 a = __builtin_bit_cast(u16x2, x[2 * i] & 0x7F807F80u);
+    u16x2 b = __builtin_bit_cast(u16x2, x[2 * i + 1] & 0x7F807F80u);
+    m[i] = __builtin_elementwise_max(a, b);
+  }
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) m[i] = __builtin_elementwise_max(m[i], m[i + w]);
+  uint32_t hi = m[0].x > m[0].y ? m[0].x : m[0].y;
+  uint32_t E = hi >> 7;
+  return E > 2u ? E - 2u : 0u;
+}
+
+// Quantize one block: q[j] byte b holds elements (8j + 2b) (low nibble) and (8j + 2b + 1).
+// The hardware conversion divides by the scale operand, rounds to nearest even, saturates
+// and keeps the sign of zero; a scale byte of 0 is passed as the fp32 value 2^-127.
+__device__ __forceinline__ uint32_t quant_block(const uint32_t (&x)[16], uint32_t (&q)[4]) {
+  const uint32_t s = block_scale_byte(x);
+  const float sc = __builtin_bit_cast(float, s ? (s << 23) : 0x00400000u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x[4 * j + 0]), sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x[4 * j + 1]), sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x[4 * j + 2]), sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x[4 * j + 3]), sc, 3);
+    q[j] = r;
+  }
+  return s;
+}
+
+// Load one 32-element bf16 block (64 bytes, 16-byte aligned) into 16 words.
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ p, uint32_t (&x)[16]) {
+  const uint4* v = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 u = v[i];
+    x[4 * i + 0] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+  }
+}
+
+// 16-byte streaming load (non-temporal: data read once, e.g. the prepared weight).
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void zero_block(uint32_t (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 0u;
+}
+
+// ------------------------------------------------------------------ MFMA
+
+// acc += (a * 2^(sa-127)) (16 x 128 FP4, rows) times (b * 2^(sb-127)) (128 x 16 FP4, cols).
+// Lane l supplies row/col l % 16, K block l / 16 of each operand and the scale byte for it
+// in byte 0 of sa / sb. acc lane l, element r is C[row 4*(l/16) + r][col l % 16].
+__device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f acc, uint32_t sa, uint32_t sb) {
+  v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+}  // namespace mx

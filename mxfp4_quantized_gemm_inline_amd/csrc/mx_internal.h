@@ -1,0 +1,19 @@
+// mx_internal.h - launchers shared between the C ABI (mx_api.cpp) and the kernels
+// (mx_kernels.hip). Shapes are validated by the caller before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace mx {
+
+hipError_t launch_quant_act(const void* a, int64_t M, int64_t K, void* q, void* s, hipStream_t st);
+hipError_t launch_prepare(const void* w, int64_t N, int64_t K, void* wp, hipStream_t st);
+hipError_t launch_unprepare(const void* wp, int64_t N, int64_t K, void* q, void* s, hipStream_t st);
+hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K,
+                       hipStream_t st);
+hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const int32_t* offsets,
+                               int64_t E, int64_t R_max, const void* wp, void* c, int64_t T,
+                               int64_t N, int64_t K, int64_t rows_hint, hipStream_t st);
+
+}  // namespace mx

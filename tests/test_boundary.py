@@ -1,0 +1,102 @@
+"""The C ABI boundary on the host: the library loads, exports every function that
+include/mx.h declares, sizes its buffers as documented, and rejects bad arguments
+synchronously (before any HIP call, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_quantized_gemm_inline_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mx.LIB_PATH), reason="libmxgemm.so not built")
+
+A = 0x10000   # fake, 16-byte aligned addresses: every call below returns before using them
+B = 0x20000
+Cp = 0x30000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = mx.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mx.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    for s in range(7):
+        assert mx.status_string(s).startswith("MX_")
+    assert "UNKNOWN" in mx.status_string(99)
+
+
+def test_prepared_bytes():
+    assert mx.mx_prepared_weight_bytes(8448, 7168) == 32_169_984      # the page's figure
+    assert mx.mx_prepared_weight_bytes(7168, 768) == 7168 * 384 + 7168 * 16 * 2
+    assert mx.mx_prepared_weight_bytes(7168, 4224) == 7168 * 2112 + 7168 * 16 * 9  # ceil(33/4) words
+    assert mx.mx_prepared_weight_bytes(1536, 3584) == 2_924_544
+    for n, k in [(0, 256), (256, 0), (100, 256), (256, 100), (-256, 256), (256, 64)]:
+        assert mx.mx_prepared_weight_bytes(n, k) == 0
+    assert mx.mx_prepared_layout_version() == 1
+    assert mx.mx_a4w4_gemm_workspace_bytes(1, 7168, 768) >= 0
+
+
+def test_gemm_argument_errors():
+    f = mx.lib().mx_a4w4_gemm
+    assert f(A, B, Cp, 16, 100, 256, None, 0, None) == mx.MX_ERR_SHAPE
+    assert f(A, B, Cp, 16, 256, 100, None, 0, None) == mx.MX_ERR_SHAPE
+    assert f(A, B, Cp, -1, 256, 256, None, 0, None) == mx.MX_ERR_SHAPE
+    assert f(A, B, Cp, 0, 256, 256, None, 0, None) == mx.MX_OK          # M = 0 is a no-op
+    assert f(None, B, Cp, 16, 256, 256, None, 0, None) == mx.MX_ERR_NULL
+    assert f(A, None, Cp, 16, 256, 256, None, 0, None) == mx.MX_ERR_NULL
+    assert f(A, B, None, 16, 256, 256, None, 0, None) == mx.MX_ERR_NULL
+    assert f(MIS, B, Cp, 16, 256, 256, None, 0, None) == mx.MX_ERR_ALIGN
+    assert f(A, MIS, Cp, 16, 256, 256, None, 0, None) == mx.MX_ERR_ALIGN
+    assert f(A, B, MIS, 16, 256, 256, None, 0, None) == mx.MX_ERR_ALIGN
+
+
+def test_quant_and_prepare_argument_errors():
+    q = mx.lib().mx_quant_act
+    assert q(A, 4, 33, B, Cp, None) == mx.MX_ERR_SHAPE
+    assert q(A, -1, 64, B, Cp, None) == mx.MX_ERR_SHAPE
+    assert q(A, 0, 64, B, Cp, None) == mx.MX_OK
+    assert q(None, 4, 64, B, Cp, None) == mx.MX_ERR_NULL
+    assert q(A, 4, 64, MIS, Cp, None) == mx.MX_ERR_ALIGN
+    p = mx.lib().mx_prepare_weight
+    assert p(None, 256, 256, B, None) == mx.MX_ERR_NULL
+    assert p(A, 255, 256, B, None) == mx.MX_ERR_SHAPE
+    assert p(A, 256, 256, MIS, None) == mx.MX_ERR_ALIGN
+    u = mx.lib().mx_unprepare_weight
+    assert u(A, 256, 128 + 64, B, Cp, None) == mx.MX_ERR_SHAPE
+    assert u(A, 256, 256, None, Cp, None) == mx.MX_ERR_NULL
+
+
+def test_grouped_argument_errors():
+    g = mx.lib().mx_a4w4_gemm_grouped
+    #       a  rt  offs E   Rmax w   c   T   N    K    hint stream
+    assert g(A, B, Cp, 0, 16, A, B, 1, 256, 256, 1, None) == mx.MX_ERR_SHAPE
+    assert g(A, B, Cp, 4, 16, A, B, 1, 100, 256, 1, None) == mx.MX_ERR_SHAPE
+    assert g(A, B, Cp, 4, -1, A, B, 1, 256, 256, 1, None) == mx.MX_ERR_SHAPE
+    assert g(A, B, None, 4, 16, A, B, 1, 256, 256, 1, None) == mx.MX_ERR_NULL
+    assert g(A, None, Cp, 4, 16, A, B, 1, 256, 256, 1, None) == mx.MX_ERR_NULL
+    assert g(None, B, Cp, 4, 16, A, B, 1, 256, 256, 1, None) == mx.MX_ERR_NULL
+    assert g(A, B, Cp, 4, 16, MIS, B, 1, 256, 256, 1, None) == mx.MX_ERR_ALIGN
+    assert g(A, B, Cp, 4, 0, A, B, 1, 256, 256, 1, None) == mx.MX_OK     # no rows: no-op
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mx, "_lib", None)
+    monkeypatch.setattr(mx, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        mx.lib()

@@ -1,0 +1,98 @@
+"""GPU parity of the grouped MoE GEMM1 (E = 896 experts, top-16 uniform routing,
+K = 3584, N = 1536) against the oracle, plus malformed-table handling."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import mx_oracle as O
+
+from gpu_util import check_gemm, dev_bf16, host_bits, lib_or_fail, sample_rows, torch_or_skip
+
+pytestmark = pytest.mark.gpu
+
+_stack = {"experts": set(), "buf": None}
+
+
+def stacked_weights(experts):
+    """Stacked prepared weights of all E experts; only the listed ones are filled
+    (the others are never read by a launch whose table leaves them empty)."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    per = mx.mx_prepared_weight_bytes(W.MOE_N, W.MOE_K)
+    if _stack["buf"] is None:
+        _stack["buf"] = torch.zeros(W.MOE_E * per, dtype=torch.uint8, device="cuda")
+    need = sorted(set(int(e) for e in experts) - _stack["experts"])
+    for e, w in W.moe_expert_weights(need):
+        mx.mx_prepare_weight(dev_bf16(w), out=_stack["buf"][e * per:(e + 1) * per])
+        _stack["experts"].add(e)
+    torch.cuda.synchronize()
+    return _stack["buf"]
+
+
+def rows_hint(T):
+    R = W.MOE_TOPK * T
+    return max(1, -(-R // min(W.MOE_E, R)))
+
+
+@pytest.mark.parametrize("T", list(W.MOE_TOKENS))
+def test_grouped_matches_oracle(T):
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    a = W.moe_activation(T)
+    ids, offs, row_token = W.moe_routing(T)
+    active = np.flatnonzero(np.diff(offs) > 0)
+    wst = stacked_weights(active)
+    R = int(offs[-1])
+    out = torch.full((R + 3, W.MOE_N), 5.0, dtype=torch.bfloat16, device="cuda")
+    mx.mx_a4w4_gemm_grouped(dev_bf16(a), torch.from_numpy(row_token).cuda(), torch.from_numpy(offs).cuda(),
+                            W.MOE_E, R, wst, W.MOE_N, rows_hint=rows_hint(T), out=out[:R])
+    c = host_bits(out)
+    torch.cuda.synchronize()
+    assert np.all(c[R:] == host_bits(torch.full((1,), 5.0, dtype=torch.bfloat16))[0])
+    rows = sample_rows(R, n=64, seed=T)
+    exact = O.grouped_gemm_ref(a, row_token, offs, W.moe_expert_weight, rows=rows)
+    check_gemm(c[rows], exact, what=f"grouped T={T}")
+
+
+@pytest.mark.parametrize("hint", [1, 20, 64])
+def test_grouped_tiling_hint_only_changes_tiling(hint):
+    """The rows-per-expert hint selects the tiling; every choice meets the tolerance."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    T = 256
+    a = W.moe_activation(T)
+    _, offs, row_token = W.moe_routing(T)
+    wst = stacked_weights(np.flatnonzero(np.diff(offs) > 0))
+    R = int(offs[-1])
+    c = host_bits(mx.mx_a4w4_gemm_grouped(dev_bf16(a), torch.from_numpy(row_token).cuda(),
+                                          torch.from_numpy(offs).cuda(), W.MOE_E, R, wst, W.MOE_N,
+                                          rows_hint=hint))
+    torch.cuda.synchronize()
+    rows = sample_rows(R, n=32, seed=hint)
+    exact = O.grouped_gemm_ref(a, row_token, offs, W.moe_expert_weight, rows=rows)
+    check_gemm(c[rows], exact, what=f"grouped hint={hint}")
+
+
+def test_grouped_malformed_table_is_clamped():
+    """Out-of-range tokens read as zero rows; segments are clamped to [0, R_max]."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    E, N, K, T = 4, 256, 256, 3
+    rng = np.random.default_rng(0)
+    a = W.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    ws = [W.dense_weight(N, K, seed=50 + e) for e in range(E)]
+    wst = torch.cat([mx.mx_prepare_weight(dev_bf16(w)) for w in ws])
+    offs = np.array([0, 2, 2, 5, 9], dtype=np.int32)       # last segment runs past R_max = 6
+    row_token = np.array([0, 2, 1, 7, -1, 2], dtype=np.int32)  # 7 and -1 are out of range
+    R_max = 6
+    c = host_bits(mx.mx_a4w4_gemm_grouped(dev_bf16(a), torch.from_numpy(row_token).cuda(),
+                                          torch.from_numpy(offs).cuda(), E, R_max, wst, N, rows_hint=2))
+    torch.cuda.synchronize()
+    expert_of = [0, 0, 2, 2, 2, 3]
+    for r in range(R_max):
+        tok = int(row_token[r])
+        if 0 <= tok < T:
+            want = O.gemm_ref(a[tok:tok + 1], ws[expert_of[r]])[0]
+            check_gemm(c[r:r + 1], want[None, :], what=f"row {r}")
+        else:
+            assert np.all(O.bf16_to_f64(c[r]) == 0.0), r
