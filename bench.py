@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the inline-quantized A4W4 MXFP4 GEMM on one MI355X.
+
+Headline workload (one "step"): the dense GEMM N=7168, K=768 at every M of the
+microbenchmark sweep (1, 8, 32, 128, 512, 2048), one call per M, each with bf16
+activations quantized inside the kernel against a prepared MXFP4 weight; weight
+preparation is outside the timed region, as in "[gfx950][FlyDSL] Add direct dense A4W4
+MXFP4 GEMM", Kernel microbenchmark. Inputs are synthetic (seeded, see workloads/).
+
+Timing: every timed region is a HIP graph replay bracketed by HIP events on the
+stream the kernels run on. Buffers rotate over R distinct (A, prepared W, C) sets so
+the working set exceeds the 256 MB Infinity Cache ("cold"); single-set ("warm") times
+are reported as context. Per-point times are averages per launch over the replay.
+
+Output: one JSON line (rank 0, N=1) with the headline step, the roofline of the
+dominant kernel, the CPU oracle baseline, and the full sweep (all dense points and
+the grouped MoE GEMM1 points) under "sweep".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "A4W4 GEMM us + %HBM roofline (M<=32) / %MXFP4 MFMA peak (M>=512)"
+HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
+MFMA_FP4_PEAK = 10.1e15      # flop/s, MI355X dense MXFP4
+MALL_BYTES = 256 << 20       # Infinity Cache
+ROTATE_TARGET = 1 << 30      # bytes touched per rotation cycle (4x the Infinity Cache)
+HEADLINE = "n7168_k768"
+# The pages' direct-kernel median times for this workload ("[gfx950][FlyDSL] Add direct
+# dense A4W4 MXFP4 GEMM", Kernel microbenchmark table), summed over the M sweep.
+PAGE_US = {("n7168_k768", 1): 12.580, ("n7168_k768", 8): 11.921, ("n7168_k768", 32): 12.120,
+           ("n7168_k768", 128): 12.380, ("n7168_k768", 512): 15.520, ("n7168_k768", 2048): 31.700,
+           ("n7168_k4224", 1): 15.960, ("n7168_k4224", 8): 23.041, ("n7168_k4224", 32): 23.520,
+           ("n7168_k4224", 128): 23.280, ("n7168_k4224", 512): 50.041, ("n7168_k4224", 2048): 107.041,
+           ("n1536_k7168", 1): 18.420, ("n1536_k7168", 8): 23.320, ("n1536_k7168", 32): 26.181,
+           ("n1536_k7168", 128): 28.300, ("n1536_k7168", 512): 29.621, ("n1536_k7168", 2048): 65.081,
+           ("n8448_k7168", 1): 23.201, ("n8448_k7168", 8): 26.940, ("n8448_k7168", 32): 30.240,
+           ("n8448_k7168", 128): 60.121, ("n8448_k7168", 512): 89.480, ("n8448_k7168", 2048): 237.863}
+
+
+def algo_bytes(M, N, K):
+    """Prepared MXFP4 weight (N*K*17/32) + bf16 activations + bf16 output."""
+    return N * K * 17 // 32 + 2 * M * K + 2 * M * N
+
+
+def algo_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- GPU timing
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+
+    def graph(self, launches):
+        """Capture the callables (each enqueues kernels on the current stream) in one graph."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            launches[0]()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in launches:
+                f()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_ms(self, g, reps=1):
+        torch = self.torch
+        g.replay()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+
+def dev_bf16(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+class DensePoint:
+    """R rotating buffer sets for one (N, K, M) point."""
+
+    def __init__(self, torch, mx, wp, a_bits, N, K, M, rotate=True):
+        self.N, self.K, self.M = N, K, M
+        per = wp.numel() + 2 * M * K + 2 * M * N
+        self.R = max(1, min(256, math.ceil(ROTATE_TARGET / per))) if rotate else 1
+        a = dev_bf16(torch, a_bits)
+        self.sets = []
+        for r in range(self.R):
+            w_r = wp if r == 0 else wp.clone()
+            a_r = a if r == 0 else a.clone()
+            c_r = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            self.sets.append((a_r, w_r, c_r))
+        self.mx = mx
+
+    def launch(self, i):
+        a, w, c = self.sets[i % self.R]
+        return lambda: self.mx.mx_a4w4_gemm(a, w, self.N, out=c)
+
+
+def time_point(timer, pt, launches=200):
+    g = timer.graph([pt.launch(i) for i in range(launches)])
+    ms = timer.replay_ms(g, reps=3)
+    del g
+    return ms * 1e3 / launches  # us per launch
+
+
+def point_record(name, N, K, M, us_cold, us_warm, kernel=None):
+    B, F = algo_bytes(M, N, K), algo_flops(M, N, K)
+    t_hbm, t_mfma = B / HBM_PEAK * 1e6, F / MFMA_FP4_PEAK * 1e6
+    rec = {
+        "workload": name, "N": N, "K": K, "M": M,
+        "us": round(us_cold, 3), "us_warm": round(us_warm, 3),
+        "tflops": round(F / us_cold / 1e6, 2), "gbps": round(B / us_cold / 1e3, 1),
+        "frac_hbm": round(t_hbm / us_cold, 4), "frac_mfma": round(t_mfma / us_cold, 4),
+        "binds": "hbm" if t_hbm >= t_mfma else "mfma",
+        "frac_binding": round(max(t_hbm, t_mfma) / us_cold, 4),
+    }
+    if (name, M) in PAGE_US:
+        rec["page_us"] = PAGE_US[(name, M)]
+    if kernel:
+        rec["kernel"] = kernel
+    return rec
+
+
+def kernel_name(M, N, K):
+    """Which kernel family the library launches for this shape (mirrors its selection)."""
+    if M <= 32 and M * (K // 2 + 16) + M * (K // 32) <= 160 * 1024:
+        return "k_gemm_skinny"
+    return "k_gemm_tile"
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(a_by_m, w_bits, ms):
+    """The oracle as it stands on the host cores: one whole step of the headline workload."""
+    from oracle import mx_oracle as O
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 1) for p in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    for m in ms:
+        O.gemm_ref(a_by_m[m], w_bits)
+    dt = time.perf_counter() - t0
+    return {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": threads or cores,
+            "kind": "oracle",
+            "sample": f"one full step (N=7168 K=768, M in {list(ms)}: quantize A and W, decode, "
+                      f"float64 matmul), {cores} host cores visible, BLAS threads {threads}; "
+                      f"quantization is single-threaded numpy"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-sweep", action="store_true", help="headline step only")
+    ap.add_argument("--no-grouped", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--launches", type=int, default=200, help="launches per sweep point")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_quantized_gemm_inline_amd as mx
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    mx.lib()  # fail loudly if the HIP library is missing
+    timer = Timer(torch)
+
+    # ---------------- headline: N=7168 K=768 M sweep, one call per M per step
+    N, K, ms, structure = W.DENSE_CONFIGS[HEADLINE]
+    w_bits = W.dense_weight(N, K)
+    a_all = W.dense_activation(max(ms), K, structure)
+    a_by_m = {m: a_all[:m] for m in ms}
+    wp = mx.mx_prepare_weight(dev_bf16(torch, w_bits))
+    torch.cuda.synchronize()
+    log(f"headline {HEADLINE}: prepared weight {wp.numel()} B")
+
+    # rotating sets for the whole step
+    per_step = wp.numel() + sum(2 * m * K + 2 * m * N for m in ms)
+    R = max(1, min(256, math.ceil(ROTATE_TARGET / per_step)))
+    sets = []
+    for r in range(R):
+        w_r = wp if r == 0 else wp.clone()
+        a_r = {m: dev_bf16(torch, a_by_m[m]) for m in ms}
+        c_r = {m: torch.empty((m, N), dtype=torch.bfloat16, device="cuda") for m in ms}
+        sets.append((w_r, a_r, c_r))
+
+    def step_launches(i):
+        w_r, a_r, c_r = sets[i % R]
+        return [(lambda m=m: mx.mx_a4w4_gemm(a_r[m], w_r, N, out=c_r[m])) for m in ms]
+
+    warm_g = timer.graph([f for i in range(max(1, args.warmup)) for f in step_launches(i)])
+    warm_g.replay()
+    torch.cuda.synchronize()
+    step_g = timer.graph([f for i in range(args.steps) for f in step_launches(i)])
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    step_ms = timer.replay_ms(step_g, reps=1) / args.steps
+    t_wall = time.perf_counter() - t_wall0
+    del step_g, warm_g
+    log(f"headline step: {step_ms * 1e3:.2f} us/step over {args.steps} steps, R={R} buffer sets")
+
+    # per-point detail for the headline workload (cold = rotated, warm = one set)
+    head_points = []
+    for m in ms:
+        cold = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=True)
+        us_c = time_point(timer, cold, args.launches)
+        del cold
+        warm = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=False)
+        us_w = time_point(timer, warm, args.launches)
+        del warm
+        head_points.append(point_record(HEADLINE, N, K, m, us_c, us_w, kernel_name(m, N, K)))
+        log(f"  M={m}: {us_c:.2f} us cold, {us_w:.2f} us warm")
+    dom = max(head_points, key=lambda p: p["us"])
+    Bd = algo_bytes(dom["M"], N, K)
+    Fd = algo_flops(dom["M"], N, K)
+    if dom["binds"] == "hbm":
+        roof = {"bound": "hbm", "achieved": round(Bd / dom["us"] / 1e3, 1), "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": dom["frac_hbm"], "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(Fd / dom["us"] / 1e6, 1), "peak": MFMA_FP4_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": dom["frac_mfma"], "traffic": None}
+    roof["kernel"] = f"{dom['kernel']} (N={N} K={K} M={dom['M']})"
+    roof["algorithmic_bytes"] = Bd
+    roof["algorithmic_flops"] = Fd
+
+    # ---------------- full sweep (context)
+    sweep = {"dense": [], "grouped": []}
+    if not args.no_sweep:
+        for name, (Nn, Kk, mss, st) in W.DENSE_CONFIGS.items():
+            if name in ("smoke_16x256x256", HEADLINE):
+                continue
+            wb = W.dense_weight(Nn, Kk)
+            wpn = mx.mx_prepare_weight(dev_bf16(torch, wb))
+            aa = W.dense_activation(max(mss), Kk, st)
+            for m in mss:
+                cold = DensePoint(torch, mx, wpn, aa[:m], Nn, Kk, m, rotate=True)
+                us_c = time_point(timer, cold, args.launches)
+                del cold
+                warm = DensePoint(torch, mx, wpn, aa[:m], Nn, Kk, m, rotate=False)
+                us_w = time_point(timer, warm, args.launches)
+                del warm
+                sweep["dense"].append(point_record(name, Nn, Kk, m, us_c, us_w, kernel_name(m, Nn, Kk)))
+                log(f"  {name} M={m}: {us_c:.2f} us cold, {us_w:.2f} us warm")
+            del wpn
+            torch.cuda.empty_cache()
+        sweep["dense"] = [*head_points, *sweep["dense"]]
+        if not args.no_grouped:
+            sweep["grouped"] = grouped_sweep(torch, mx, W, timer)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(a_by_m, w_bits, ms)
+        log(f"cpu oracle: {cpu['value']:.0f} us/step")
+
+    page_total = sum(PAGE_US[(HEADLINE, m)] for m in ms)
+    value = step_ms * 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(value / page_total, 4),
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": f"dense A4W4 MXFP4 GEMM N={N} K={K}, one call per M in {list(ms)} per step",
+                   "N": N, "K": K, "M": list(ms), "buffer_sets": R,
+                   "a": "bf16 ~N(0,1), 1% of K channels x20", "w": "bf16 ~N(0,0.02) prepared to MXFP4",
+                   "timing": "HIP graph replay, HIP events; rotating buffer sets > Infinity Cache"},
+        "baseline_note": f"vs_baseline = value / {page_total:.3f} us, the sum of the pages' direct-kernel "
+                         f"medians for this sweep on MI355X (lower is better)",
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "points": head_points,
+        "sweep": sweep,
+        "wall_s_timed": round(t_wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def grouped_sweep(torch, mx, W, timer):
+    """Grouped MoE GEMM1 (E=896, top-16, K=3584, N=1536) at T = 1, 16, 256, 4096."""
+    N, K, E = W.MOE_N, W.MOE_K, W.MOE_E
+    per = mx.mx_prepared_weight_bytes(N, K)
+    stack = torch.empty(E * per, dtype=torch.uint8, device="cuda")
+    t0 = time.perf_counter()
+    for e, w in W.moe_expert_weights(range(E), threads=min(16, os.cpu_count() or 8)):
+        mx.mx_prepare_weight(dev_bf16(torch, w), out=stack[e * per:(e + 1) * per])
+    torch.cuda.synchronize()
+    log(f"grouped: prepared {E} experts in {time.perf_counter() - t0:.1f} s")
+    recs = []
+    for T in W.MOE_TOKENS:
+        a = dev_bf16(torch, W.moe_activation(T))
+        _, offs, row_token = W.moe_routing(T)
+        R = int(offs[-1])
+        active = int((offs[1:] > offs[:-1]).sum())
+        hint = max(1, -(-R // min(E, R)))
+        rt = torch.from_numpy(row_token).cuda()
+        of = torch.from_numpy(offs).cuda()
+        c = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+        n = 20 if T >= 256 else 100
+        g = timer.graph([lambda: mx.mx_a4w4_gemm_grouped(a, rt, of, E, R, stack, N, rows_hint=hint, out=c)] * n)
+        us = timer.replay_ms(g, reps=2) * 1e3 / n
+        del g
+        B = active * per + 2 * T * K + 2 * R * N
+        F = 2 * R * N * K
+        recs.append({"workload": "grouped_moe_gemm1_e896_top16_k3584_n1536", "T": T, "rows": R,
+                     "active_experts": active, "us": round(us, 3),
+                     "tflops": round(F / us / 1e6, 2), "gbps": round(B / us / 1e3, 1),
+                     "frac_hbm": round(B / HBM_PEAK * 1e6 / us, 4),
+                     "frac_mfma": round(F / MFMA_FP4_PEAK * 1e6 / us, 4)})
+        log(f"  grouped T={T}: {us:.2f} us ({active} experts, {R} rows)")
+    del stack
+    torch.cuda.empty_cache()
+    return recs
+
+
+if __name__ == "__main__":
+    main()

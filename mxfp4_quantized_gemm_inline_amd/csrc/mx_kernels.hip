@@ -9,6 +9,8 @@
 // the quantized activations are the "B" operand (16 output rows m as columns), so lane l's
 // accumulator element r is C[m = l % 16][n = 4 * (l / 16) + r]: four consecutive columns of
 // one output row, stored as one 8-byte write.
+#include <atomic>
+
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -508,6 +510,19 @@ namespace {
 constexpr int kSkinnyPD = 16;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU (and per workgroup) on gfx950
 
+// Raise a kernel's dynamic-LDS limit to the full 160 KiB once per device. `done` is the
+// caller's per-kernel bitmask of devices already configured.
+hipError_t ensure_lds_limit(const void* kern, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 size_t skinny_lds_bytes(int M, int K, int MT, int NG, int WK) {
   const size_t act = (size_t)M * (K / 2 + 16) + (size_t)M * (K / kBlock);
   const size_t red = (size_t)WK * NG * MT * 64 * 16;
@@ -517,10 +532,10 @@ size_t skinny_lds_bytes(int M, int K, int MT, int NG, int WK) {
 template <int MT, int NG, int WK>
 hipError_t run_skinny(const void* a, const void* wp, void* c, int M, int N, int K, hipStream_t st) {
   auto kern = k_gemm_skinny<MT, NG, WK, kSkinnyPD>;
+  static std::atomic<uint64_t> configured{0};
   const size_t lds = skinny_lds_bytes(M, K, MT, NG, WK);
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), configured);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)(N / (16 * NG))), dim3(64 * WK), lds, st,
@@ -571,10 +586,10 @@ template <int MT, int NG, int WK>
 hipError_t run_grouped(const void* a, const int32_t* rt, const int32_t* offs, int E, int R_max,
                        const void* wp, void* c, int T, int N, int K, hipStream_t st) {
   auto kern = k_gemm_grouped<MT, NG, WK, kSkinnyPD>;
+  static std::atomic<uint64_t> configured{0};
   const size_t lds = skinny_lds_bytes(16 * MT, K, MT, NG, WK);
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), configured);
     if (e != hipSuccess) return e;
   }
   const int64_t slots = (int64_t)(E < R_max ? E : R_max);
