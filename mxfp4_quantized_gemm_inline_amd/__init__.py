@@ -141,14 +141,22 @@ def mx_quant_act(a_bf16, q_out=None, s_out=None, stream=None):
 
 
 def mx_a4w4_gemm(a_bf16, w_prep, N: int, out=None, workspace=None, stream=None):
-    """C [M, N] bf16 = Q(A) Q(W)^T with A [M, K] bf16 and a prepared weight of shape [N, K]."""
+    """C [M, N] bf16 = Q(A) Q(W)^T with A [M, K] bf16 and a prepared weight of shape [N, K].
+
+    workspace: a device tensor for split-K partials, None to allocate
+    mx_a4w4_gemm_workspace_bytes(M, N, K) bytes through torch, or False to pass none
+    (the library then picks a configuration that needs no workspace).
+    """
     torch = _torch()
     M, K = a_bf16.shape
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_bf16.device)
     if M == 0:
         return c
+    if workspace is None:
+        nbytes = mx_a4w4_gemm_workspace_bytes(M, N, K)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=a_bf16.device) if nbytes else False
     ws_ptr, ws_bytes = (None, 0)
-    if workspace is not None:
+    if workspace is not False:
         ws_ptr, ws_bytes = _dev(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
     _check(lib().mx_a4w4_gemm(_dev(a_bf16, torch.bfloat16, "a_bf16"), _dev(w_prep, torch.uint8, "w_prep"),
                               _dev(c, torch.bfloat16, "c_bf16"), M, int(N), K, ws_ptr, ws_bytes,

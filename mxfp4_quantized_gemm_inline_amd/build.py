@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 # Packed FP32 ops are kept out of device code; no fast-math and no denormal flushing, so
 # bf16 subnormals survive the quantizer.
-HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+HIP_FLAGS = ["-O3", "-std=c++20", f"--offload-arch={ARCH}", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fno-gpu-rdc", "-Wall", "-Wno-unused-function"]
 SOURCES = ["mx_kernels.hip", "mx_api.cpp"]

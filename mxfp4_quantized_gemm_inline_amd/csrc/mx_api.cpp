@@ -93,20 +93,20 @@ mx_status mx_quant_act(const void* a_bf16, int64_t M, int64_t K, void* a_fp4, vo
 }
 
 size_t mx_a4w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N; (void)K;
-  return 0;
+  if (M <= 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return 0;
+  return mx::gemm_workspace_bytes(M, N, K);
 }
 
 mx_status mx_a4w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int64_t M, int64_t N,
                        int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace; (void)workspace_bytes;
   if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
   if (M == 0) return MX_OK;
   if (!a_bf16 || !w_prep || !c_bf16) return MX_ERR_NULL;
   if (!aligned16(a_bf16) || !aligned16(w_prep) || !aligned16(c_bf16)) return MX_ERR_ALIGN;
+  if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
   mx_status d = check_device();
   if (d != MX_OK) return d;
-  return from_hip(mx::launch_gemm(a_bf16, w_prep, c_bf16, M, N, K, stream));
+  return from_hip(mx::launch_gemm(a_bf16, w_prep, c_bf16, M, N, K, workspace, workspace_bytes, stream));
 }
 
 mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token, const int32_t* expert_offsets,

@@ -11,7 +11,8 @@ hipError_t launch_quant_act(const void* a, int64_t M, int64_t K, void* q, void* 
 hipError_t launch_prepare(const void* w, int64_t N, int64_t K, void* wp, hipStream_t st);
 hipError_t launch_unprepare(const void* wp, int64_t N, int64_t K, void* q, void* s, hipStream_t st);
 hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K,
-                       hipStream_t st);
+                       void* workspace, size_t workspace_bytes, hipStream_t st);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const int32_t* offsets,
                                int64_t E, int64_t R_max, const void* wp, void* c, int64_t T,
                                int64_t N, int64_t K, int64_t rows_hint, hipStream_t st);

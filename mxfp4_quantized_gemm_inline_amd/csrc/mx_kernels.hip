@@ -10,6 +10,9 @@
 // accumulator element r is C[m = l % 16][n = 4 * (l / 16) + r]: four consecutive columns of
 // one output row, stored as one 8-byte write.
 #include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <utility>
 
 #include "mx_device.h"
 #include "mx_internal.h"
@@ -81,65 +84,93 @@ __global__ __launch_bounds__(256) void k_unprepare(const uint8_t* __restrict__ W
   s[(size_t)n * KB + kb] = (uint8_t)(sword >> (8 * (t & 3)));
 }
 
-// ====================================================================== small-M GEMM
+// ====================================================================== streaming GEMM (small and mid M)
 //
-// For decode-sized M (<= 16 * MT). A CTA owns NG column groups (16 * NG output columns)
-// and the whole K range; its WK waves split the K steps, each wave streaming its share of
-// the prepared weight straight from HBM into registers (no reuse, so no LDS staging), while
-// its own activation blocks are quantized once into LDS. The wave partial sums are added in
-// LDS in a fixed wave order (deterministic), then rounded to bf16 and stored for rows < M.
+// For M <= 16 * MT. CTA (x, y) owns NG column groups (16 * NG output columns) and the y-th
+// slice of TS K steps; its WK waves split the slice's steps. Each wave streams its share of
+// the prepared weight straight from HBM into registers, PD steps at a time (the weight has
+// no reuse here, so it is not staged in LDS) while it quantizes its own activation blocks
+// (rows < M) into LDS,
+// several blocks per lane in flight. The wave partial sums are added in LDS in a fixed wave
+// order. With one slice the result is rounded to bf16 and stored; with several, each slice
+// writes an FP32 partial tile to the workspace P[slice][M][N] and k_splitk_reduce adds the
+// slices in order (so the result is deterministic).
 //
-// LDS: quantized activations [M][K/2 + 16] (the 16-byte pad staggers rows across banks),
-// then their scales [M][K/32]; reused for the cross-wave reduction.
+// LDS: quantized activations [M][TS * 64 + 16] (the 16-byte pad staggers rows across
+// banks), then their scales [M][4 * TS]; reused for the cross-wave reduction.
+constexpr int kQuantBatch = 4;
+
 template <int MT, int NG, int WK, int PD>
-__global__ __launch_bounds__(64 * WK) void k_gemm_skinny(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restrict__ A,
                                                          const uint8_t* __restrict__ Wp,
-                                                         uint16_t* __restrict__ C, int M, int N,
-                                                         int K) {
+                                                         uint16_t* __restrict__ C,
+                                                         float* __restrict__ P, int M, int N, int K,
+                                                         int TS) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int T = steps_of(K), T4 = quads_of(K), KB = K / kBlock;
-  const int RS = K / 2 + 16;
+  const int T = steps_of(K), T4 = quads_of(K);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g0 = blockIdx.x * NG;
+  const int ks0 = min(T, (int)blockIdx.y * TS), ks1 = min(T, ks0 + TS);
+  const int slice = ks1 - ks0;
+  const int RS = TS * 64 + 16, SB = 4 * TS;
   const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
   uint8_t* aq = smem;
   uint8_t* as = smem + (size_t)M * RS;
 
-  const int per = (T + WK - 1) / WK;
-  const int t0 = min(T, w * per), t1 = min(T, t0 + per);
+  const int w_u = __builtin_amdgcn_readfirstlane(w);
+  const int per = (slice + WK - 1) / WK;
+  const int t0 = ks0 + min(slice, w_u * per), t1 = min(ks1, t0 + per);
   const int S = t1 - t0;
 
+  // Weight loads are branch-free (steps past the wave's range re-load its last step and
+  // are never multiplied), so the compiler can keep them in flight across the quantizer.
   uint4 wq[PD][NG];
   uint32_t wsb[PD][NG];
   auto load_chunk = [&](int tb) {
-    const int nh = min(PD, t1 - tb);
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
-      if (i < nh) {
-        const int t = tb + i;
+      const int t = min(tb + i, t1 - 1);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          wq[i][g] = load16_nt(Wp + wp_payload_off(g0 + g, t, lane, T));
-          wsb[i][g] = __builtin_nontemporal_load(Wsc + wp_scale_off(g0 + g, t >> 2, lane, T4) + (t & 3));
-        }
+      for (int g = 0; g < NG; ++g) {
+        wq[i][g] = load16_nt(Wp + wp_payload_off(g0 + g, t, lane, T));
+        wsb[i][g] = __builtin_nontemporal_load(Wsc + wp_scale_off(g0 + g, t >> 2, lane, T4) + (t & 3));
       }
     }
   };
-
   if (S > 0) load_chunk(t0);
 
-  // Quantize this wave's activation blocks (rows < M, blocks 4*t0 .. 4*t1-1) into LDS.
+  // Quantize this wave's activation blocks: rows < M, blocks 4*t0 .. 4*t1-1, batches of
+  // kQuantBatch blocks per lane with all their loads issued before any is used (lanes past
+  // the last block re-load it and store nothing).
   {
-    const int nbw = 4 * S;
-    const int nb = M * nbw;
-    for (int b = lane; b < nb; b += 64) {
-      const int m = b / nbw, kb = 4 * t0 + b % nbw;
-      uint32_t x[16];
-      load_block(A + (size_t)m * K + (size_t)kb * kBlock, x);
-      uint32_t q[4];
-      const uint32_t s = quant_block(x, q);
-      *reinterpret_cast<uint4*>(aq + (size_t)m * RS + kb * 16) = make_uint4(q[0], q[1], q[2], q[3]);
-      as[(size_t)m * KB + kb] = (uint8_t)s;
+    const int nbw = 4 * S, nb = M * nbw;
+    if (nb > 0) {
+      const int q64 = 64 / nbw, r64 = 64 % nbw;
+      int m = lane / nbw, r = lane % nbw;  // coordinates of block b = lane
+      for (int base = 0; base < nb; base += 64 * kQuantBatch) {
+        uint32_t x[kQuantBatch][16];
+        int mm[kQuantBatch], rr[kQuantBatch];
+#pragma unroll
+        for (int j = 0; j < kQuantBatch; ++j) {
+          mm[j] = m;
+          rr[j] = r;
+          const bool ok = base + j * 64 + lane < nb;
+          load_block(A + (size_t)(ok ? m : M - 1) * K + (size_t)(4 * t0 + (ok ? r : nbw - 1)) * kBlock, x[j]);
+          m += q64;
+          r += r64;
+          if (r >= nbw) { r -= nbw; ++m; }
+        }
+#pragma unroll
+        for (int j = 0; j < kQuantBatch; ++j) {
+          if (base + j * 64 + lane < nb) {
+            uint32_t q[4];
+            const uint32_t sc = quant_block(x[j], q);
+            const int kbl = 4 * (t0 - ks0) + rr[j];  // block index within the slice
+            *reinterpret_cast<uint4*>(aq + (size_t)mm[j] * RS + kbl * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+            as[(size_t)mm[j] * SB + kbl] = (uint8_t)sc;
+          }
+        }
+      }
     }
   }
   __syncthreads();
@@ -155,17 +186,13 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_skinny(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
       if (i < nh) {
-        const int t = tb + i;
+        const int kbl = 4 * (tb + i - ks0) + (lane >> 4);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const int m = 16 * mt + (lane & 15);
-          const int kb = 4 * t + (lane >> 4);
-          uint4 b = make_uint4(0u, 0u, 0u, 0u);
-          uint32_t sb = 0u;
-          if (m < M) {
-            b = *reinterpret_cast<const uint4*>(aq + (size_t)m * RS + kb * 16);
-            sb = as[(size_t)m * KB + kb];
-          }
+          // rows past M read row M-1: their output columns are never stored
+          const int m = min(16 * mt + (lane & 15), M - 1);
+          const uint4 b = *reinterpret_cast<const uint4*>(aq + (size_t)m * RS + kbl * 16);
+          const uint32_t sb = as[(size_t)m * SB + kbl];
 #pragma unroll
           for (int g = 0; g < NG; ++g) acc[g][mt] = mfma_fp4(wq[i][g], b, acc[g][mt], wsb[i][g], sb);
         }
@@ -177,7 +204,10 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_skinny(const uint16_t* __restr
   auto store = [&](int g, int mt, const v4f& v) {
     const int m = 16 * mt + (lane & 15);
     const int n = 16 * (g0 + g) + 4 * (lane >> 4);
-    if (m < M) *reinterpret_cast<uint2*>(C + (size_t)m * N + n) = pack4_bf16(v[0], v[1], v[2], v[3]);
+    if (m < M) {
+      if (P) *reinterpret_cast<v4f*>(P + ((size_t)blockIdx.y * M + m) * N + n) = v;
+      else *reinterpret_cast<uint2*>(C + (size_t)m * N + n) = pack4_bf16(v[0], v[1], v[2], v[3]);
+    }
   };
 
   if constexpr (WK == 1) {
@@ -201,66 +231,107 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_skinny(const uint16_t* __restr
   }
 }
 
-// ====================================================================== tiled GEMM
-//
-// For larger M. A CTA owns a BM x BN output tile (BM = 16 * MT rows, BN = 16 * NG * WN
-// columns); its WN waves split the columns. Each 128-wide K step: every thread loads and
-// quantizes its share of the BM x 128 activation tile (one 32-block per thread at BM=64),
-// writing operand-ordered payload and scales into one of two LDS buffers; each wave loads
-// its NG weight operands straight from global memory (a contiguous 1 KiB per operand) one
-// step ahead, then reads MT activation operands from LDS and issues NG * MT MFMAs.
-template <int MT, int NG, int WN>
-__global__ __launch_bounds__(64 * WN) void k_gemm_tile(const uint16_t* __restrict__ A,
-                                                       const uint8_t* __restrict__ Wp,
-                                                       uint16_t* __restrict__ C, int M, int N,
-                                                       int K) {
-  constexpr int BM = 16 * MT, BN = 16 * NG * WN, NTH = 64 * WN;
-  constexpr int NBLK = 4 * BM;
-  constexpr int BPT = (NBLK + NTH - 1) / NTH;
-  __shared__ __align__(16) uint8_t sq[2][MT * 64 * 16];
-  __shared__ __align__(16) uint8_t ss[2][MT * 64];
+// C = bf16(sum over slices s = 0..S-1, in order, of P[s]); four elements per thread.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ P,
+                                                       uint16_t* __restrict__ C, int64_t MN, int S) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  v4f acc = *reinterpret_cast<const v4f*>(P + i);
+  for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const v4f*>(P + (size_t)s * MN + i);
+  *reinterpret_cast<uint2*>(C + i) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
+}
 
-  const int T = steps_of(K), T4 = quads_of(K);
-  const int n_tiles = N / BN;
-  const int bm = blockIdx.x / n_tiles, bn = blockIdx.x % n_tiles;
+// ====================================================================== tiled GEMM (large M)
+//
+// A CTA owns a BM x BN output tile, BM = 16 * MT * WM rows and BN = 16 * NG * WN columns,
+// computed by WM x WN waves of MT x NG MFMA tiles each. Every 128-wide K step, all threads
+// quantize their share of the BM x 128 activation tile (one or more 32-blocks per thread)
+// into one of two LDS buffers in MFMA operand order; each wave reads its weight operands
+// straight from global memory (a contiguous 1 KiB each) and its activation operands from
+// LDS. Global loads run PF steps ahead of the MFMAs (activations in PF register slots,
+// weights in PF + 1). A tile whose columns run past N (BN not dividing N) masks whole
+// column groups.
+//
+// Tile order: CTAs are dealt round-robin to the 8 XCDs (blockIdx % 8), each with its own
+// L2, so CTA i is given logical tile (its XCD's contiguous share) and logical tiles walk
+// GM tile-rows at a time; the CTAs resident on one XCD then share activation rows and
+// weight columns in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int i, int total, int tiles_m, int tiles_n, int GM, int& bm,
+                                            int& bn) {
+  const int q = total / 8, r = total % 8;
+  const int x = i % 8, j = i / 8;
+  const int logical = x * q + min(x, r) + j;
+  const int gsize = GM * tiles_n;
+  const int grp = logical / gsize, first = grp * GM;
+  const int gm = min(tiles_m - first, GM);
+  const int rem = logical - grp * gsize;
+  bm = first + rem % gm;
+  bn = rem / gm;
+}
+
+template <int N_, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) { (f(std::integral_constant<int, I>{}), ...); }(
+      std::make_integer_sequence<int, N_>{});
+}
+
+template <int WM, int WN, int MT, int NG, int PF, int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void k_gemm_tile(const uint16_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ Wp,
+                                                            uint16_t* __restrict__ C, int M, int N,
+                                                            int K, int GM) {
+  constexpr int NTH = 64 * WM * WN;
+  constexpr int MTC = MT * WM;  // 16-row tiles per CTA
+  constexpr int BM = 16 * MTC, BN = 16 * NG * WN;
+  constexpr int NBLK = 4 * BM;
+  static_assert(NBLK % NTH == 0, "every thread quantizes the same number of blocks");
+  constexpr int BPT = NBLK / NTH;
+  __shared__ __align__(16) uint8_t sq[2][MTC * 64 * 16];
+  __shared__ __align__(16) uint8_t ss[2][MTC * 64];
+
+  const int T = steps_of(K), T4 = quads_of(K), G = N / 16;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int bm, bn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, GM, bm, bn);
   const int m0 = bm * BM;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int gw0 = (bn * BN) / 16 + w * NG;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / WN, wn = w % WN;
+  const int gw0 = bn * (BN / 16) + wn * NG;
   const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
 
-  uint32_t areg[BPT][16];
-  auto load_a = [&](int t) {
+  // Loads are branch-free so the compiler can count them: rows past M re-read row M-1
+  // and column groups past N re-read the last group; neither result is ever stored.
+  const uint16_t* arow[BPT];
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int b = threadIdx.x + i * NTH;
-      if (b < NBLK) {
-        const int m = m0 + (b >> 2);
-        if (m < M) load_block(A + (size_t)m * K + (size_t)t * kStepK + (b & 3) * kBlock, areg[i]);
-        else zero_block(areg[i]);
-      }
-    }
-  };
-  auto quant_store = [&](int buf) {
+  for (int i = 0; i < BPT; ++i) {
+    const int b = threadIdx.x + i * NTH;
+    arow[i] = A + (size_t)min(m0 + (b >> 2), M - 1) * K + (b & 3) * kBlock;
+  }
+  size_t woff[NG], soff[NG];
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int b = threadIdx.x + i * NTH;
-      if (b < NBLK) {
-        const int r = b >> 2, kbl = b & 3;
-        const int slot = (r >> 4) * 64 + (r & 15) + 16 * kbl;
-        uint32_t q[4];
-        const uint32_t s = quant_block(areg[i], q);
-        *reinterpret_cast<uint4*>(&sq[buf][slot * 16]) = make_uint4(q[0], q[1], q[2], q[3]);
-        ss[buf][slot] = (uint8_t)s;
-      }
-    }
+  for (int g = 0; g < NG; ++g) {
+    const int gc = min(gw0 + g, G - 1);
+    woff[g] = wp_payload_off(gc, 0, lane, T);
+    soff[g] = wp_scale_off(gc, 0, lane, T4);
+  }
+
+  uint32_t areg[PF][BPT][16];
+  uint4 wq[PF + 1][NG];
+  uint32_t wsc[PF + 1][NG];
+
+  auto load_a = [&](int t, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) load_block(arow[i] + (size_t)t * kStepK, areg[SL][i]);
   };
-  uint4 wq[2][NG];
-  uint32_t wsc[2][NG];
-  auto load_w = [&](int t, int slot) {
+  auto load_w = [&](int t, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      wq[slot][g] = load16_nt(Wp + wp_payload_off(gw0 + g, t, lane, T));
-      wsc[slot][g] = Wsc[wp_scale_off(gw0 + g, t >> 2, lane, T4) + (t & 3)];
+      wq[SL][g] = *reinterpret_cast<const uint4*>(Wp + woff[g] + (size_t)t * 1024);  // reused: cached
+      wsc[SL][g] = Wsc[soff[g] + (size_t)(t >> 2) * 256 + (t & 3)];
     }
   };
 
@@ -270,42 +341,67 @@ __global__ __launch_bounds__(64 * WN) void k_gemm_tile(const uint16_t* __restric
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](int t, int cur, int nxt) {
-    quant_store(t & 1);
-    if (t + 1 < T) {
-      load_a(t + 1);
-      load_w(t + 1, nxt);
+  // prologue: steps 0 .. PF-1 in flight (clamped to the last step when T < PF)
+  static_for<PF>([&](auto p) {
+    load_a(min((int)decltype(p)::value, T - 1), p);
+    load_w(min((int)decltype(p)::value, T - 1), p);
+  });
+
+  auto step = [&](int t, auto sa_c, auto sw_c) {
+    constexpr int SA = decltype(sa_c)::value, SW = decltype(sw_c)::value;
+    const int buf = t & 1;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int b = threadIdx.x + i * NTH;
+      const int r = b >> 2, kbl = b & 3;
+      const int slot = (r >> 4) * 64 + (r & 15) + 16 * kbl;
+      uint32_t q[4];
+      const uint32_t sc = quant_block(areg[SA][i], q);
+      *reinterpret_cast<uint4*>(&sq[buf][slot * 16]) = make_uint4(q[0], q[1], q[2], q[3]);
+      ss[buf][slot] = (uint8_t)sc;
     }
+    const int tn = min(t + PF, T - 1);  // past the end: a harmless re-load of the last step
+    load_a(tn, sa_c);
+    load_w(tn, std::integral_constant<int, (SW + PF) % (PF + 1)>{});
     __syncthreads();
     uint4 b[MT];
     uint32_t sb[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      b[mt] = *reinterpret_cast<const uint4*>(&sq[t & 1][(mt * 64 + lane) * 16]);
-      sb[mt] = ss[t & 1][mt * 64 + lane];
+      const int slot = (wm * MT + mt) * 64 + lane;
+      b[mt] = *reinterpret_cast<const uint4*>(&sq[buf][slot * 16]);
+      sb[mt] = ss[buf][slot];
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[g][mt] = mfma_fp4(wq[cur][g], b[mt], acc[g][mt], wsc[cur][g], sb[mt]);
+      for (int mt = 0; mt < MT; ++mt) acc[g][mt] = mfma_fp4(wq[SW][g], b[mt], acc[g][mt], wsc[SW][g], sb[mt]);
   };
 
-  load_a(0);
-  load_w(0, 0);
-  for (int t = 0; t < T; t += 2) {
-    step(t, 0, 1);
-    if (t + 1 < T) step(t + 1, 1, 0);
+  constexpr int U = PF * (PF + 1);
+  int t = 0;
+  for (; t + U <= T; t += U) {
+    static_for<U>([&](auto i) {
+      constexpr int I = decltype(i)::value;
+      step(t + I, std::integral_constant<int, I % PF>{}, std::integral_constant<int, I % (PF + 1)>{});
+    });
   }
+  static_for<U - 1>([&](auto i) {
+    constexpr int I = decltype(i)::value;
+    if (t + I < T) step(t + I, std::integral_constant<int, I % PF>{}, std::integral_constant<int, I % (PF + 1)>{});
+  });
 
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
+    if (gw0 + g < G) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = m0 + 16 * mt + (lane & 15);
-      const int n = 16 * (gw0 + g) + 4 * (lane >> 4);
-      if (m < M)
-        *reinterpret_cast<uint2*>(C + (size_t)m * N + n) =
-            pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = m0 + 16 * (wm * MT + mt) + (lane & 15);
+        const int n = 16 * (gw0 + g) + 4 * (lane >> 4);
+        if (m < M)
+          *reinterpret_cast<uint2*>(C + (size_t)m * N + n) =
+              pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
+      }
     }
   }
 }
@@ -523,61 +619,205 @@ hipError_t ensure_lds_limit(const void* kern, std::atomic<uint64_t>& done) {
   return e;
 }
 
+// LDS of the grouped kernel: quantized rows [M][K/2 + 16] and scales [M][K/32], or the
+// cross-wave reduction, whichever is larger.
 size_t skinny_lds_bytes(int M, int K, int MT, int NG, int WK) {
   const size_t act = (size_t)M * (K / 2 + 16) + (size_t)M * (K / kBlock);
   const size_t red = (size_t)WK * NG * MT * 64 * 16;
   return act > red ? act : red;
 }
 
+// LDS of the streaming kernel for a slice of TS steps.
+size_t stream_lds_bytes(int M, int TS, int MT, int NG, int WK) {
+  const size_t act = (size_t)M * (TS * 64 + 16) + (size_t)M * 4 * TS;
+  const size_t red = (size_t)WK * NG * MT * 64 * 16;
+  return act > red ? act : red;
+}
+
+// ---------------------------------------------------------------- configurations
+struct GemmConfig {
+  bool tile = false;
+  int MT = 1, NG = 1, WK = 4, S = 1;     // streaming kernel (S = K slices)
+  int WM = 1, WN = 4, PF = 2, GM = 8;    // tiled kernel (uses MT, NG too)
+  int OCC = 1;                           // tiled kernel: minimum waves per SIMD asked of the compiler
+};
+
+#define MX_STREAM_CONFIGS(X) \
+  X(1, 1, 2) X(1, 1, 4) X(1, 1, 8) X(1, 2, 4) X(1, 2, 8) X(1, 4, 4) \
+  X(2, 1, 2) X(2, 1, 4) X(2, 1, 8) X(2, 2, 4) X(2, 2, 8) X(2, 4, 4) \
+  X(4, 1, 4) X(4, 1, 8) X(4, 2, 4) X(4, 4, 4) X(8, 1, 4) X(8, 2, 4)
+
+#define MX_TILE_CONFIGS(X) \
+  X(1, 4, 4, 4, 2, 1) X(2, 4, 4, 4, 2, 1) X(1, 4, 8, 4, 1, 1) X(2, 2, 4, 8, 1, 1) X(1, 4, 4, 2, 2, 1) \
+  X(1, 4, 4, 4, 1, 2) X(1, 4, 4, 4, 2, 2) X(2, 4, 4, 4, 1, 1) X(1, 4, 4, 2, 2, 2)
+
 template <int MT, int NG, int WK>
-hipError_t run_skinny(const void* a, const void* wp, void* c, int M, int N, int K, hipStream_t st) {
-  auto kern = k_gemm_skinny<MT, NG, WK, kSkinnyPD>;
+hipError_t run_stream(const void* a, const void* wp, void* c, float* P, int M, int N, int K, int S,
+                      hipStream_t st) {
+  auto kern = k_gemm_stream<MT, NG, WK, kSkinnyPD / NG>;
   static std::atomic<uint64_t> configured{0};
-  const size_t lds = skinny_lds_bytes(M, K, MT, NG, WK);
+  const int T = steps_of(K);
+  const int TS = (T + S - 1) / S;
+  const size_t lds = stream_lds_bytes(M, TS, MT, NG, WK);
+  if (lds > kMaxLds) return hipErrorInvalidValue;
   if (lds > 65536) {
     hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), configured);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(N / (16 * NG))), dim3(64 * WK), lds, st,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(N / (16 * NG)), (unsigned)S), dim3(64 * WK), lds, st,
                      static_cast<const uint16_t*>(a), static_cast<const uint8_t*>(wp),
-                     static_cast<uint16_t*>(c), M, N, K);
+                     static_cast<uint16_t*>(c), P, M, N, K, TS);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t MN = (int64_t)M * N;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, st, P,
+                     static_cast<uint16_t*>(c), MN, S);
   return hipGetLastError();
 }
 
-template <int MT, int NG, int WN>
-hipError_t run_tile(const void* a, const void* wp, void* c, int M, int N, int K, hipStream_t st) {
-  constexpr int BM = 16 * MT, BN = 16 * NG * WN;
-  const int64_t grid = (int64_t)((M + BM - 1) / BM) * (N / BN);
-  hipLaunchKernelGGL((k_gemm_tile<MT, NG, WN>), dim3((unsigned)grid), dim3(64 * WN), 0, st,
+template <int WM, int WN, int MT, int NG, int PF, int OCC>
+hipError_t run_tile(const void* a, const void* wp, void* c, int M, int N, int K, int GM, hipStream_t st) {
+  constexpr int BM = 16 * MT * WM, BN = 16 * NG * WN;
+  const int64_t grid = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((k_gemm_tile<WM, WN, MT, NG, PF, OCC>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st,
                      static_cast<const uint16_t*>(a), static_cast<const uint8_t*>(wp),
-                     static_cast<uint16_t*>(c), M, N, K);
+                     static_cast<uint16_t*>(c), M, N, K, GM);
   return hipGetLastError();
+}
+
+bool stream_supported(int MT, int NG, int WK) {
+#define X(mt, ng, wk) if (MT == mt && NG == ng && WK == wk) return true;
+  MX_STREAM_CONFIGS(X)
+#undef X
+  return false;
+}
+
+bool tile_supported(const GemmConfig& c) {
+#define X(wm, wn, mt, ng, pf, occ) \
+  if (c.WM == wm && c.WN == wn && c.MT == mt && c.NG == ng && c.PF == pf && c.OCC == occ) return true;
+  MX_TILE_CONFIGS(X)
+#undef X
+  return false;
+}
+
+hipError_t run_config(const GemmConfig& c, const void* a, const void* wp, void* out, float* P, int M,
+                      int N, int K, hipStream_t st) {
+  if (!c.tile) {
+#define X(mt, ng, wk) \
+  if (c.MT == mt && c.NG == ng && c.WK == wk) return run_stream<mt, ng, wk>(a, wp, out, P, M, N, K, c.S, st);
+    MX_STREAM_CONFIGS(X)
+#undef X
+  } else {
+#define X(wm, wn, mt, ng, pf, occ) \
+  if (c.WM == wm && c.WN == wn && c.MT == mt && c.NG == ng && c.PF == pf && c.OCC == occ) \
+    return run_tile<wm, wn, mt, ng, pf, occ>(a, wp, out, M, N, K, c.GM, st);
+    MX_TILE_CONFIGS(X)
+#undef X
+  }
+  return hipErrorInvalidValue;
+}
+
+int round_up_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Default configuration for a shape, given the workspace the caller offers. The rules come
+// from sweeping every compiled configuration over the microbenchmark shapes on MI355X
+// (rotating buffer sets larger than the Infinity Cache).
+GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
+  GemmConfig c;
+  const int T = steps_of(K), G = N / 16;
+  auto stream_fits = [&](const GemmConfig& s) {
+    const int TS = (T + s.S - 1) / s.S;
+    const size_t need = s.S > 1 ? (size_t)s.S * M * N * 4 : 0;
+    return need <= ws_bytes && stream_lds_bytes(M, TS, s.MT, s.NG, s.WK) <= kMaxLds && G % s.NG == 0;
+  };
+  if (M <= 32 || (M <= 128 && G <= 96)) {
+    // weight-streaming kernel: the weight is read once, straight into registers
+    GemmConfig s;
+    s.tile = false;
+    s.MT = round_up_pow2((M + 15) / 16);
+    if (M <= 4) {
+      s.NG = 1;
+      s.WK = G >= 256 ? 2 : 4;
+    } else if (M <= 16) {
+      s.NG = G >= 512 ? 4 : (G >= 256 ? 2 : 1);
+      s.WK = (G >= 256 && G < 512) ? 8 : 4;
+    } else if (M <= 32) {
+      s.NG = G >= 512 ? 4 : 2;
+      s.WK = 4;
+    } else {
+      s.NG = 2;
+      s.WK = 4;
+    }
+    // few column groups (N = 1536): split K so the grid covers the chip
+    if (G <= 96) s.S = M <= 16 ? 1 : 4;
+    while (!stream_fits(s) && s.S < T && (size_t)(2 * s.S) * M * N * 4 <= ws_bytes) s.S *= 2;
+    if (!stream_fits(s)) s.S = 1;
+    if (stream_fits(s)) return s;
+  }
+  // tiled kernel: 64 x 256 tiles when there are enough of them, else 64 x 128
+  c.tile = true;
+  c.WM = 1; c.WN = 4; c.MT = 4; c.PF = 2; c.OCC = 2;
+  const int64_t tiles256 = (int64_t)((M + 63) / 64) * ((N + 255) / 256);
+  if (tiles256 >= 150) { c.NG = 4; c.GM = 8; }
+  else { c.NG = 2; c.GM = 16; }
+  return c;
+}
+
+// Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming) or "t,WM,WN,MT,NG,PF,GM[,OCC]" (tiled)
+// replaces the default choice. Returns 0 when unset, 1 when applied, -1 when the string
+// does not name a compiled configuration (the call then fails rather than silently
+// running something else).
+int override_config(GemmConfig& c) {
+  const char* e = std::getenv("MX_GEMM_CONFIG");
+  if (!e || !*e) return 0;
+  GemmConfig o;
+  int v[7] = {0, 0, 0, 0, 0, 0, 0};
+  if (e[0] == 's' && std::sscanf(e, "s,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) == 4) {
+    o.tile = false; o.MT = v[0]; o.NG = v[1]; o.WK = v[2]; o.S = v[3];
+    if (!stream_supported(o.MT, o.NG, o.WK) || o.S < 1) return -1;
+  } else if (e[0] == 't' && std::sscanf(e, "t,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6]) >= 6) {
+    o.tile = true; o.WM = v[0]; o.WN = v[1]; o.MT = v[2]; o.NG = v[3]; o.PF = v[4]; o.GM = v[5] < 1 ? 1 : v[5];
+    o.OCC = v[6] < 1 ? 1 : v[6];
+    if (!tile_supported(o)) return -1;
+  } else {
+    return -1;
+  }
+  c = o;
+  return 1;
 }
 
 }  // namespace
 
-// The largest M the small-M kernel takes, and its LDS need at that M.
-int skinny_max_m() { return 32; }
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0) return 0;
+  const GemmConfig c = select_config((int)M, (int)N, (int)K, (size_t)-1);
+  return (!c.tile && c.S > 1) ? (size_t)c.S * (size_t)M * (size_t)N * 4 : 0;
+}
 
 hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M64, int64_t N64, int64_t K64,
-                       hipStream_t st) {
+                       void* ws, size_t ws_bytes, hipStream_t st) {
   const int M = (int)M64, N = (int)N64, K = (int)K64;
-  const int T = steps_of(K);
-  const int G = N / 16;
-  if (M <= 32 && skinny_lds_bytes(M, K, 2, 1, 8) <= kMaxLds) {
-    const int WK = (G < 256) ? 8 : (T >= 8 ? 4 : 2);
-    if (M <= 16) {
-      if (WK == 8) return run_skinny<1, 1, 8>(a, wp, c, M, N, K, st);
-      if (WK == 4) return run_skinny<1, 1, 4>(a, wp, c, M, N, K, st);
-      return run_skinny<1, 1, 2>(a, wp, c, M, N, K, st);
-    }
-    if (WK == 8) return run_skinny<2, 1, 8>(a, wp, c, M, N, K, st);
-    if (WK == 4) return run_skinny<2, 1, 4>(a, wp, c, M, N, K, st);
-    return run_skinny<2, 1, 2>(a, wp, c, M, N, K, st);
+  if (!ws) ws_bytes = 0;
+  GemmConfig cfg = select_config(M, N, K, ws_bytes);
+  const int ov = override_config(cfg);
+  if (ov < 0) return hipErrorInvalidValue;
+  if (ov > 0 && !cfg.tile) {
+    // an overriding streaming choice must fit its slice in LDS and its partials in the
+    // workspace, and cover M
+    const int T = steps_of(K);
+    if (cfg.S > T) cfg.S = T;
+    const size_t need = cfg.S > 1 ? (size_t)cfg.S * M * N * 4 : 0;
+    const int TS = (T + cfg.S - 1) / cfg.S;
+    if (M > 16 * cfg.MT || need > ws_bytes || (N / 16) % cfg.NG != 0 ||
+        stream_lds_bytes(M, TS, cfg.MT, cfg.NG, cfg.WK) > kMaxLds)
+      return hipErrorInvalidValue;
   }
-  const int64_t tiles_wide = (int64_t)((M + 63) / 64) * (N / 256);
-  if (tiles_wide >= 512) return run_tile<4, 4, 4>(a, wp, c, M, N, K, st);
-  return run_tile<4, 1, 4>(a, wp, c, M, N, K, st);
+  return run_config(cfg, a, wp, c, cfg.tile ? nullptr : (cfg.S > 1 ? static_cast<float*>(ws) : nullptr),
+                    M, N, K, st);
 }
 
 namespace {

@@ -1,0 +1,95 @@
+"""Every compiled GEMM configuration (streaming kernel with and without K slices, tiled
+kernel with and without masked tail tiles, several tile orders) against the oracle.
+
+The library's tuning override (environment variable MX_GEMM_CONFIG) forces each
+configuration; an override that does not name a compiled, feasible configuration fails
+the call, so each case below provably ran the configuration it names."""
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import mx_oracle as O
+
+from gpu_util import check_gemm, dev_bf16, host_bits, lib_or_fail, torch_or_skip
+
+pytestmark = pytest.mark.gpu
+
+# mirrors MX_STREAM_CONFIGS / MX_TILE_CONFIGS in the kernels
+STREAM = [(1, 1, 2), (1, 1, 4), (1, 1, 8), (1, 2, 4), (1, 2, 8), (1, 4, 4),
+          (2, 1, 2), (2, 1, 4), (2, 1, 8), (2, 2, 4), (2, 2, 8), (2, 4, 4),
+          (4, 1, 4), (4, 1, 8), (4, 2, 4), (4, 4, 4), (8, 1, 4), (8, 2, 4)]
+TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8, 1, 1), (1, 4, 4, 2, 2, 1),
+        (1, 4, 4, 4, 1, 2), (1, 4, 4, 4, 2, 2), (2, 4, 4, 4, 1, 1), (1, 4, 4, 2, 2, 2)]
+N_TEST = 768          # 3 x 256: tail tiles for BN = 512
+K_TESTS = (4224, 768)  # 33 and 6 steps of 128
+LDS_MAX = 160 * 1024
+
+_cache = {}
+
+
+def _case(K):
+    if K not in _cache:
+        mx = lib_or_fail()
+        a = W.dense_activation(300, K, "plain", seed=21)
+        w = W.dense_weight(N_TEST, K, seed=22)
+        qw, sw = O.quantize_mx(w)
+        qa, sa = O.quantize_mx(a)
+        exact = O.gemm_from_mx(qa, sa, qw, sw)
+        _cache[K] = (a, mx.mx_prepare_weight(dev_bf16(w)), exact)
+    return _cache[K]
+
+
+def _run(cfg, a, wp, ws):
+    mx = lib_or_fail()
+    os.environ["MX_GEMM_CONFIG"] = cfg
+    try:
+        return host_bits(mx.mx_a4w4_gemm(dev_bf16(a), wp, N_TEST, workspace=ws))
+    finally:
+        del os.environ["MX_GEMM_CONFIG"]
+
+
+def _stream_lds(M, TS, MT, NG, WK):
+    return max(M * (TS * 64 + 16) + M * 4 * TS, WK * NG * MT * 1024)
+
+
+@pytest.mark.parametrize("K", K_TESTS)
+@pytest.mark.parametrize("mt,ng,wk", STREAM, ids=[f"s{c}" for c in STREAM])
+def test_stream_config(mt, ng, wk, K):
+    torch = torch_or_skip()
+    a, wp, exact = _case(K)
+    T = K // 128
+    M = 16 * mt - 3
+    ws = torch.empty(16 * M * N_TEST * 4, dtype=torch.uint8, device="cuda")
+    splits = [s for s in (1, 3, 16) if s <= T and _stream_lds(M, -(-T // s), mt, ng, wk) <= LDS_MAX]
+    assert splits
+    for S in splits:
+        c = _run(f"s,{mt},{ng},{wk},{S}", a[:M], wp, ws)
+        torch.cuda.synchronize()
+        check_gemm(c, exact[:M], what=f"stream {mt},{ng},{wk} S={S} K={K}")
+
+
+@pytest.mark.parametrize("K", K_TESTS)
+@pytest.mark.parametrize("cfg", TILE, ids=[f"t{c}" for c in TILE])
+def test_tile_config(cfg, K):
+    torch = torch_or_skip()
+    a, wp, exact = _case(K)
+    for M, gm in ((100, 1), (300, 8), (37, 3)):
+        c = _run("t," + ",".join(map(str, cfg[:5])) + f",{gm},{cfg[5]}", a[:M], wp, False)
+        torch.cuda.synchronize()
+        check_gemm(c, exact[:M], what=f"tile {cfg} GM={gm} M={M} K={K}")
+
+
+def test_invalid_override_fails_loudly():
+    torch_or_skip()
+    mx = lib_or_fail()
+    a, wp, _ = _case(768)
+    # not compiled, malformed, and a streaming choice that cannot cover M = 40
+    for bad, M in (("s,3,1,4,1", 5), ("t,9,9,9,9,9,9", 5), ("garbage", 5), ("s,1,1,4,1", 40)):
+        os.environ["MX_GEMM_CONFIG"] = bad
+        try:
+            with pytest.raises(mx.MxError):
+                mx.mx_a4w4_gemm(dev_bf16(a[:M]), wp, N_TEST, workspace=False)
+        finally:
+            del os.environ["MX_GEMM_CONFIG"]
