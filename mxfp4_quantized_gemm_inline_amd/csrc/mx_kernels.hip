@@ -86,47 +86,77 @@ __global__ __launch_bounds__(256) void k_unprepare(const uint8_t* __restrict__ W
 
 // ====================================================================== streaming GEMM (small and mid M)
 //
-// For M <= 16 * MT. CTA (x, y) owns NG column groups (16 * NG output columns) and the y-th
-// slice of TS K steps; its WK waves split the slice's steps. Each wave streams its share of
+// StreamCTA is the CTA-level building block shared by the dense small-M GEMM and the
+// grouped GEMM: WK waves compute 16 * NG output columns for up to 16 * MT rows over a range
+// of 128-wide K steps, splitting the steps between waves. Each wave streams its share of
 // the prepared weight straight from HBM into registers, PD steps at a time (the weight has
-// no reuse here, so it is not staged in LDS) while it quantizes its own activation blocks
-// (rows < M) into LDS,
-// several blocks per lane in flight. The wave partial sums are added in LDS in a fixed wave
-// order. With one slice the result is rounded to bf16 and stored; with several, each slice
-// writes an FP32 partial tile to the workspace P[slice][M][N] and k_splitk_reduce adds the
-// slices in order (so the result is deterministic).
+// no reuse here, so it is not staged in LDS), quantizes its own activation blocks into LDS
+// (QB blocks per lane per batch, loads issued before any is used), runs its MFMAs, and the
+// wave partial sums are added in LDS in a fixed wave order.
 //
-// LDS: quantized activations [M][TS * 64 + 16] (the 16-byte pad staggers rows across
-// banks), then their scales [M][4 * TS]; reused for the cross-wave reduction.
-constexpr int kQuantBatch = 4;
+// Weight loads are branch-free (steps past the wave's range re-load its last step and are
+// never multiplied), and the first activation batch is issued before them, so the compiler's
+// in-order wait counts let the weight stream stay in flight while the quantizer runs.
+//
+// LDS: quantized activations [16 MT][TS * 64 + 16] (the 16-byte pad staggers rows across
+// banks), then their scales [16 MT][4 TS]; reused for the cross-wave reduction.
+constexpr int kSkinnyPD = 16;
 
-template <int MT, int NG, int WK, int PD>
-__global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restrict__ A,
-                                                         const uint8_t* __restrict__ Wp,
-                                                         uint16_t* __restrict__ C,
-                                                         float* __restrict__ P, int M, int N, int K,
-                                                         int TS) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int T = steps_of(K), T4 = quads_of(K);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g0 = blockIdx.x * NG;
-  const int ks0 = min(T, (int)blockIdx.y * TS), ks1 = min(T, ks0 + TS);
-  const int slice = ks1 - ks0;
-  const int RS = TS * 64 + 16, SB = 4 * TS;
-  const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
-  uint8_t* aq = smem;
-  uint8_t* as = smem + (size_t)M * RS;
+// Rows of a dense row-major A.
+struct DenseRows {
+  const uint16_t* A;
+  int K;
+  __device__ __forceinline__ const uint16_t* ptr(int m, bool& valid) const {
+    valid = true;
+    return A + (size_t)m * K;
+  }
+};
 
-  const int w_u = __builtin_amdgcn_readfirstlane(w);
-  const int per = (slice + WK - 1) / WK;
-  const int t0 = ks0 + min(slice, w_u * per), t1 = min(ks1, t0 + per);
-  const int S = t1 - t0;
+// Rows gathered by token index; an index outside [0, T) reads as an all-zero row (its
+// load goes to row 0 and the quantized block is replaced by zeros).
+struct GatherRows {
+  const uint16_t* A;
+  const int32_t* tok;
+  int base, T, K;
+  __device__ __forceinline__ const uint16_t* ptr(int m, bool& valid) const {
+    const int t = tok[base + m];
+    valid = t >= 0 && t < T;
+    return A + (size_t)(valid ? t : 0) * K;
+  }
+};
 
-  // Weight loads are branch-free (steps past the wave's range re-load its last step and
-  // are never multiplied), so the compiler can keep them in flight across the quantizer.
+template <int MT, int NG, int WK, int PD, int QB>
+struct StreamCTA {
+  int lane, T, T4, g0, ks0, t0, t1, S, RS, SB;
+  const uint8_t* __restrict__ Wp;
+  const uint8_t* __restrict__ Wsc;
+  uint8_t* aq;
+  uint8_t* as;
   uint4 wq[PD][NG];
   uint32_t wsb[PD][NG];
-  auto load_chunk = [&](int tb) {
+
+  __device__ __forceinline__ void init(const uint8_t* wp, int N, int K, int g0_, int ks0_, int ks1, int TS,
+                                       uint8_t* smem) {
+    lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    T = steps_of(K);
+    T4 = quads_of(K);
+    g0 = g0_;
+    ks0 = ks0_;
+    const int slice = ks1 - ks0;
+    const int per = (slice + WK - 1) / WK;
+    t0 = ks0 + min(slice, w * per);
+    t1 = min(ks1, t0 + per);
+    S = t1 - t0;
+    RS = TS * 64 + 16;
+    SB = 4 * TS;
+    Wp = wp;
+    Wsc = wp + payload_bytes(N, K);
+    aq = smem;
+    as = smem + (size_t)(16 * MT) * RS;
+  }
+
+  __device__ __forceinline__ void load_w(int tb) {
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
       const int t = min(tb + i, t1 - 1);
@@ -136,99 +166,136 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restr
         wsb[i][g] = __builtin_nontemporal_load(Wsc + wp_scale_off(g0 + g, t >> 2, lane, T4) + (t & 3));
       }
     }
-  };
-  if (S > 0) load_chunk(t0);
+  }
 
-  // Quantize this wave's activation blocks: rows < M, blocks 4*t0 .. 4*t1-1, batches of
-  // kQuantBatch blocks per lane with all their loads issued before any is used (lanes past
-  // the last block re-load it and store nothing).
-  {
-    const int nbw = 4 * S, nb = M * nbw;
-    if (nb > 0) {
-      const int q64 = 64 / nbw, r64 = 64 % nbw;
-      int m = lane / nbw, r = lane % nbw;  // coordinates of block b = lane
-      for (int base = 0; base < nb; base += 64 * kQuantBatch) {
-        uint32_t x[kQuantBatch][16];
-        int mm[kQuantBatch], rr[kQuantBatch];
+  // Quantize rows [0, Mc) of this wave's blocks 4*t0 .. 4*t1-1 into LDS. `after_first`
+  // runs once, right after the first batch's loads are issued.
+  template <class Rows, class F>
+  __device__ __forceinline__ void quant(const Rows& rows, int Mc, F&& after_first) {
+    const int nbw = 4 * S, nb = Mc * nbw;
+    if (nb <= 0) {
+      after_first();
+      return;
+    }
+    const int q64 = 64 / nbw, r64 = 64 % nbw;
+    int m = lane / nbw, r = lane % nbw;  // coordinates of block b = lane
+    bool first = true;
+    for (int base = 0; base < nb; base += 64 * QB) {
+      uint32_t x[QB][16];
+      int mm[QB], rr[QB];
+      bool val[QB];
 #pragma unroll
-        for (int j = 0; j < kQuantBatch; ++j) {
-          mm[j] = m;
-          rr[j] = r;
-          const bool ok = base + j * 64 + lane < nb;
-          load_block(A + (size_t)(ok ? m : M - 1) * K + (size_t)(4 * t0 + (ok ? r : nbw - 1)) * kBlock, x[j]);
-          m += q64;
-          r += r64;
-          if (r >= nbw) { r -= nbw; ++m; }
+      for (int j = 0; j < QB; ++j) {
+        const bool ok = base + j * 64 + lane < nb;
+        mm[j] = ok ? m : Mc - 1;  // lanes past the last block re-load it and store nothing
+        rr[j] = ok ? r : nbw - 1;
+        const uint16_t* row = rows.ptr(mm[j], val[j]);
+        load_block(row + (size_t)(4 * t0 + rr[j]) * kBlock, x[j]);
+        mm[j] = ok ? m : -1;
+        m += q64;
+        r += r64;
+        if (r >= nbw) { r -= nbw; ++m; }
+      }
+      if (first) {
+        after_first();
+        first = false;
+      }
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        uint32_t q[4];
+        uint32_t sc = quant_block(x[j], q);
+        if (!val[j]) { q[0] = q[1] = q[2] = q[3] = 0u; sc = 0u; }
+        if (mm[j] >= 0) {
+          const int kbl = 4 * (t0 - ks0) + rr[j];  // block index within the slice
+          *reinterpret_cast<uint4*>(aq + (size_t)mm[j] * RS + kbl * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+          as[(size_t)mm[j] * SB + kbl] = (uint8_t)sc;
         }
+      }
+    }
+  }
+
+  // acc += this wave's steps for rows [0, Mc) (rows past Mc read row Mc-1 and are never stored).
+  // With `resident`, the weight chunk loaded at t0 is reused; otherwise chunks are (re)loaded.
+  __device__ __forceinline__ void mma(int Mc, bool resident, v4f (&acc)[NG][MT]) {
 #pragma unroll
-        for (int j = 0; j < kQuantBatch; ++j) {
-          if (base + j * 64 + lane < nb) {
-            uint32_t q[4];
-            const uint32_t sc = quant_block(x[j], q);
-            const int kbl = 4 * (t0 - ks0) + rr[j];  // block index within the slice
-            *reinterpret_cast<uint4*>(aq + (size_t)mm[j] * RS + kbl * 16) = make_uint4(q[0], q[1], q[2], q[3]);
-            as[(size_t)mm[j] * SB + kbl] = (uint8_t)sc;
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int tb = t0; tb < t1; tb += PD) {
+      if (!resident && tb != t0) load_w(tb);
+      const int nh = min(PD, t1 - tb);
+#pragma unroll
+      for (int i = 0; i < PD; ++i) {
+        if (i < nh) {
+          const int kbl = 4 * (tb + i - ks0) + (lane >> 4);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int m = min(16 * mt + (lane & 15), Mc - 1);
+            const uint4 b = *reinterpret_cast<const uint4*>(aq + (size_t)m * RS + kbl * 16);
+            const uint32_t sb = as[(size_t)m * SB + kbl];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acc[g][mt] = mfma_fp4(wq[i][g], b, acc[g][mt], wsb[i][g], sb);
           }
         }
       }
     }
   }
-  __syncthreads();
 
-  v4f acc[NG][MT];
+  // Sum the wave partials in wave order through LDS (which must be free) and hand each
+  // (g, mt) 4-column group to store(g, mt, value).
+  template <class Store>
+  __device__ __forceinline__ void reduce_store(v4f (&acc)[NG][MT], uint8_t* smem, Store&& store) {
+    if constexpr (WK == 1) {
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int tb = t0; tb < t1; tb += PD) {
-    const int nh = min(PD, t1 - tb);
+        for (int mt = 0; mt < MT; ++mt) store(g, mt, acc[g][mt]);
+    } else {
+      const int w = threadIdx.x >> 6;
+      v4f* red = reinterpret_cast<v4f*>(smem);  // [WK][NG*MT][64]
 #pragma unroll
-    for (int i = 0; i < PD; ++i) {
-      if (i < nh) {
-        const int kbl = 4 * (tb + i - ks0) + (lane >> 4);
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          // rows past M read row M-1: their output columns are never stored
-          const int m = min(16 * mt + (lane & 15), M - 1);
-          const uint4 b = *reinterpret_cast<const uint4*>(aq + (size_t)m * RS + kbl * 16);
-          const uint32_t sb = as[(size_t)m * SB + kbl];
-#pragma unroll
-          for (int g = 0; g < NG; ++g) acc[g][mt] = mfma_fp4(wq[i][g], b, acc[g][mt], wsb[i][g], sb);
-        }
+        for (int mt = 0; mt < MT; ++mt) red[(w * NG * MT + g * MT + mt) * 64 + lane] = acc[g][mt];
+      __syncthreads();
+      for (int p = w; p < NG * MT; p += WK) {
+        v4f sum = red[p * 64 + lane];
+        for (int ww = 1; ww < WK; ++ww) sum += red[(ww * NG * MT + p) * 64 + lane];
+        store(p / MT, p % MT, sum);
       }
     }
-    if (tb + PD < t1) load_chunk(tb + PD);
   }
+};
 
-  auto store = [&](int g, int mt, const v4f& v) {
+// Dense small-M GEMM: CTA (x, y) owns column groups [x NG, x NG + NG) and K slice y of TS
+// steps. One slice: bf16 C directly; several: FP32 partials to P[slice][M][N], added in
+// slice order by k_splitk_reduce (deterministic).
+template <int MT, int NG, int WK, int PD, int QB>
+__global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restrict__ A,
+                                                         const uint8_t* __restrict__ Wp,
+                                                         uint16_t* __restrict__ C,
+                                                         float* __restrict__ P, int M, int N, int K,
+                                                         int TS) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int T = steps_of(K);
+  const int ks0 = min(T, (int)blockIdx.y * TS), ks1 = min(T, ks0 + TS);
+  StreamCTA<MT, NG, WK, PD, QB> cta;
+  cta.init(Wp, N, K, blockIdx.x * NG, ks0, ks1, TS, smem);
+  const DenseRows rows{A, K};
+  cta.quant(rows, M, [&] { if (cta.S > 0) cta.load_w(cta.t0); });
+  __syncthreads();
+  v4f acc[NG][MT];
+  cta.mma(M, false, acc);
+  if constexpr (WK > 1) __syncthreads();  // every wave is done with the activation region
+  const int lane = threadIdx.x & 63;
+  cta.reduce_store(acc, smem, [&](int g, int mt, const v4f& v) {
     const int m = 16 * mt + (lane & 15);
-    const int n = 16 * (g0 + g) + 4 * (lane >> 4);
+    const int n = 16 * (blockIdx.x * NG + g) + 4 * (lane >> 4);
     if (m < M) {
       if (P) *reinterpret_cast<v4f*>(P + ((size_t)blockIdx.y * M + m) * N + n) = v;
       else *reinterpret_cast<uint2*>(C + (size_t)m * N + n) = pack4_bf16(v[0], v[1], v[2], v[3]);
     }
-  };
-
-  if constexpr (WK == 1) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) store(g, mt, acc[g][mt]);
-  } else {
-    __syncthreads();  // every wave is done with the activation region
-    v4f* red = reinterpret_cast<v4f*>(smem);  // [WK][NG*MT][64]
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) red[(w * NG * MT + g * MT + mt) * 64 + lane] = acc[g][mt];
-    __syncthreads();
-    for (int p = w; p < NG * MT; p += WK) {
-      v4f sum = red[p * 64 + lane];
-      for (int ww = 1; ww < WK; ++ww) sum += red[(ww * NG * MT + p) * 64 + lane];
-      store(p / MT, p % MT, sum);
-    }
-  }
+  });
 }
 
 // C = bf16(sum over slices s = 0..S-1, in order, of P[s]); four elements per thread.
@@ -412,12 +479,12 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
 // Work item = (a, c): the a-th expert with at least one row, and NG column groups. Grid size
 // is min(E, R_max) * (N / (16 NG)); each CTA finds its expert by a block-wide scan of the
 // segment table, so no host sync or workspace is needed and empty experts cost nothing.
-// Inside, the small-M scheme: WK waves split K, each keeping its whole share of the expert's
-// weight columns in registers while the CTA walks the expert's rows in chunks of 16 * MT;
-// each chunk's rows are gathered by token index and quantized into LDS.
+// Inside, the streaming scheme (StreamCTA): WK waves split K, each keeping its share of the
+// expert's weight columns in registers while the CTA walks the expert's rows in chunks of
+// 16 * MT, gathering each chunk's rows by token index into the quantizer.
 // Malformed tables are clamped (segments to [0, R_max], tokens outside [0, T) read as zero
 // rows), so every access stays in bounds.
-template <int MT, int NG, int WK, int PD>
+template <int MT, int NG, int WK, int PD, int QB, bool RES>
 __global__ __launch_bounds__(64 * WK) void k_gemm_grouped(const uint16_t* __restrict__ A,
                                                           const int32_t* __restrict__ row_token,
                                                           const int32_t* __restrict__ offs, int E,
@@ -471,107 +538,39 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_grouped(const uint16_t* __rest
   const int e = s_e;
   if (e < 0) return;
   const int lo = s_lo, cnt = s_hi - s_lo;
-
-  const int T = steps_of(K), T4 = quads_of(K), KB = K / kBlock;
-  const int RS = K / 2 + 16;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
   const int g0 = c * NG;
-  const uint8_t* __restrict__ Wp = Wall + (size_t)e * (payload_bytes(N, K) + scale_region_bytes(N, K));
-  const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
-  uint8_t* aq = smem;
-  uint8_t* as = smem + (size_t)CH * RS;
 
-  const int per = (T + WK - 1) / WK;
-  const int t0 = min(T, w * per), t1 = min(T, t0 + per);
-  const int S = t1 - t0;
-  const bool resident = S <= PD;
-
-  uint4 wq[PD][NG];
-  uint32_t wsb[PD][NG];
-  auto load_chunk = [&](int tb) {
-    const int nh = min(PD, t1 - tb);
-#pragma unroll
-    for (int i = 0; i < PD; ++i) {
-      if (i < nh) {
-        const int t = tb + i;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          wq[i][g] = load16_nt(Wp + wp_payload_off(g0 + g, t, lane, T));
-          wsb[i][g] = __builtin_nontemporal_load(Wsc + wp_scale_off(g0 + g, t >> 2, lane, T4) + (t & 3));
-        }
-      }
+  if (Ttok <= 0) {  // no activations at all: every row is Q(0) W^T = 0
+    for (int i = tid; i < cnt * 4 * NG; i += NTH) {
+      const int r = i / (4 * NG), q = i % (4 * NG);
+      *reinterpret_cast<uint2*>(C + (size_t)(lo + r) * N + 16 * g0 + 4 * q) = make_uint2(0u, 0u);
     }
-  };
-  if (S > 0 && resident) load_chunk(t0);
+    return;
+  }
+
+  const int T = steps_of(K);
+  const uint8_t* __restrict__ Wp = Wall + (size_t)e * (payload_bytes(N, K) + scale_region_bytes(N, K));
+  StreamCTA<MT, NG, WK, PD, QB> cta;
+  cta.init(Wp, N, K, g0, 0, T, T, smem);
+  // RES: every wave's whole K share fits in its PD weight registers (checked by the host),
+  // so the weight is loaded once and reused for every row chunk.
 
   for (int r0 = 0; r0 < cnt; r0 += CH) {
     const int Mc = min(CH, cnt - r0);
     __syncthreads();  // the previous chunk is done with LDS
-    {
-      const int nbw = 4 * S;
-      const int nb = Mc * nbw;
-      for (int b = lane; b < nb; b += 64) {
-        const int m = b / nbw, kb = 4 * t0 + b % nbw;
-        const int tok = row_token[lo + r0 + m];
-        uint32_t x[16];
-        if (tok >= 0 && tok < Ttok) load_block(A + (size_t)tok * K + (size_t)kb * kBlock, x);
-        else zero_block(x);
-        uint32_t q[4];
-        const uint32_t s = quant_block(x, q);
-        *reinterpret_cast<uint4*>(aq + (size_t)m * RS + kb * 16) = make_uint4(q[0], q[1], q[2], q[3]);
-        as[(size_t)m * KB + kb] = (uint8_t)s;
-      }
-    }
+    const GatherRows rows{A, row_token, lo + r0, Ttok, K};
+    cta.quant(rows, Mc, [&] { if ((!RES || r0 == 0) && cta.S > 0) cta.load_w(cta.t0); });
     __syncthreads();
-
     v4f acc[NG][MT];
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    for (int tb = t0; tb < t1; tb += PD) {
-      if (!resident) load_chunk(tb);
-      const int nh = min(PD, t1 - tb);
-#pragma unroll
-      for (int i = 0; i < PD; ++i) {
-        if (i < nh) {
-          const int t = tb + i;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int m = 16 * mt + (lane & 15);
-            const int kb = 4 * t + (lane >> 4);
-            uint4 b = make_uint4(0u, 0u, 0u, 0u);
-            uint32_t sb = 0u;
-            if (m < Mc) {
-              b = *reinterpret_cast<const uint4*>(aq + (size_t)m * RS + kb * 16);
-              sb = as[(size_t)m * KB + kb];
-            }
-#pragma unroll
-            for (int g = 0; g < NG; ++g) acc[g][mt] = mfma_fp4(wq[i][g], b, acc[g][mt], wsb[i][g], sb);
-          }
-        }
-      }
-    }
-
-    auto store = [&](int g, int mt, const v4f& v) {
+    cta.mma(Mc, RES, acc);
+    __syncthreads();  // every wave is done with the activation region
+    cta.reduce_store(acc, smem, [&](int g, int mt, const v4f& v) {
       const int m = 16 * mt + (lane & 15);
       const int n = 16 * (g0 + g) + 4 * (lane >> 4);
       if (m < Mc)
         *reinterpret_cast<uint2*>(C + (size_t)(lo + r0 + m) * N + n) = pack4_bf16(v[0], v[1], v[2], v[3]);
-    };
-    __syncthreads();  // every wave is done with the activation region
-    v4f* red = reinterpret_cast<v4f*>(smem);  // [WK][NG*MT][64]
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) red[(w * NG * MT + g * MT + mt) * 64 + lane] = acc[g][mt];
-    __syncthreads();
-    for (int p = w; p < NG * MT; p += WK) {
-      v4f sum = red[p * 64 + lane];
-      for (int ww = 1; ww < WK; ++ww) sum += red[(ww * NG * MT + p) * 64 + lane];
-      store(p / MT, p % MT, sum);
-    }
+    });
   }
 }
 
@@ -603,7 +602,6 @@ hipError_t launch_unprepare(const void* wp, int64_t N, int64_t K, void* q, void*
 
 namespace {
 
-constexpr int kSkinnyPD = 16;
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU (and per workgroup) on gfx950
 
 // Raise a kernel's dynamic-LDS limit to the full 160 KiB once per device. `done` is the
@@ -619,15 +617,8 @@ hipError_t ensure_lds_limit(const void* kern, std::atomic<uint64_t>& done) {
   return e;
 }
 
-// LDS of the grouped kernel: quantized rows [M][K/2 + 16] and scales [M][K/32], or the
-// cross-wave reduction, whichever is larger.
-size_t skinny_lds_bytes(int M, int K, int MT, int NG, int WK) {
-  const size_t act = (size_t)M * (K / 2 + 16) + (size_t)M * (K / kBlock);
-  const size_t red = (size_t)WK * NG * MT * 64 * 16;
-  return act > red ? act : red;
-}
-
-// LDS of the streaming kernel for a slice of TS steps.
+// LDS of a StreamCTA with room for 16 * MT rows of a slice of TS steps: quantized rows, their
+// scales, or the cross-wave reduction, whichever is larger.
 size_t stream_lds_bytes(int M, int TS, int MT, int NG, int WK) {
   const size_t act = (size_t)M * (TS * 64 + 16) + (size_t)M * 4 * TS;
   const size_t red = (size_t)WK * NG * MT * 64 * 16;
@@ -651,15 +642,21 @@ struct GemmConfig {
   X(1, 4, 4, 4, 2, 1) X(2, 4, 4, 4, 2, 1) X(1, 4, 8, 4, 1, 1) X(2, 2, 4, 8, 1, 1) X(1, 4, 4, 2, 2, 1) \
   X(1, 4, 4, 4, 1, 2) X(1, 4, 4, 4, 2, 2) X(2, 4, 4, 4, 1, 1) X(1, 4, 4, 2, 2, 2)
 
-template <int MT, int NG, int WK>
-hipError_t run_stream(const void* a, const void* wp, void* c, float* P, int M, int N, int K, int S,
-                      hipStream_t st) {
-  auto kern = k_gemm_stream<MT, NG, WK, kSkinnyPD / NG>;
+// Weight prefetch depth: enough registers for a wave's whole K share when it fits (4, 8 or
+// 16 steps of NG operands, at most 16 operands), so no registers go to duplicate loads.
+template <int NG>
+int pick_pd(int steps_per_wave) {
+  constexpr int cap = kSkinnyPD / NG;
+  int pd = 4;
+  while (pd < steps_per_wave && pd < cap) pd *= 2;
+  return pd > cap ? cap : pd;
+}
+
+template <int MT, int NG, int WK, int PD, int QB>
+hipError_t launch_stream(const void* a, const void* wp, void* c, float* P, int M, int N, int K, int S,
+                         int TS, size_t lds, hipStream_t st) {
+  auto kern = k_gemm_stream<MT, NG, WK, PD, QB>;
   static std::atomic<uint64_t> configured{0};
-  const int T = steps_of(K);
-  const int TS = (T + S - 1) / S;
-  const size_t lds = stream_lds_bytes(M, TS, MT, NG, WK);
-  if (lds > kMaxLds) return hipErrorInvalidValue;
   if (lds > 65536) {
     hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), configured);
     if (e != hipSuccess) return e;
@@ -667,7 +664,32 @@ hipError_t run_stream(const void* a, const void* wp, void* c, float* P, int M, i
   hipLaunchKernelGGL(kern, dim3((unsigned)(N / (16 * NG)), (unsigned)S), dim3(64 * WK), lds, st,
                      static_cast<const uint16_t*>(a), static_cast<const uint8_t*>(wp),
                      static_cast<uint16_t*>(c), P, M, N, K, TS);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <int MT, int NG, int WK, int QB>
+hipError_t launch_stream_pd(int pd, const void* a, const void* wp, void* c, float* P, int M, int N, int K,
+                            int S, int TS, size_t lds, hipStream_t st) {
+  if constexpr (kSkinnyPD / NG >= 16)
+    if (pd >= 16) return launch_stream<MT, NG, WK, 16, QB>(a, wp, c, P, M, N, K, S, TS, lds, st);
+  if constexpr (kSkinnyPD / NG >= 8)
+    if (pd >= 8) return launch_stream<MT, NG, WK, 8, QB>(a, wp, c, P, M, N, K, S, TS, lds, st);
+  return launch_stream<MT, NG, WK, 4, QB>(a, wp, c, P, M, N, K, S, TS, lds, st);
+}
+
+template <int MT, int NG, int WK>
+hipError_t run_stream(const void* a, const void* wp, void* c, float* P, int M, int N, int K, int S,
+                      hipStream_t st) {
+  const int T = steps_of(K);
+  const int TS = (T + S - 1) / S;
+  const size_t lds = stream_lds_bytes(16 * MT, TS, MT, NG, WK);
+  if (lds > kMaxLds) return hipErrorInvalidValue;
+  const int per = (TS + WK - 1) / WK;
+  const int pd = pick_pd<NG>(per);
+  // a wave's activation blocks fit one lane each: one quant batch, fewer registers;
+  // otherwise four blocks per lane in flight per batch
+  hipError_t e = M * 4 * per <= 64 ? launch_stream_pd<MT, NG, WK, 1>(pd, a, wp, c, P, M, N, K, S, TS, lds, st)
+                                   : launch_stream_pd<MT, NG, WK, 4>(pd, a, wp, c, P, M, N, K, S, TS, lds, st);
   if (e != hipSuccess || S == 1) return e;
   const int64_t MN = (int64_t)M * N;
   hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, st, P,
@@ -732,7 +754,7 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   auto stream_fits = [&](const GemmConfig& s) {
     const int TS = (T + s.S - 1) / s.S;
     const size_t need = s.S > 1 ? (size_t)s.S * M * N * 4 : 0;
-    return need <= ws_bytes && stream_lds_bytes(M, TS, s.MT, s.NG, s.WK) <= kMaxLds && G % s.NG == 0;
+    return need <= ws_bytes && stream_lds_bytes(16 * s.MT, TS, s.MT, s.NG, s.WK) <= kMaxLds && G % s.NG == 0;
   };
   if (M <= 32 || (M <= 128 && G <= 96)) {
     // weight-streaming kernel: the weight is read once, straight into registers
@@ -813,7 +835,7 @@ hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M64, int6
     const size_t need = cfg.S > 1 ? (size_t)cfg.S * M * N * 4 : 0;
     const int TS = (T + cfg.S - 1) / cfg.S;
     if (M > 16 * cfg.MT || need > ws_bytes || (N / 16) % cfg.NG != 0 ||
-        stream_lds_bytes(M, TS, cfg.MT, cfg.NG, cfg.WK) > kMaxLds)
+        stream_lds_bytes(16 * cfg.MT, TS, cfg.MT, cfg.NG, cfg.WK) > kMaxLds)
       return hipErrorInvalidValue;
   }
   return run_config(cfg, a, wp, c, cfg.tile ? nullptr : (cfg.S > 1 ? static_cast<float*>(ws) : nullptr),
@@ -822,12 +844,11 @@ hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M64, int6
 
 namespace {
 
-template <int MT, int NG, int WK>
-hipError_t run_grouped(const void* a, const int32_t* rt, const int32_t* offs, int E, int R_max,
-                       const void* wp, void* c, int T, int N, int K, hipStream_t st) {
-  auto kern = k_gemm_grouped<MT, NG, WK, kSkinnyPD>;
+template <int MT, int NG, int WK, int PD, bool RES>
+hipError_t launch_grouped(const void* a, const int32_t* rt, const int32_t* offs, int E, int R_max,
+                          const void* wp, void* c, int T, int N, int K, size_t lds, hipStream_t st) {
+  auto kern = k_gemm_grouped<MT, NG, WK, PD, (MT == 1 ? 1 : 4), RES>;
   static std::atomic<uint64_t> configured{0};
-  const size_t lds = skinny_lds_bytes(16 * MT, K, MT, NG, WK);
   if (lds > 65536) {
     hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), configured);
     if (e != hipSuccess) return e;
@@ -839,15 +860,37 @@ hipError_t run_grouped(const void* a, const int32_t* rt, const int32_t* offs, in
   return hipGetLastError();
 }
 
+template <int MT, int NG, int WK>
+hipError_t run_grouped(const void* a, const int32_t* rt, const int32_t* offs, int E, int R_max,
+                       const void* wp, void* c, int T, int N, int K, hipStream_t st) {
+  const int steps = steps_of(K);
+  const size_t lds = stream_lds_bytes(16 * MT, steps, MT, NG, WK);
+  if (lds > kMaxLds) return hipErrorInvalidValue;
+  const int per = (steps + WK - 1) / WK;
+  const int pd = pick_pd<NG>(per);
+  if (per > pd) return launch_grouped<MT, NG, WK, kSkinnyPD / NG, false>(a, rt, offs, E, R_max, wp, c, T, N, K, lds, st);
+  if constexpr (kSkinnyPD / NG >= 16)
+    if (pd >= 16) return launch_grouped<MT, NG, WK, 16, true>(a, rt, offs, E, R_max, wp, c, T, N, K, lds, st);
+  if constexpr (kSkinnyPD / NG >= 8)
+    if (pd >= 8) return launch_grouped<MT, NG, WK, 8, true>(a, rt, offs, E, R_max, wp, c, T, N, K, lds, st);
+  return launch_grouped<MT, NG, WK, 4, true>(a, rt, offs, E, R_max, wp, c, T, N, K, lds, st);
+}
+
 }  // namespace
 
 hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const int32_t* offsets, int64_t E,
                                int64_t R_max, const void* wp, void* c, int64_t T, int64_t N, int64_t K,
                                int64_t rows_hint, hipStream_t st) {
   const int e = (int)E, r = (int)R_max, t = (int)T, n = (int)N, k = (int)K;
-  if (skinny_lds_bytes(32, k, 2, 4, 4) > kMaxLds) return hipErrorInvalidValue;
-  if (rows_hint <= 16) return run_grouped<1, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
-  if (rows_hint <= 32) return run_grouped<2, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+  const int G = n / 16;
+  // more weight columns per CTA as segments grow, to amortize each CTA's serial
+  // segment-lookup -> token -> activation latency chain over more streamed weight
+  const int64_t active = e < r ? e : r;
+  if (rows_hint <= 16) {
+    if (active < 128 || G % 4 != 0) return run_grouped<1, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+    return run_grouped<1, 4, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+  }
+  if (rows_hint <= 32 || G % 4 != 0) return run_grouped<2, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
   return run_grouped<2, 4, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
 }
 

@@ -51,7 +51,8 @@ def _run(cfg, a, wp, ws):
 
 
 def _stream_lds(M, TS, MT, NG, WK):
-    return max(M * (TS * 64 + 16) + M * 4 * TS, WK * NG * MT * 1024)
+    R = 16 * MT
+    return max(R * (TS * 64 + 16) + R * 4 * TS, WK * NG * MT * 1024)
 
 
 @pytest.mark.parametrize("K", K_TESTS)
