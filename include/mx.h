@@ -56,11 +56,9 @@ int mx_prepared_layout_version(void);
 
 /*
  * Size in bytes of a prepared MXFP4 weight of shape [N, K]: N*K/2 bytes of packed E2M1
- * payload followed by the E8M0 scales, N*16*ceil(K/512) bytes (the scales of four
- * consecutive 128-wide K steps share one 32-bit word per lane; a K that is not a
- * multiple of 512 pads its last word). For K a multiple of 512 this is N*K*17/32,
- * e.g. 32,169,984 bytes for 8448 x 7168 ("[gfx950][FlyDSL] Add direct dense A4W4
- * MXFP4 GEMM", Model validation). Returns 0 when N <= 0, K <= 0, N % 256 or K % 128.
+ * payload followed by N*K/32 bytes of E8M0 scales, N*K*17/32 in all, e.g. 32,169,984
+ * bytes for 8448 x 7168 ("[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", Model
+ * validation). Returns 0 when N <= 0, K <= 0, N % 256 or K % 128.
  */
 size_t mx_prepared_weight_bytes(int64_t N, int64_t K);
 

@@ -54,12 +54,11 @@ const char* mx_status_string(mx_status s) {
   return "MX_ERR_UNKNOWN";
 }
 
-int mx_prepared_layout_version(void) { return 1; }
+int mx_prepared_layout_version(void) { return 2; }
 
 size_t mx_prepared_weight_bytes(int64_t N, int64_t K) {
   if (!gemm_shape_ok(N, K)) return 0;
-  const size_t quads = (size_t)((K / 128 + 3) / 4);
-  return (size_t)N * (size_t)K / 2 + (size_t)N * 16 * quads;
+  return (size_t)N * (size_t)K / 2 + (size_t)N * (size_t)K / 32;
 }
 
 mx_status mx_prepare_weight(const void* w_bf16, int64_t N, int64_t K, void* w_prep, hipStream_t stream) {

@@ -21,7 +21,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBlock = 32;      // elements per E8M0 scale
 constexpr int kStepK = 128;     // K covered by one 16x16x128 MFMA
 constexpr int kFragBytes = 16;  // one lane's share of an MFMA operand: one 32-block
-constexpr int kLayoutVersion = 1;
+constexpr int kLayoutVersion = 2;
 
 // ------------------------------------------------------------------ prepared weight layout
 //
@@ -32,21 +32,23 @@ constexpr int kLayoutVersion = 1;
 // global_load_dwordx4 per lane fetches a whole operand and a wave's load is 1 KiB contiguous.
 // Tiles are ordered [g][t]: a column group's whole K range is contiguous.
 //
-// Scales: after the payload, for column group g and step quad t4 (steps 4t4..4t4+3) one
-// 32-bit word per lane whose byte j is the E8M0 scale of (n, kb = 4(4t4 + j) + l/16); the
-// byte index j is the MFMA's scale op_sel. A K that is not a multiple of 512 pads the last
-// word with zero bytes (ceil-sized scale region).
+// Scales: after the payload, for column-group quad q (groups 4q..4q+3, columns 64q..64q+63)
+// and K step t, one 32-bit word per lane l whose byte j is the E8M0 scale of
+// (n = 16 (4q + j) + l % 16, kb = 4t + l / 16). Byte j is the MFMA scale op_sel for column
+// group 4q + j, so a wave that owns four adjacent column groups fetches all their scales
+// for a step with one dword load per lane. The scale region is exactly N * K / 32 bytes.
 __host__ __device__ inline int steps_of(int K) { return K / kStepK; }
-__host__ __device__ inline int quads_of(int K) { return (K / kStepK + 3) / 4; }
 __host__ __device__ inline size_t payload_bytes(int64_t N, int64_t K) { return (size_t)N * (size_t)K / 2; }
-__host__ __device__ inline size_t scale_region_bytes(int64_t N, int64_t K) {
-  return (size_t)(N / 16) * (size_t)quads_of((int)K) * 256;
+__host__ __device__ inline size_t scale_region_bytes(int64_t N, int64_t K) { return (size_t)N * (size_t)K / 32; }
+__host__ __device__ inline size_t prepared_bytes(int64_t N, int64_t K) {
+  return payload_bytes(N, K) + scale_region_bytes(N, K);
 }
 __host__ __device__ inline size_t wp_payload_off(int g, int t, int lane, int T) {
   return (((size_t)g * T + t) * 64 + lane) * 16;
 }
-__host__ __device__ inline size_t wp_scale_off(int g, int t4, int lane, int T4) {
-  return (((size_t)g * T4 + t4) * 64 + lane) * 4;
+// byte offset of the scale word of (column-group quad q, step t, lane)
+__host__ __device__ inline size_t wp_scale_off(int q, int t, int lane, int T) {
+  return (((size_t)q * T + t) * 64 + lane) * 4;
 }
 
 // ------------------------------------------------------------------ bf16 helpers
@@ -120,6 +122,16 @@ __device__ __forceinline__ uint4 load16_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Load one 32-element bf16 block at byte offset `off` from a wave-uniform base (the
+// compiler can then use a scalar base with a 32-bit per-lane offset).
+__device__ __forceinline__ void load_block_at(const uint8_t* __restrict__ base, uint32_t off, uint32_t (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = *reinterpret_cast<const uint4*>(base + off + 16 * i);
+    x[4 * i + 0] = u.x; x[4 * i + 1] = u.y; x[4 * i + 2] = u.z; x[4 * i + 3] = u.w;
+  }
+}
+
 __device__ __forceinline__ void zero_block(uint32_t (&x)[16]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = 0u;
@@ -134,6 +146,14 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f acc,
   v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+// Same, with the scales taken from byte SA of sa and byte SB of sb (the op_sel fields).
+template <int SA, int SB>
+__device__ __forceinline__ v4f mfma_fp4_sel(const uint4& a, const uint4& b, v4f acc, uint32_t sa, uint32_t sb) {
+  v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, SA, (int)sa, SB, (int)sb);
 }
 
 }  // namespace mx

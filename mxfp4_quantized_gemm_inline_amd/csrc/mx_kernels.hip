@@ -38,39 +38,37 @@ __global__ __launch_bounds__(256) void k_quant_act(const uint16_t* __restrict__ 
 
 // ====================================================================== weight prepare
 
-// One thread per (column group g, step quad t4, lane): quantizes the up to four 32-blocks
-// that lane owns in steps 4t4..4t4+3 and writes them and their scale word in place.
+// One thread per (column-group quad q, step t, lane): quantizes the four 32-blocks that lane
+// owns in column groups 4q..4q+3 at step t and writes them and their scale word in place.
 __global__ __launch_bounds__(256) void k_prepare(const uint16_t* __restrict__ W,
                                                   uint8_t* __restrict__ Wp, int N, int K) {
-  const int T = steps_of(K), T4 = quads_of(K), G = N / 16;
+  const int T = steps_of(K), Q = N / 64;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)G * T4 * 64) return;
+  if (idx >= (int64_t)Q * T * 64) return;
   const int lane = (int)(idx % 64);
   const int64_t r = idx / 64;
-  const int t4 = (int)(r % T4), g = (int)(r / T4);
-  const int n = 16 * g + (lane & 15);
+  const int t = (int)(r % T), q = (int)(r / T);
+  const int kb = 4 * t + (lane >> 4);
   uint32_t sword = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int t = 4 * t4 + j;
-    if (t < T) {
-      const int kb = 4 * t + (lane >> 4);
-      uint32_t x[16];
-      load_block(W + (size_t)n * K + (size_t)kb * kBlock, x);
-      uint32_t qq[4];
-      const uint32_t sc = quant_block(x, qq);
-      *reinterpret_cast<uint4*>(Wp + wp_payload_off(g, t, lane, T)) = make_uint4(qq[0], qq[1], qq[2], qq[3]);
-      sword |= sc << (8 * j);
-    }
+    const int g = 4 * q + j;
+    const int n = 16 * g + (lane & 15);
+    uint32_t x[16];
+    load_block(W + (size_t)n * K + (size_t)kb * kBlock, x);
+    uint32_t qq[4];
+    const uint32_t sc = quant_block(x, qq);
+    *reinterpret_cast<uint4*>(Wp + wp_payload_off(g, t, lane, T)) = make_uint4(qq[0], qq[1], qq[2], qq[3]);
+    sword |= sc << (8 * j);
   }
-  *reinterpret_cast<uint32_t*>(Wp + payload_bytes(N, K) + wp_scale_off(g, t4, lane, T4)) = sword;
+  *reinterpret_cast<uint32_t*>(Wp + payload_bytes(N, K) + wp_scale_off(q, t, lane, T)) = sword;
 }
 
 // Inverse of the preshuffle: canonical payload [N, K/2] and scales [N, K/32].
 __global__ __launch_bounds__(256) void k_unprepare(const uint8_t* __restrict__ Wp,
                                                     uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ s, int N, int K) {
-  const int T = steps_of(K), T4 = quads_of(K), G = N / 16, KB = K / kBlock;
+  const int T = steps_of(K), G = N / 16, KB = K / kBlock;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)G * T * 64) return;
   const int lane = (int)(idx % 64);
@@ -80,8 +78,8 @@ __global__ __launch_bounds__(256) void k_unprepare(const uint8_t* __restrict__ W
   const uint4 v = *reinterpret_cast<const uint4*>(Wp + wp_payload_off(g, t, lane, T));
   *reinterpret_cast<uint4*>(q + (size_t)n * (K / 2) + (size_t)kb * 16) = v;
   const uint32_t sword =
-      *reinterpret_cast<const uint32_t*>(Wp + payload_bytes(N, K) + wp_scale_off(g, t >> 2, lane, T4));
-  s[(size_t)n * KB + kb] = (uint8_t)(sword >> (8 * (t & 3)));
+      *reinterpret_cast<const uint32_t*>(Wp + payload_bytes(N, K) + wp_scale_off(g >> 2, t, lane, T));
+  s[(size_t)n * KB + kb] = (uint8_t)(sword >> (8 * (g & 3)));
 }
 
 // ====================================================================== streaming GEMM (small and mid M)
@@ -127,7 +125,7 @@ struct GatherRows {
 
 template <int MT, int NG, int WK, int PD, int QB>
 struct StreamCTA {
-  int lane, T, T4, g0, ks0, t0, t1, S, RS, SB;
+  int lane, T, g0, ks0, t0, t1, S, RS, SB;
   const uint8_t* __restrict__ Wp;
   const uint8_t* __restrict__ Wsc;
   uint8_t* aq;
@@ -140,7 +138,6 @@ struct StreamCTA {
     lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     T = steps_of(K);
-    T4 = quads_of(K);
     g0 = g0_;
     ks0 = ks0_;
     const int slice = ks1 - ks0;
@@ -163,7 +160,8 @@ struct StreamCTA {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         wq[i][g] = load16_nt(Wp + wp_payload_off(g0 + g, t, lane, T));
-        wsb[i][g] = __builtin_nontemporal_load(Wsc + wp_scale_off(g0 + g, t >> 2, lane, T4) + (t & 3));
+        // the scale byte of group g0+g sits in byte (g0+g)%4 of its quad's word
+        wsb[i][g] = __builtin_nontemporal_load(Wsc + wp_scale_off((g0 + g) >> 2, t, lane, T) + ((g0 + g) & 3));
       }
     }
   }
@@ -357,7 +355,7 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
   __shared__ __align__(16) uint8_t sq[2][MTC * 64 * 16];
   __shared__ __align__(16) uint8_t ss[2][MTC * 64];
 
-  const int T = steps_of(K), T4 = quads_of(K), G = N / 16;
+  const int T = steps_of(K), G = N / 16;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int bm, bn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, GM, bm, bn);
@@ -370,36 +368,40 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
 
   // Loads are branch-free so the compiler can count them: rows past M re-read row M-1
   // and column groups past N re-read the last group; neither result is ever stored.
-  const uint16_t* arow[BPT];
+  // Bases are wave-uniform; only 32-bit lane offsets live in vector registers.
+  const uint8_t* __restrict__ A8 = reinterpret_cast<const uint8_t*>(A);
+  uint32_t aoff[BPT];
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     const int b = threadIdx.x + i * NTH;
-    arow[i] = A + (size_t)min(m0 + (b >> 2), M - 1) * K + (b & 3) * kBlock;
+    aoff[i] = (uint32_t)((size_t)min(m0 + (b >> 2), M - 1) * K * 2 + (b & 3) * kBlock * 2);
   }
-  size_t woff[NG], soff[NG];
+  constexpr int NQ = (NG + 3) / 4;  // scale words per step: one per column-group quad
+  const uint8_t* wbase[NG];
+  const uint8_t* sbase[NQ];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int gc = min(gw0 + g, G - 1);
-    woff[g] = wp_payload_off(gc, 0, lane, T);
-    soff[g] = wp_scale_off(gc, 0, lane, T4);
-  }
+  for (int g = 0; g < NG; ++g) wbase[g] = Wp + (size_t)min(gw0 + g, G - 1) * T * 1024;
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) sbase[qi] = Wsc + (size_t)min((gw0 >> 2) + qi, G / 4 - 1) * T * 256;
+  const uint32_t wlane = lane * 16, slane = lane * 4;
+  const int sbyte = gw0 & 3;  // byte of group gw0 in its scale word (0 when NG % 4 == 0)
 
   uint32_t areg[PF][BPT][16];
   uint4 wq[PF + 1][NG];
-  uint32_t wsc[PF + 1][NG];
+  uint32_t wsw[PF + 1][NQ];
 
   auto load_a = [&](int t, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
+    const uint8_t* base = A8 + (size_t)t * kStepK * 2;
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) load_block(arow[i] + (size_t)t * kStepK, areg[SL][i]);
+    for (int i = 0; i < BPT; ++i) load_block_at(base, aoff[i], areg[SL][i]);
   };
   auto load_w = [&](int t, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      wq[SL][g] = *reinterpret_cast<const uint4*>(Wp + woff[g] + (size_t)t * 1024);  // reused: cached
-      wsc[SL][g] = Wsc[soff[g] + (size_t)(t >> 2) * 256 + (t & 3)];
-    }
+    for (int g = 0; g < NG; ++g) wq[SL][g] = *reinterpret_cast<const uint4*>(wbase[g] + (size_t)t * 1024 + wlane);
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) wsw[SL][qi] = *reinterpret_cast<const uint32_t*>(sbase[qi] + (size_t)t * 256 + slane);
   };
 
   v4f acc[NG][MT];
@@ -439,10 +441,18 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
       b[mt] = *reinterpret_cast<const uint4*>(&sq[buf][slot * 16]);
       sb[mt] = ss[buf][slot];
     }
+    static_for<NG>([&](auto g_c) {
+      constexpr int g = decltype(g_c)::value;
+      if constexpr (NG % 4 == 0) {  // aligned quads: the group's byte is a compile-time op_sel
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+        for (int mt = 0; mt < MT; ++mt)
+          acc[g][mt] = mfma_fp4_sel<g & 3, 0>(wq[SW][g], b[mt], acc[g][mt], wsw[SW][g >> 2], sb[mt]);
+      } else {
+        const uint32_t sw = wsw[SW][0] >> (8 * (sbyte + g));
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[g][mt] = mfma_fp4(wq[SW][g], b[mt], acc[g][mt], wsc[SW][g], sb[mt]);
+        for (int mt = 0; mt < MT; ++mt) acc[g][mt] = mfma_fp4(wq[SW][g], b[mt], acc[g][mt], sw, sb[mt]);
+      }
+    });
   };
 
   constexpr int U = PF * (PF + 1);
@@ -464,6 +474,178 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = m0 + 16 * (wm * MT + mt) + (lane & 15);
+        const int n = 16 * (gw0 + g) + 4 * (lane >> 4);
+        if (m < M)
+          *reinterpret_cast<uint2*>(C + (size_t)m * N + n) =
+              pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
+      }
+    }
+  }
+}
+
+// ====================================================================== wide-tile GEMM (large M)
+//
+// One wave per SIMD, four waves side by side along N: a CTA owns a BM x BN tile with
+// BM = 16 * MT rows and BN = 64 * NG columns, each wave MT x NG MFMA tiles (accumulators
+// live in the unified register file, 4 * MT * NG per lane). Wide N per CTA cuts both the
+// activation re-reads (each bf16 A row is read N / BN times) and the redundant inline
+// quantization (about 208 / BN of the MFMA time). With MT = 8 and NG = ceil(G / 64) the
+// tile grid is 16 x 16 for M = 2048, one tile per CU.
+//
+// Software pipeline, per K step t: the MFMAs of step t are issued in the same stretch of
+// code as the quantization of step t+1 (whose bf16 loads were issued a step earlier), so a
+// single wave keeps the matrix core and the vector ALU busy together; then the step-(t+1)
+// operands go to LDS, loads for step t+2 are issued, one barrier, and the step-(t+1)
+// activation operands are read back. Weight operands for step t+1 load straight into
+// registers one step ahead. Column groups past N (a tail tile) re-load the last group and
+// are never stored; rows past M re-read row M-1 and are never stored.
+//
+// The activation store to LDS is bank-conflict free: thread (wave v, lane l) quantizes row
+// 16 * (tile) + (l % 16), block l / 16, so a wave writes 64 consecutive 16-byte slots.
+template <int MT, int NG>
+__global__ __launch_bounds__(256) void k_gemm_wide(const uint16_t* __restrict__ A,
+                                                   const uint8_t* __restrict__ Wp,
+                                                   uint16_t* __restrict__ C, int M, int N, int K,
+                                                   int GM) {
+  constexpr int BM = 16 * MT, BNG = 4 * NG;   // rows, column groups per CTA
+  constexpr int NBLK = 4 * BM;                // 32-blocks of A per K step
+  static_assert(NBLK % 256 == 0, "every thread quantizes the same number of blocks");
+  constexpr int BPT = NBLK / 256;             // blocks per thread per step (= MT / 4)
+  __shared__ __align__(16) uint8_t sq[2][MT * 64 * 16];
+  __shared__ __align__(16) uint8_t ss[2][MT * 64];
+
+  const int T = steps_of(K), G = N / 16;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (G + BNG - 1) / BNG;
+  int bm, bn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, GM, bm, bn);
+  const int m0 = bm * BM;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw0 = bn * BNG + w * NG;
+  const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
+
+  // thread -> (16-row tile, row, block): consecutive lanes write consecutive LDS slots
+  const uint8_t* __restrict__ A8 = reinterpret_cast<const uint8_t*>(A);
+  uint32_t aoff[BPT];
+  int aslot[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const int tile = w + 4 * i;                 // 16-row tile index within the CTA
+    const int r = 16 * tile + (lane & 15);
+    aslot[i] = tile * 64 + lane;                // = tile*64 + (r%16) + 16*block
+    aoff[i] = (uint32_t)((size_t)min(m0 + r, M - 1) * K * 2 + (lane >> 4) * kBlock * 2);
+  }
+  // Column-group bases are wave-uniform (scalar registers); only the lane offset is per lane.
+  constexpr int NQ = (NG + 3) / 4;
+  const uint8_t* wbase[NG];
+  const uint8_t* sbase[NQ];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) wbase[g] = Wp + (size_t)min(gw0 + g, G - 1) * T * 1024;
+#pragma unroll
+  for (int qi = 0; qi < NQ; ++qi) sbase[qi] = Wsc + (size_t)min((gw0 >> 2) + qi, G / 4 - 1) * T * 256;
+  const uint32_t wlane = lane * 16, slane = lane * 4;
+  const int sbyte = gw0 & 3;
+
+  uint32_t areg[BPT][16];
+  uint4 wq[2][NG];
+  uint32_t wsw[2][NQ];
+  uint4 af[MT];
+  uint32_t asc[MT];
+
+  auto load_a = [&](int t) {
+    const uint8_t* base = A8 + (size_t)t * kStepK * 2;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) load_block_at(base, aoff[i], areg[i]);
+  };
+  auto load_w = [&](int t, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) wq[SL][g] = *reinterpret_cast<const uint4*>(wbase[g] + (size_t)t * 1024 + wlane);
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) wsw[SL][qi] = *reinterpret_cast<const uint32_t*>(sbase[qi] + (size_t)t * 256 + slane);
+  };
+  auto quant_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      uint32_t q[4];
+      const uint32_t sc = quant_block(areg[i], q);
+      *reinterpret_cast<uint4*>(&sq[buf][aslot[i] * 16]) = make_uint4(q[0], q[1], q[2], q[3]);
+      ss[buf][aslot[i]] = (uint8_t)sc;
+    }
+  };
+  auto read_frags = [&](int buf) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      af[mt] = *reinterpret_cast<const uint4*>(&sq[buf][(mt * 64 + lane) * 16]);
+      asc[mt] = ss[buf][mt * 64 + lane];
+    }
+  };
+
+  v4f acc[NG][MT];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: step 0 quantized and its operands read; step 1 loads in flight
+  load_a(0);
+  load_w(0, std::integral_constant<int, 0>{});
+  quant_store(0);
+  load_a(min(1, T - 1));
+  load_w(min(1, T - 1), std::integral_constant<int, 1>{});
+  __syncthreads();
+  read_frags(0);
+
+  auto mfmas = [&](auto sw_c) {
+    constexpr int SW = decltype(sw_c)::value;
+    static_for<NG>([&](auto g_c) {
+      constexpr int g = decltype(g_c)::value;
+      if constexpr (NG % 4 == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[g][mt] = mfma_fp4_sel<g & 3, 0>(wq[SW][g], af[mt], acc[g][mt], wsw[SW][g >> 2], asc[mt]);
+      } else {
+        const uint32_t sw = wsw[SW][0] >> (8 * (sbyte + g));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[g][mt] = mfma_fp4(wq[SW][g], af[mt], acc[g][mt], sw, asc[mt]);
+      }
+    });
+  };
+  // One step t that has a successor: its MFMAs and step t+1's quantization in one basic
+  // block (so they can be interleaved), then the step-(t+2) loads, one barrier, and the
+  // step-(t+1) activation operands.
+  // Scheduling fences keep the phases in order, so the compiler cannot hoist the next
+  // step's loads above this step's MFMAs (which would double the live operand registers).
+  auto step = [&](int t, auto sw_c) {
+    mfmas(sw_c);
+    quant_store((t + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int tn = min(t + 2, T - 1);  // past the end: a harmless re-load of the last step
+    load_a(tn);
+    load_w(tn, sw_c);                  // the slot step t just consumed
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    read_frags((t + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int t = 0;
+  for (; t + 2 < T; t += 2) {  // straight-line body: both steps have a successor
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
+  }
+  if (t + 1 < T) {  // two steps left
+    step(t, std::integral_constant<int, 0>{});
+    mfmas(std::integral_constant<int, 1>{});
+  } else {          // one step left
+    mfmas(std::integral_constant<int, 0>{});
+  }
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (gw0 + g < G) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = m0 + 16 * mt + (lane & 15);
         const int n = 16 * (gw0 + g) + 4 * (lane >> 4);
         if (m < M)
           *reinterpret_cast<uint2*>(C + (size_t)m * N + n) =
@@ -550,7 +732,7 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_grouped(const uint16_t* __rest
   }
 
   const int T = steps_of(K);
-  const uint8_t* __restrict__ Wp = Wall + (size_t)e * (payload_bytes(N, K) + scale_region_bytes(N, K));
+  const uint8_t* __restrict__ Wp = Wall + (size_t)e * prepared_bytes(N, K);
   StreamCTA<MT, NG, WK, PD, QB> cta;
   cta.init(Wp, N, K, g0, 0, T, T, smem);
   // RES: every wave's whole K share fits in its PD weight registers (checked by the host),
@@ -586,7 +768,7 @@ hipError_t launch_quant_act(const void* a, int64_t M, int64_t K, void* q, void* 
 }
 
 hipError_t launch_prepare(const void* w, int64_t N, int64_t K, void* wp, hipStream_t st) {
-  const int64_t n = (N / 16) * quads_of((int)K) * 64;
+  const int64_t n = (N / 64) * steps_of((int)K) * 64;
   hipLaunchKernelGGL(k_prepare, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(w), static_cast<uint8_t*>(wp), (int)N, (int)K);
   return hipGetLastError();
@@ -628,6 +810,7 @@ size_t stream_lds_bytes(int M, int TS, int MT, int NG, int WK) {
 // ---------------------------------------------------------------- configurations
 struct GemmConfig {
   bool tile = false;
+  bool wide = false;                     // wide-tile kernel (uses MT, NG, GM)
   int MT = 1, NG = 1, WK = 4, S = 1;     // streaming kernel (S = K slices)
   int WM = 1, WN = 4, PF = 2, GM = 8;    // tiled kernel (uses MT, NG too)
   int OCC = 1;                           // tiled kernel: minimum waves per SIMD asked of the compiler
@@ -637,6 +820,8 @@ struct GemmConfig {
   X(1, 1, 2) X(1, 1, 4) X(1, 1, 8) X(1, 2, 4) X(1, 2, 8) X(1, 4, 4) \
   X(2, 1, 2) X(2, 1, 4) X(2, 1, 8) X(2, 2, 4) X(2, 2, 8) X(2, 4, 4) \
   X(4, 1, 4) X(4, 1, 8) X(4, 2, 4) X(4, 4, 4) X(8, 1, 4) X(8, 2, 4)
+
+#define MX_WIDE_CONFIGS(X) X(8, 2) X(8, 4) X(4, 4) X(4, 8)
 
 #define MX_TILE_CONFIGS(X) \
   X(1, 4, 4, 4, 2, 1) X(2, 4, 4, 4, 2, 1) X(1, 4, 8, 4, 1, 1) X(2, 2, 4, 8, 1, 1) X(1, 4, 4, 2, 2, 1) \
@@ -707,6 +892,24 @@ hipError_t run_tile(const void* a, const void* wp, void* c, int M, int N, int K,
   return hipGetLastError();
 }
 
+template <int MT, int NG>
+hipError_t run_wide(const void* a, const void* wp, void* c, int M, int N, int K, int GM, hipStream_t st) {
+  constexpr int BM = 16 * MT, BNG = 4 * NG;
+  const int G = N / 16;
+  const int64_t grid = (int64_t)((M + BM - 1) / BM) * ((G + BNG - 1) / BNG);
+  hipLaunchKernelGGL((k_gemm_wide<MT, NG>), dim3((unsigned)grid), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(a), static_cast<const uint8_t*>(wp),
+                     static_cast<uint16_t*>(c), M, N, K, GM);
+  return hipGetLastError();
+}
+
+bool wide_supported(int MT, int NG) {
+#define X(mt, ng) if (MT == mt && NG == ng) return true;
+  MX_WIDE_CONFIGS(X)
+#undef X
+  return false;
+}
+
 bool stream_supported(int MT, int NG, int WK) {
 #define X(mt, ng, wk) if (MT == mt && NG == ng && WK == wk) return true;
   MX_STREAM_CONFIGS(X)
@@ -724,6 +927,12 @@ bool tile_supported(const GemmConfig& c) {
 
 hipError_t run_config(const GemmConfig& c, const void* a, const void* wp, void* out, float* P, int M,
                       int N, int K, hipStream_t st) {
+  if (c.wide) {
+#define X(mt, ng) if (c.MT == mt && c.NG == ng) return run_wide<mt, ng>(a, wp, out, M, N, K, c.GM, st);
+    MX_WIDE_CONFIGS(X)
+#undef X
+    return hipErrorInvalidValue;
+  }
   if (!c.tile) {
 #define X(mt, ng, wk) \
   if (c.MT == mt && c.NG == ng && c.WK == wk) return run_stream<mt, ng, wk>(a, wp, out, P, M, N, K, c.S, st);
@@ -782,14 +991,15 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   }
   // tiled kernel: 64 x 256 tiles when there are enough of them, else 64 x 128
   c.tile = true;
-  c.WM = 1; c.WN = 4; c.MT = 4; c.PF = 2; c.OCC = 2;
+  c.WM = 1; c.WN = 4; c.MT = 4; c.OCC = 2;
   const int64_t tiles256 = (int64_t)((M + 63) / 64) * ((N + 255) / 256);
-  if (tiles256 >= 150) { c.NG = 4; c.GM = 8; }
-  else { c.NG = 2; c.GM = 16; }
+  if (tiles256 >= 150) { c.NG = 4; c.PF = M >= 1024 || G >= 512 ? 1 : 2; c.GM = 8; }
+  else { c.NG = 2; c.PF = 2; c.GM = 16; }
   return c;
 }
 
-// Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming) or "t,WM,WN,MT,NG,PF,GM[,OCC]" (tiled)
+// Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming), "t,WM,WN,MT,NG,PF,GM[,OCC]" (tiled)
+// or "w,MT,NG,GM" (wide-tile)
 // replaces the default choice. Returns 0 when unset, 1 when applied, -1 when the string
 // does not name a compiled configuration (the call then fails rather than silently
 // running something else).
@@ -801,6 +1011,9 @@ int override_config(GemmConfig& c) {
   if (e[0] == 's' && std::sscanf(e, "s,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) == 4) {
     o.tile = false; o.MT = v[0]; o.NG = v[1]; o.WK = v[2]; o.S = v[3];
     if (!stream_supported(o.MT, o.NG, o.WK) || o.S < 1) return -1;
+  } else if (e[0] == 'w' && std::sscanf(e, "w,%d,%d,%d", &v[0], &v[1], &v[2]) == 3) {
+    o.tile = true; o.wide = true; o.MT = v[0]; o.NG = v[1]; o.GM = v[2] < 1 ? 1 : v[2];
+    if (!wide_supported(o.MT, o.NG)) return -1;
   } else if (e[0] == 't' && std::sscanf(e, "t,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6]) >= 6) {
     o.tile = true; o.WM = v[0]; o.WN = v[1]; o.MT = v[2]; o.NG = v[3]; o.PF = v[4]; o.GM = v[5] < 1 ? 1 : v[5];
     o.OCC = v[6] < 1 ? 1 : v[6];

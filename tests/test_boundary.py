@@ -43,12 +43,12 @@ def test_status_strings():
 
 def test_prepared_bytes():
     assert mx.mx_prepared_weight_bytes(8448, 7168) == 32_169_984      # the page's figure
-    assert mx.mx_prepared_weight_bytes(7168, 768) == 7168 * 384 + 7168 * 16 * 2
-    assert mx.mx_prepared_weight_bytes(7168, 4224) == 7168 * 2112 + 7168 * 16 * 9  # ceil(33/4) words
+    assert mx.mx_prepared_weight_bytes(7168, 768) == 7168 * 768 * 17 // 32
+    assert mx.mx_prepared_weight_bytes(7168, 4224) == 7168 * 4224 * 17 // 32
     assert mx.mx_prepared_weight_bytes(1536, 3584) == 2_924_544
     for n, k in [(0, 256), (256, 0), (100, 256), (256, 100), (-256, 256), (256, 64)]:
         assert mx.mx_prepared_weight_bytes(n, k) == 0
-    assert mx.mx_prepared_layout_version() == 1
+    assert mx.mx_prepared_layout_version() == 2
     assert mx.mx_a4w4_gemm_workspace_bytes(1, 7168, 768) >= 0
 
 

@@ -22,6 +22,7 @@ STREAM = [(1, 1, 2), (1, 1, 4), (1, 1, 8), (1, 2, 4), (1, 2, 8), (1, 4, 4),
           (4, 1, 4), (4, 1, 8), (4, 2, 4), (4, 4, 4), (8, 1, 4), (8, 2, 4)]
 TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8, 1, 1), (1, 4, 4, 2, 2, 1),
         (1, 4, 4, 4, 1, 2), (1, 4, 4, 4, 2, 2), (2, 4, 4, 4, 1, 1), (1, 4, 4, 2, 2, 2)]
+WIDE = [(8, 2), (8, 4), (4, 4), (4, 8)]
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
 K_TESTS = (4224, 768)  # 33 and 6 steps of 128
 LDS_MAX = 160 * 1024
@@ -80,6 +81,17 @@ def test_tile_config(cfg, K):
         c = _run("t," + ",".join(map(str, cfg[:5])) + f",{gm},{cfg[5]}", a[:M], wp, False)
         torch.cuda.synchronize()
         check_gemm(c, exact[:M], what=f"tile {cfg} GM={gm} M={M} K={K}")
+
+
+@pytest.mark.parametrize("K", K_TESTS)
+@pytest.mark.parametrize("cfg", WIDE, ids=[f"w{c}" for c in WIDE])
+def test_wide_config(cfg, K):
+    torch = torch_or_skip()
+    a, wp, exact = _case(K)
+    for M, gm in ((300, 8), (37, 1), (129, 3)):
+        c = _run(f"w,{cfg[0]},{cfg[1]},{gm}", a[:M], wp, False)
+        torch.cuda.synchronize()
+        check_gemm(c, exact[:M], what=f"wide {cfg} GM={gm} M={M} K={K}")
 
 
 def test_invalid_override_fails_loudly():

@@ -111,12 +111,21 @@ def test_prepare_moe_expert_shape():
     assert np.array_equal(host_u8(s), so) and np.array_equal(host_u8(q), qo)
 
 
-def test_prepare_scale_padding_is_zero():
-    """K = 4224 is 33 steps of 128: the last scale word of each lane holds one real byte."""
-    torch = torch_or_skip()
+def test_prepared_layout_scale_words():
+    """Scale word (quad q, step t, lane l) byte j is the scale of column 16(4q+j) + l%16 and
+    K block 4t + l/16 (checked against the oracle's canonical scales, K = 4224 = 33 steps)."""
+    torch_or_skip()
     mx = lib_or_fail()
     N, K = 256, 4224
     w = W.dense_weight(N, K, seed=77)
     wp = host_u8(mx.mx_prepare_weight(dev_bf16(w)))
-    words = wp[N * K // 2:].view(np.uint32).reshape(N // 16, 9, 64)
-    assert np.all((words[:, 8, :] >> 8) == 0)
+    assert wp.size == N * K * 17 // 32
+    _, so = O.quantize_mx(w)
+    T = K // 128
+    words = wp[N * K // 2:].view(np.uint32).reshape(N // 64, T, 64)
+    for q in range(N // 64):
+        for t in (0, 7, T - 1):
+            for l in (0, 17, 63):
+                for j in range(4):
+                    n, kb = 16 * (4 * q + j) + l % 16, 4 * t + l // 16
+                    assert (int(words[q, t, l]) >> (8 * j)) & 0xFF == so[n, kb]
