@@ -346,14 +346,15 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
                                                             const uint8_t* __restrict__ Wp,
                                                             uint16_t* __restrict__ C, int M, int N,
                                                             int K, int GM) {
-  constexpr int NTH = 64 * WM * WN;
   constexpr int MTC = MT * WM;  // 16-row tiles per CTA
   constexpr int BM = 16 * MTC, BN = 16 * NG * WN;
-  constexpr int NBLK = 4 * BM;
-  static_assert(NBLK % NTH == 0, "every thread quantizes the same number of blocks");
-  constexpr int BPT = NBLK / NTH;
+  constexpr int NW = WM * WN;
+  static_assert(MTC % NW == 0, "every wave quantizes whole 16-row tiles");
+  constexpr int BPT = MTC / NW;  // 32-blocks per thread per step
   __shared__ __align__(16) uint8_t sq[2][MTC * 64 * 16];
-  __shared__ __align__(16) uint8_t ss[2][MTC * 64];
+  // activation scales as [lane][16-row tile] bytes: a lane's scales for four tiles are one word
+  __shared__ __align__(16) uint8_t ss[2][64 * MTC];
+  static_assert(MT % 4 == 0, "a wave's tiles cover whole scale words");
 
   const int T = steps_of(K), G = N / 16;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -370,12 +371,21 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
   // and column groups past N re-read the last group; neither result is ever stored.
   // Bases are wave-uniform; only 32-bit lane offsets live in vector registers.
   const uint8_t* __restrict__ A8 = reinterpret_cast<const uint8_t*>(A);
+  // Thread (wave v, lane l) quantizes, for i < BPT, row l / 4 of the 16-row tile v + NW i,
+  // 32-block l % 4 of the step, so four neighbouring lanes read one row's 256 contiguous
+  // bytes. In LDS a tile holds its 16 x 4 operand blocks row-major with the block index
+  // XOR-swizzled by the row; both the quant stores (row-major lanes) and the MFMA reads
+  // (lane = row + 16 block) then fall on distinct banks in every 8- or 16-lane phase.
   uint32_t aoff[BPT];
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    const int b = threadIdx.x + i * NTH;
-    aoff[i] = (uint32_t)((size_t)min(m0 + (b >> 2), M - 1) * K * 2 + (b & 3) * kBlock * 2);
+    const int r = 16 * (w + NW * i) + (lane >> 2);
+    aoff[i] = (uint32_t)((size_t)min(m0 + r, M - 1) * K * 2 + (lane & 3) * kBlock * 2);
   }
+  auto swz = [](int rr) { return ((rr >> 1) ^ (rr >> 2)) & 3; };
+  const uint32_t st_off = (uint32_t)(((lane >> 2) * 4 + ((lane & 3) ^ swz(lane >> 2))) * 16);
+  const uint32_t st_sc = (uint32_t)(((lane >> 2) + 16 * (lane & 3)) * MTC);  // operand lane's scale row
+  const uint32_t ld_off = (uint32_t)(((lane & 15) * 4 + ((lane >> 4) ^ swz(lane & 15))) * 16);
   constexpr int NQ = (NG + 3) / 4;  // scale words per step: one per column-group quad
   const uint8_t* wbase[NG];
   const uint8_t* sbase[NQ];
@@ -421,37 +431,35 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
     const int buf = t & 1;
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
-      const int b = threadIdx.x + i * NTH;
-      const int r = b >> 2, kbl = b & 3;
-      const int slot = (r >> 4) * 64 + (r & 15) + 16 * kbl;
+      const int tile = w + NW * i;
       uint32_t q[4];
       const uint32_t sc = quant_block(areg[SA][i], q);
-      *reinterpret_cast<uint4*>(&sq[buf][slot * 16]) = make_uint4(q[0], q[1], q[2], q[3]);
-      ss[buf][slot] = (uint8_t)sc;
+      *reinterpret_cast<uint4*>(&sq[buf][tile * 1024 + st_off]) = make_uint4(q[0], q[1], q[2], q[3]);
+      ss[buf][st_sc + tile] = (uint8_t)sc;
     }
     const int tn = min(t + PF, T - 1);  // past the end: a harmless re-load of the last step
     load_a(tn, sa_c);
     load_w(tn, std::integral_constant<int, (SW + PF) % (PF + 1)>{});
     __syncthreads();
     uint4 b[MT];
-    uint32_t sb[MT];
+    uint32_t sbw[MT / 4];  // byte mt % 4 of word mt / 4: the scale of this wave's tile mt
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int slot = (wm * MT + mt) * 64 + lane;
-      b[mt] = *reinterpret_cast<const uint4*>(&sq[buf][slot * 16]);
-      sb[mt] = ss[buf][slot];
-    }
+    for (int mt = 0; mt < MT; ++mt)
+      b[mt] = *reinterpret_cast<const uint4*>(&sq[buf][(wm * MT + mt) * 1024 + ld_off]);
+#pragma unroll
+    for (int j = 0; j < MT / 4; ++j)
+      sbw[j] = *reinterpret_cast<const uint32_t*>(&ss[buf][lane * MTC + wm * MT + 4 * j]);
     static_for<NG>([&](auto g_c) {
       constexpr int g = decltype(g_c)::value;
-      if constexpr (NG % 4 == 0) {  // aligned quads: the group's byte is a compile-time op_sel
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[g][mt] = mfma_fp4_sel<g & 3, 0>(wq[SW][g], b[mt], acc[g][mt], wsw[SW][g >> 2], sb[mt]);
-      } else {
-        const uint32_t sw = wsw[SW][0] >> (8 * (sbyte + g));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[g][mt] = mfma_fp4(wq[SW][g], b[mt], acc[g][mt], sw, sb[mt]);
-      }
+      static_for<MT>([&](auto m_c) {
+        constexpr int mt = decltype(m_c)::value;
+        if constexpr (NG % 4 == 0) {  // aligned quads: the group's byte is a compile-time op_sel
+          acc[g][mt] = mfma_fp4_sel<g & 3, mt & 3>(wq[SW][g], b[mt], acc[g][mt], wsw[SW][g >> 2], sbw[mt >> 2]);
+        } else {
+          acc[g][mt] = mfma_fp4_sel<0, mt & 3>(wq[SW][g], b[mt], acc[g][mt], wsw[SW][0] >> (8 * (sbyte + g)),
+                                               sbw[mt >> 2]);
+        }
+      });
     });
   };
 
