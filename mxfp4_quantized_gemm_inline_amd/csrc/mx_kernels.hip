@@ -371,20 +371,23 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
   // and column groups past N re-read the last group; neither result is ever stored.
   // Bases are wave-uniform; only 32-bit lane offsets live in vector registers.
   const uint8_t* __restrict__ A8 = reinterpret_cast<const uint8_t*>(A);
-  // Thread (wave v, lane l) quantizes, for i < BPT, row l / 4 of the 16-row tile v + NW i,
-  // 32-block l % 4 of the step, so four neighbouring lanes read one row's 256 contiguous
-  // bytes. In LDS a tile holds its 16 x 4 operand blocks row-major with the block index
-  // XOR-swizzled by the row; both the quant stores (row-major lanes) and the MFMA reads
-  // (lane = row + 16 block) then fall on distinct banks in every 8- or 16-lane phase.
+  // The quad of lanes 4r..4r+3 of wave v quantizes, for i < BPT, row r of the 16-row tile
+  // v + NW i: lane 4r+j holds the 16-byte chunk j of each of the step's four 32-blocks, so
+  // every load instruction of the quad reads one block's 64 contiguous bytes. In LDS a tile
+  // holds its 16 x 4 operand blocks row-major with the block index XOR-swizzled by the row;
+  // the quant stores (one word per lane and block) and the MFMA reads (lane = row + 16 block)
+  // then fall on distinct banks.
   uint32_t aoff[BPT];
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     const int r = 16 * (w + NW * i) + (lane >> 2);
-    aoff[i] = (uint32_t)((size_t)min(m0 + r, M - 1) * K * 2 + (lane & 3) * kBlock * 2);
+    aoff[i] = (uint32_t)((size_t)min(m0 + r, M - 1) * K * 2 + (lane & 3) * 16);
   }
   auto swz = [](int rr) { return ((rr >> 1) ^ (rr >> 2)) & 3; };
-  const uint32_t st_off = (uint32_t)(((lane >> 2) * 4 + ((lane & 3) ^ swz(lane >> 2))) * 16);
-  const uint32_t st_sc = (uint32_t)(((lane >> 2) + 16 * (lane & 3)) * MTC);  // operand lane's scale row
+  // LDS byte of this lane's word of block c within a tile is st_off ^ (c << 4) (bits 4-5
+  // of the unswizzled offset are zero, so the XOR applies the block swizzle)
+  const uint32_t st_off = (uint32_t)((lane >> 2) * 64 + (swz(lane >> 2) << 4) + (lane & 3) * 4);
+  const uint32_t st_sc = (uint32_t)(((lane >> 2) + 16 * (lane & 3)) * MTC);  // scale of block lane % 4
   const uint32_t ld_off = (uint32_t)(((lane & 15) * 4 + ((lane >> 4) ^ swz(lane & 15))) * 16);
   constexpr int NQ = (NG + 3) / 4;  // scale words per step: one per column-group quad
   const uint8_t* wbase[NG];
@@ -404,7 +407,7 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
     constexpr int SL = decltype(slot_c)::value;
     const uint8_t* base = A8 + (size_t)t * kStepK * 2;
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) load_block_at(base, aoff[i], areg[SL][i]);
+    for (int i = 0; i < BPT; ++i) load_quad_at(base, aoff[i], areg[SL][i]);
   };
   auto load_w = [&](int t, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
@@ -429,13 +432,17 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
   auto step = [&](int t, auto sa_c, auto sw_c) {
     constexpr int SA = decltype(sa_c)::value, SW = decltype(sw_c)::value;
     const int buf = t & 1;
+    // Keep each step's quantization inside its step: hoisted into the previous step, it
+    // would wait there on loads issued only one step earlier and void the prefetch depth.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
       const int tile = w + NW * i;
       uint32_t q[4];
-      const uint32_t sc = quant_block(areg[SA][i], q);
-      *reinterpret_cast<uint4*>(&sq[buf][tile * 1024 + st_off]) = make_uint4(q[0], q[1], q[2], q[3]);
-      ss[buf][st_sc + tile] = (uint8_t)sc;
+      const uint32_t sc = quant_quad4(areg[SA][i], q);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(&sq[buf][tile * 1024 + (st_off ^ (c << 4))]) = q[c];
+      ss[buf][st_sc + tile] = (uint8_t)(sc >> (8 * (lane & 3)));
     }
     const int tn = min(t + PF, T - 1);  // past the end: a harmless re-load of the last step
     load_a(tn, sa_c);
