@@ -351,9 +351,15 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
   constexpr int NW = WM * WN;
   static_assert(MTC % NW == 0, "every wave quantizes whole 16-row tiles");
   constexpr int BPT = MTC / NW;  // 32-blocks per thread per step
-  __shared__ __align__(16) uint8_t sq[2][MTC * 64 * 16];
-  // activation scales as [lane][16-row tile] bytes: a lane's scales for four tiles are one word
-  __shared__ __align__(16) uint8_t ss[2][64 * MTC];
+  // LDS: two buffers of quantized activation operands (sq) and their scales (ss), stored
+  // as [lane][16-row tile] bytes so a lane's scales for four tiles are one word; after the
+  // K loop the same memory stages the bf16 output tile (rows padded by 16 bytes).
+  constexpr int SQ = MTC * 1024, SS = 64 * MTC;
+  constexpr int CROW = BN * 2 + 16, CSTAGE = BM * CROW;
+  constexpr int SMEM = 2 * (SQ + SS) > CSTAGE ? 2 * (SQ + SS) : CSTAGE;
+  __shared__ __align__(16) uint8_t smem[SMEM];
+  auto sq = [&](int buf, int off) { return smem + buf * SQ + off; };
+  auto ss = [&](int buf, int off) { return smem + 2 * SQ + buf * SS + off; };
   static_assert(MT % 4 == 0, "a wave's tiles cover whole scale words");
 
   const int T = steps_of(K), G = N / 16;
@@ -441,8 +447,8 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
       uint32_t q[4];
       const uint32_t sc = quant_quad4(areg[SA][i], q);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(&sq[buf][tile * 1024 + (st_off ^ (c << 4))]) = q[c];
-      ss[buf][st_sc + tile] = (uint8_t)(sc >> (8 * (lane & 3)));
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(sq(buf, tile * 1024 + (st_off ^ (c << 4)))) = q[c];
+      *ss(buf, st_sc + tile) = (uint8_t)(sc >> (8 * (lane & 3)));
     }
     const int tn = min(t + PF, T - 1);  // past the end: a harmless re-load of the last step
     load_a(tn, sa_c);
@@ -452,10 +458,10 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
     uint32_t sbw[MT / 4];  // byte mt % 4 of word mt / 4: the scale of this wave's tile mt
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      b[mt] = *reinterpret_cast<const uint4*>(&sq[buf][(wm * MT + mt) * 1024 + ld_off]);
+      b[mt] = *reinterpret_cast<const uint4*>(sq(buf, (wm * MT + mt) * 1024 + ld_off));
 #pragma unroll
     for (int j = 0; j < MT / 4; ++j)
-      sbw[j] = *reinterpret_cast<const uint32_t*>(&ss[buf][lane * MTC + wm * MT + 4 * j]);
+      sbw[j] = *reinterpret_cast<const uint32_t*>(ss(buf, lane * MTC + wm * MT + 4 * j));
     static_for<NG>([&](auto g_c) {
       constexpr int g = decltype(g_c)::value;
       static_for<MT>([&](auto m_c) {
@@ -483,17 +489,30 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
     if (t + I < T) step(t + I, std::integral_constant<int, I % PF>{}, std::integral_constant<int, I % (PF + 1)>{});
   });
 
+  // Epilogue: each lane holds four consecutive columns of one row per MFMA tile; stage the
+  // tile in LDS as bf16, then every wave store writes 16 bytes per lane along whole rows.
+  __syncthreads();  // every wave has finished reading the operand buffers
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    if (gw0 + g < G) {
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = m0 + 16 * (wm * MT + mt) + (lane & 15);
-        const int n = 16 * (gw0 + g) + 4 * (lane >> 4);
-        if (m < M)
-          *reinterpret_cast<uint2*>(C + (size_t)m * N + n) =
-              pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = 16 * (wm * MT + mt) + (lane & 15);
+      const int cl = 16 * (wn * NG + g) + 4 * (lane >> 4);
+      *reinterpret_cast<uint2*>(smem + r * CROW + cl * 2) =
+          pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
+    }
+  __syncthreads();
+  constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+  static_assert((BM * CPR) % (64 * NW) == 0, "every thread stores the same number of chunks");
+  const int n0 = bn * BN;
+#pragma unroll
+  for (int i = 0; i < BM * CPR / (64 * NW); ++i) {
+    const int id = threadIdx.x + i * 64 * NW;
+    const int r = id / CPR, ch = id % CPR;
+    const int m = m0 + r, n = n0 + 8 * ch;
+    if (m < M && n < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * CROW + ch * 16);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * N + n));
     }
   }
 }
