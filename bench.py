@@ -148,17 +148,110 @@ def point_record(name, N, K, M, us_cold, us_warm, kernel=None):
     return rec
 
 
-def kernel_name(M, N, K):
-    """Which kernel family the library launches for this shape (mirrors its selection)."""
-    if M <= 32 and M * (K // 2 + 16) + M * (K // 32) <= 160 * 1024:
-        return "k_gemm_skinny"
-    return "k_gemm_tile"
+def kernel_name(mx, M, N, K):
+    """The kernel instantiation(s) the library launches for this shape (its own plan)."""
+    return mx.mx_a4w4_gemm_plan(M, N, K)
+
+
+# ----------------------------------------------------------------------------- HBM traffic
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["mxfp4_quantized_gemm_inline_amd/csrc/mx_kernels.hip",
+                  "mxfp4_quantized_gemm_inline_amd/csrc/mx_device.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload, M):
+    """Calibrated HBM bytes per launch from the committed counter summary, or None when there
+    is none for this kernel and point or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            recs = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for r in recs:
+        if r.get("kernel") == kernel and r.get("workload") == workload and r.get("M") == M:
+            if r.get("source_hash") != kernel_source_hash():
+                return None
+            return int(r["traffic_bytes"])
+    return None
+
+
+def _counter_rows(d):
+    """(kernel name, counter, value) rows from every rocprofv3 counter CSV under d."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    for r in csv.DictReader(f):
+                        rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir, workload, M, copy_mib):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMM kernel, each scaled by the
+    factor that maps the same counter on a plain copy of copy_mib MiB to its true size."""
+    import mxfp4_quantized_gemm_inline_amd as mx
+    import workloads as W
+    N, K = W.DENSE_CONFIGS[workload][:2]
+    plan = mx.mx_a4w4_gemm_plan(M, N, K)
+    kern = plan.split(" ")[0]
+    out = {"kernel": plan, "workload": workload, "N": N, "K": K, "M": M, "copy_mib": copy_mib}
+    for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r[1] == ctr]
+        copy = [v for n, c, v in rows if "copybuffer" in n.lower()]
+        gemm = [v for n, c, v in rows if kern.split("<")[0] in n and kern.split("<")[1].rstrip(">") in n]
+        if not copy or not gemm:
+            raise SystemExit(f"{ctr}: no copy ({len(copy)}) or GEMM ({len(gemm)}) dispatches under {d}")
+        factor = copy_mib * 1024.0 / max(copy)
+        out[ctr.lower() + "_kib_raw"] = round(sum(gemm) / len(gemm), 1)
+        out[ctr.lower() + "_factor"] = round(factor, 4)
+    out["traffic_bytes"] = int((out["fetch_size_kib_raw"] * out["fetch_size_factor"] +
+                                out["write_size_kib_raw"] * out["write_size_factor"]) * 1024)
+    out["algorithmic_bytes"] = algo_bytes(M, N, K)
+    out["source_hash"] = kernel_source_hash()
+    return out
+
+
+def profile_point(workload, M, launches, copy_mib):
+    """A short run for counter collection: an optional plain copy of copy_mib MiB (the
+    calibration kernel), then `launches` cold launches of one dense point."""
+    import torch
+    import mxfp4_quantized_gemm_inline_amd as mx
+    import workloads as W
+    torch.cuda.set_device(0)
+    N, K, ms, st = W.DENSE_CONFIGS[workload]
+    if copy_mib:
+        src = torch.ones(copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    wp = mx.mx_prepare_weight(dev_bf16(torch, W.dense_weight(N, K)))
+    pt = DensePoint(torch, mx, wp, W.dense_activation(M, K, st), N, K, M, rotate=True)
+    torch.cuda.synchronize()
+    for i in range(launches):
+        pt.launch(i)()
+    torch.cuda.synchronize()
+    log(f"profiled {workload} M={M}: {launches} launches of {mx.mx_a4w4_gemm_plan(M, N, K)}")
 
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(a_by_m, w_bits, ms):
-    """The oracle as it stands on the host cores: one whole step of the headline workload."""
+def cpu_baseline(a_by_m, w_bits, ms, reps=3):
+    """The oracle as it stands on the host cores: `reps` whole steps of the headline
+    workload (about 10 s), reported per step."""
     from oracle import mx_oracle as O
     threads = None
     try:
@@ -168,14 +261,15 @@ def cpu_baseline(a_by_m, w_bits, ms):
         threads = None
     cores = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    for m in ms:
-        O.gemm_ref(a_by_m[m], w_bits)
-    dt = time.perf_counter() - t0
+    for _ in range(reps):
+        for m in ms:
+            O.gemm_ref(a_by_m[m], w_bits)
+    dt = (time.perf_counter() - t0) / reps
     return {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": threads or cores,
             "kind": "oracle",
-            "sample": f"one full step (N=7168 K=768, M in {list(ms)}: quantize A and W, decode, "
-                      f"float64 matmul), {cores} host cores visible, BLAS threads {threads}; "
-                      f"quantization is single-threaded numpy"}
+            "sample": f"{reps} full steps (N=7168 K=768, M in {list(ms)}: quantize A and W, decode, "
+                      f"float64 matmul), mean per step; {cores} host cores visible, BLAS threads "
+                      f"{threads} (the matmul); quantization is single-threaded numpy"}
 
 
 # ----------------------------------------------------------------------------- main
@@ -189,7 +283,30 @@ def main():
     ap.add_argument("--no-grouped", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--launches", type=int, default=200, help="launches per sweep point")
+    ap.add_argument("--profile-point", metavar="WORKLOAD:M",
+                    help="counter-collection run: only `--launches` cold launches of this dense point")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="with --profile-point: first run a plain copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="with --profile-point and --calibrate-copy: turn two rocprofv3 CSV counter "
+                         "runs into the calibrated traffic record in profiles/traffic.json")
     args = ap.parse_args()
+    if args.profile_point:
+        wl, m = args.profile_point.split(":")
+        if args.summarize_counters:
+            rec = summarize_counters(*args.summarize_counters, wl, int(m), args.calibrate_copy)
+            recs = []
+            if os.path.exists(TRAFFIC_FILE):
+                with open(TRAFFIC_FILE) as f:
+                    recs = [r for r in json.load(f)
+                            if not (r.get("workload") == wl and r.get("M") == int(m))]
+            recs.append(rec)
+            with open(TRAFFIC_FILE, "w") as f:
+                json.dump(recs, f, indent=1)
+            print(json.dumps(rec))
+        else:
+            profile_point(wl, int(m), args.launches, args.calibrate_copy)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -248,18 +365,23 @@ def main():
         warm = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=False)
         us_w = time_point(timer, warm, args.launches)
         del warm
-        head_points.append(point_record(HEADLINE, N, K, m, us_c, us_w, kernel_name(m, N, K)))
+        head_points.append(point_record(HEADLINE, N, K, m, us_c, us_w, kernel_name(mx, m, N, K)))
         log(f"  M={m}: {us_c:.2f} us cold, {us_w:.2f} us warm")
     dom = max(head_points, key=lambda p: p["us"])
     Bd = algo_bytes(dom["M"], N, K)
     Fd = algo_flops(dom["M"], N, K)
+    traffic = recorded_traffic(dom["kernel"], HEADLINE, dom["M"])
     if dom["binds"] == "hbm":
         roof = {"bound": "hbm", "achieved": round(Bd / dom["us"] / 1e3, 1), "peak": HBM_PEAK / 1e9,
-                "unit": "GB/s", "frac": dom["frac_hbm"], "traffic": None}
+                "unit": "GB/s", "frac": dom["frac_hbm"], "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": round(Fd / dom["us"] / 1e6, 1), "peak": MFMA_FP4_PEAK / 1e12,
-                "unit": "TFLOP/s", "frac": dom["frac_mfma"], "traffic": None}
+                "unit": "TFLOP/s", "frac": dom["frac_mfma"], "traffic": traffic}
     roof["kernel"] = f"{dom['kernel']} (N={N} K={K} M={dom['M']})"
+    roof["launch_us"] = dom["us"]
+    roof["traffic_note"] = ("HBM bytes per launch: rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by "
+                            "its reading on a plain copy of known size (profiles/traffic.json); null when "
+                            "the kernel sources changed since the counters were taken")
     roof["algorithmic_bytes"] = Bd
     roof["algorithmic_flops"] = Fd
 
@@ -279,7 +401,7 @@ def main():
                 warm = DensePoint(torch, mx, wpn, aa[:m], Nn, Kk, m, rotate=False)
                 us_w = time_point(timer, warm, args.launches)
                 del warm
-                sweep["dense"].append(point_record(name, Nn, Kk, m, us_c, us_w, kernel_name(m, Nn, Kk)))
+                sweep["dense"].append(point_record(name, Nn, Kk, m, us_c, us_w, kernel_name(mx, m, Nn, Kk)))
                 log(f"  {name} M={m}: {us_c:.2f} us cold, {us_w:.2f} us warm")
             del wpn
             torch.cuda.empty_cache()

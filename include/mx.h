@@ -6,8 +6,9 @@
  * (E2M1 elements, one E8M0 scale per 32 consecutive K) and multiplied against a
  * weight W[N,K] that was quantized to MXFP4 and preshuffled once; the product is
  * accumulated in FP32 and written as BF16 C[M,N]. Scope (same page, Scope): gfx950
- * only, N divisible by 256, K divisible by 128; rows of C at or beyond M are never
- * read or written (same page, Implementation: M-tail masking).
+ * only, N divisible by 256, K divisible by 128 (this library also caps N at 2^30 and K
+ * at 2^24); rows of C at or beyond M are never read or written (same page,
+ * Implementation: M-tail masking).
  *
  * Quantization rule (all entry points): for each 32-element block along K, the scale
  * byte is s = max(E - 2, 0) where E is the exponent field of the block's largest
@@ -58,7 +59,7 @@ int mx_prepared_layout_version(void);
  * Size in bytes of a prepared MXFP4 weight of shape [N, K]: N*K/2 bytes of packed E2M1
  * payload followed by N*K/32 bytes of E8M0 scales, N*K*17/32 in all, e.g. 32,169,984
  * bytes for 8448 x 7168 ("[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", Model
- * validation). Returns 0 when N <= 0, K <= 0, N % 256 or K % 128.
+ * validation). Returns 0 when N <= 0, K <= 0, N % 256, K % 128, N > 2^30 or K > 2^24.
  */
 size_t mx_prepared_weight_bytes(int64_t N, int64_t K);
 
@@ -131,6 +132,26 @@ mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token,
                                const int32_t* expert_offsets, int64_t E, int64_t R_max,
                                const void* w_prep_stacked, void* c_bf16, int64_t T, int64_t N,
                                int64_t K, int64_t rows_hint, hipStream_t stream);
+
+/*
+ * Introspection (host only, no GPU needed): the kernel instantiation(s) mx_a4w4_gemm
+ * would launch for (M, N, K) with a workspace of workspace_bytes, e.g.
+ * "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8" or "k_gemm_stream<1, 1, 2, 16, 1> S=1", written
+ * NUL-terminated (truncated to buf_len) into the caller's host buffer; "none" for M == 0.
+ * The names match the kernel names a profiler reports. Honours the library's tuning
+ * override (environment variable MX_GEMM_CONFIG) like the GEMM itself. Errors:
+ * MX_ERR_SHAPE (as mx_a4w4_gemm), MX_ERR_NULL (buf NULL or buf_len 0), MX_ERR_HIP (the
+ * override names no configuration that can run this call; the GEMM would fail the same way).
+ */
+mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_bytes, char* buf,
+                            size_t buf_len);
+
+/*
+ * The same for mx_a4w4_gemm_grouped (tuning override MX_GROUPED_CONFIG); "none" for
+ * R_max == 0. Same shape rules and errors as the grouped GEMM, plus MX_ERR_NULL for buf.
+ */
+mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t rows_hint,
+                                    char* buf, size_t buf_len);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,8 @@ SIGNATURES = {
     "mx_a4w4_gemm": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _c_sz, _vp]),
     "mx_a4w4_gemm_grouped": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _c_i64,
                                       _c_i64, _c_i64, _vp]),
+    "mx_a4w4_gemm_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_sz, ctypes.c_char_p, _c_sz]),
+    "mx_a4w4_gemm_grouped_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
 }
 
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE, MX_ERR_WORKSPACE, MX_ERR_HIP = range(7)
@@ -179,8 +181,28 @@ def mx_a4w4_gemm_grouped(a_bf16, row_token, expert_offsets, E: int, R_max: int, 
     return c
 
 
+def mx_a4w4_gemm_plan(M: int, N: int, K: int, workspace_bytes=None) -> str:
+    """Kernel(s) mx_a4w4_gemm launches for this shape; workspace_bytes defaults to what
+    mx_a4w4_gemm allocates when given no workspace."""
+    if workspace_bytes is None:
+        workspace_bytes = mx_a4w4_gemm_workspace_bytes(M, N, K)
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().mx_a4w4_gemm_plan(int(M), int(N), int(K), int(workspace_bytes), buf, len(buf)),
+           "mx_a4w4_gemm_plan")
+    return buf.value.decode()
+
+
+def mx_a4w4_gemm_grouped_plan(E: int, R_max: int, N: int, K: int, rows_hint: int = 1) -> str:
+    """Kernel mx_a4w4_gemm_grouped launches for this table size and hint."""
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().mx_a4w4_gemm_grouped_plan(int(E), int(R_max), int(N), int(K), int(rows_hint), buf, len(buf)),
+           "mx_a4w4_gemm_grouped_plan")
+    return buf.value.decode()
+
+
 __all__ = [
     "LIB_PATH", "MxError", "lib", "status_string", "mx_prepared_layout_version",
     "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
     "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
+    "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan",
 ]

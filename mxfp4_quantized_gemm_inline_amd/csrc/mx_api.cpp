@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <atomic>
+#include <cstdio>
 #include <cstring>
 
 #include "mx_internal.h"
@@ -17,8 +18,9 @@ std::atomic<int> g_arch_ok[kMaxDevices];
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// K <= 2^24 keeps a tile row's byte offset (at most 127 rows of 2K bytes) in 32 bits.
 bool gemm_shape_ok(int64_t N, int64_t K) {
-  return N > 0 && K > 0 && N % 256 == 0 && K % 128 == 0 && N <= (1ll << 30) && K <= (1ll << 30);
+  return N > 0 && K > 0 && N % 256 == 0 && K % 128 == 0 && N <= (1ll << 30) && K <= (1ll << 24);
 }
 
 mx_status check_device() {
@@ -125,6 +127,36 @@ mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token, con
   if (d != MX_OK) return d;
   return from_hip(mx::launch_gemm_grouped(a_bf16, row_token, expert_offsets, E, R_max, w_prep_stacked,
                                           c_bf16, T, N, K, rows_hint < 1 ? 1 : rows_hint, stream));
+}
+
+mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_bytes, char* buf, size_t buf_len) {
+  if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (!buf || buf_len == 0) return MX_ERR_NULL;
+  if (M == 0) {
+    std::snprintf(buf, buf_len, "none");
+    return MX_OK;
+  }
+  if (!mx::gemm_plan(M, N, K, workspace_bytes, buf, buf_len)) {
+    buf[0] = '\0';
+    return MX_ERR_HIP;
+  }
+  return MX_OK;
+}
+
+mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t rows_hint,
+                                    char* buf, size_t buf_len) {
+  if (E < 1 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1)
+    return MX_ERR_SHAPE;
+  if (!buf || buf_len == 0) return MX_ERR_NULL;
+  if (R_max == 0) {
+    std::snprintf(buf, buf_len, "none");
+    return MX_OK;
+  }
+  if (!mx::grouped_plan(E, R_max, N, K, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
+    buf[0] = '\0';
+    return MX_ERR_HIP;
+  }
+  return MX_OK;
 }
 
 }  // extern "C"

@@ -10,6 +10,7 @@
 // accumulator element r is C[m = l % 16][n = 4 * (l / 16) + r]: four consecutive columns of
 // one output row, stored as one 8-byte write.
 #include <atomic>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <utility>
@@ -340,54 +341,79 @@ __device__ __forceinline__ void static_for(F&& f) {
       std::make_integer_sequence<int, N_>{});
 }
 
-template <int WM, int WN, int MT, int NG, int PF, int OCC>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
-void k_gemm_tile(const uint16_t* __restrict__ A,
-                                                            const uint8_t* __restrict__ Wp,
-                                                            uint16_t* __restrict__ C, int M, int N,
-                                                            int K, int GM) {
-  constexpr int MTC = MT * WM;  // 16-row tiles per CTA
-  constexpr int BM = 16 * MTC, BN = 16 * NG * WN;
-  constexpr int NW = WM * WN;
+template <int WM, int WN, int MT, int NG>
+struct TileShape {
+  static constexpr int MTC = MT * WM;  // 16-row tiles per CTA
+  static constexpr int BM = 16 * MTC, BN = 16 * NG * WN;
+  static constexpr int NW = WM * WN, NTH = 64 * NW;
+  static constexpr int BPT = MTC / NW;  // 32-block quads per thread per step
+  // LDS: two buffers of quantized activation operands (SQ each) and their scales (SS each),
+  // the scales stored as [lane][16-row tile] bytes so a lane's scales for four tiles are one
+  // word; after the K loop the same memory stages the bf16 output tile (rows padded by 16
+  // bytes against bank conflicts).
+  static constexpr int SQ = MTC * 1024, SS = 64 * MTC;
+  static constexpr int CROW = BN * 2 + 16, CSTAGE = BM * CROW;
+  static constexpr int SMEM = 2 * (SQ + SS) > CSTAGE ? 2 * (SQ + SS) : CSTAGE;
   static_assert(MTC % NW == 0, "every wave quantizes whole 16-row tiles");
-  constexpr int BPT = MTC / NW;  // 32-blocks per thread per step
-  // LDS: two buffers of quantized activation operands (sq) and their scales (ss), stored
-  // as [lane][16-row tile] bytes so a lane's scales for four tiles are one word; after the
-  // K loop the same memory stages the bf16 output tile (rows padded by 16 bytes).
-  constexpr int SQ = MTC * 1024, SS = 64 * MTC;
-  constexpr int CROW = BN * 2 + 16, CSTAGE = BM * CROW;
-  constexpr int SMEM = 2 * (SQ + SS) > CSTAGE ? 2 * (SQ + SS) : CSTAGE;
-  __shared__ __align__(16) uint8_t smem[SMEM];
+  static_assert(MT % 4 == 0, "a wave's tiles cover whole scale words");
+};
+
+// Activation rows of one CTA tile. Dense: tile row r is the row at base + r * K (bf16), with
+// base wave-uniform, so a lane keeps only a 32-bit offset per row (K < 2^24 keeps it exact).
+struct TileRowsDense {
+  const uint8_t* base;
+  int K;
+  static constexpr bool kGather = false;
+};
+// Gathered: tile row r is A[tok[r]]; a token outside [0, T) reads as an all-zero row.
+struct TileRowsGather {
+  const uint8_t* A;
+  const int32_t* tok;
+  int T, K;
+  static constexpr bool kGather = true;
+};
+
+// The tiled main loop and epilogue for one BM x BN output tile: Mrows (1..BM) valid rows
+// from `rows`, weight column tile bn of the prepared weight Wp, output rows written at
+// Cout + r * N for r < Mrows (columns past N masked).
+template <int WM, int WN, int MT, int NG, int PF, class Rows>
+__device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uint8_t* __restrict__ Wp,
+                                          uint16_t* __restrict__ Cout, int N, int K, int bn,
+                                          uint8_t* __restrict__ smem) {
+  using S = TileShape<WM, WN, MT, NG>;
+  constexpr int MTC = S::MTC, BM = S::BM, BN = S::BN, NW = S::NW, BPT = S::BPT;
+  constexpr int SQ = S::SQ, SS = S::SS, CROW = S::CROW;
   auto sq = [&](int buf, int off) { return smem + buf * SQ + off; };
   auto ss = [&](int buf, int off) { return smem + 2 * SQ + buf * SS + off; };
-  static_assert(MT % 4 == 0, "a wave's tiles cover whole scale words");
 
   const int T = steps_of(K), G = N / 16;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int bm, bn;
-  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, GM, bm, bn);
-  const int m0 = bm * BM;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / WN, wn = w % WN;
   const int gw0 = bn * (BN / 16) + wn * NG;
   const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
 
-  // Loads are branch-free so the compiler can count them: rows past M re-read row M-1
-  // and column groups past N re-read the last group; neither result is ever stored.
-  // Bases are wave-uniform; only 32-bit lane offsets live in vector registers.
-  const uint8_t* __restrict__ A8 = reinterpret_cast<const uint8_t*>(A);
-  // The quad of lanes 4r..4r+3 of wave v quantizes, for i < BPT, row r of the 16-row tile
-  // v + NW i: lane 4r+j holds the 16-byte chunk j of each of the step's four 32-blocks, so
-  // every load instruction of the quad reads one block's 64 contiguous bytes. In LDS a tile
-  // holds its 16 x 4 operand blocks row-major with the block index XOR-swizzled by the row;
-  // the quant stores (one word per lane and block) and the MFMA reads (lane = row + 16 block)
-  // then fall on distinct banks.
+  // Loads are branch-free so the compiler can count them: tile rows past Mrows re-read the
+  // last valid row and column groups past N re-read the last group; neither result is ever
+  // stored. The quad of lanes 4r..4r+3 of wave v quantizes, for i < BPT, row r of the
+  // 16-row tile v + NW i: lane 4r+j holds the 16-byte chunk j of each of the step's four
+  // 32-blocks, so every load instruction of the quad reads one block's 64 contiguous bytes.
+  // In LDS a tile holds its 16 x 4 operand blocks row-major with the block index
+  // XOR-swizzled by the row; the quant stores (one word per lane and block) and the MFMA
+  // reads (lane = row + 16 block) then fall on distinct banks.
   uint32_t aoff[BPT];
+  const uint8_t* aptr[BPT];
+  bool avalid[BPT];
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    const int r = 16 * (w + NW * i) + (lane >> 2);
-    aoff[i] = (uint32_t)((size_t)min(m0 + r, M - 1) * K * 2 + (lane & 3) * 16);
+    const int r = min(16 * (w + NW * i) + (lane >> 2), Mrows - 1);
+    if constexpr (!Rows::kGather) {
+      aoff[i] = (uint32_t)r * (uint32_t)rows.K * 2u + (uint32_t)(lane & 3) * 16u;
+    } else {
+      const int tk = rows.tok[r];
+      avalid[i] = tk >= 0 && tk < rows.T;
+      aptr[i] = rows.A + (size_t)(avalid[i] ? tk : 0) * rows.K * 2 + (lane & 3) * 16;
+    }
   }
   auto swz = [](int rr) { return ((rr >> 1) ^ (rr >> 2)) & 3; };
   // LDS byte of this lane's word of block c within a tile is st_off ^ (c << 4) (bits 4-5
@@ -411,9 +437,14 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
 
   auto load_a = [&](int t, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    const uint8_t* base = A8 + (size_t)t * kStepK * 2;
+    if constexpr (!Rows::kGather) {
+      const uint8_t* base = rows.base + (size_t)t * kStepK * 2;
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) load_quad_at(base, aoff[i], areg[SL][i]);
+      for (int i = 0; i < BPT; ++i) load_quad_at(base, aoff[i], areg[SL][i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) load_quad_at(aptr[i] + (size_t)t * kStepK * 2, 0u, areg[SL][i]);
+    }
   };
   auto load_w = [&](int t, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
@@ -445,7 +476,12 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
     for (int i = 0; i < BPT; ++i) {
       const int tile = w + NW * i;
       uint32_t q[4];
-      const uint32_t sc = quant_quad4(areg[SA][i], q);
+      uint32_t sc = quant_quad4(areg[SA][i], q);
+      if constexpr (Rows::kGather) {  // a row with no valid token quantizes to zero
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[c] = avalid[i] ? q[c] : 0u;
+        sc = avalid[i] ? sc : 0u;
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(sq(buf, tile * 1024 + (st_off ^ (c << 4)))) = q[c];
       *ss(buf, st_sc + tile) = (uint8_t)(sc >> (8 * (lane & 3)));
@@ -509,12 +545,104 @@ void k_gemm_tile(const uint16_t* __restrict__ A,
   for (int i = 0; i < BM * CPR / (64 * NW); ++i) {
     const int id = threadIdx.x + i * 64 * NW;
     const int r = id / CPR, ch = id % CPR;
-    const int m = m0 + r, n = n0 + 8 * ch;
-    if (m < M && n < N) {
+    const int n = n0 + 8 * ch;
+    if (r < Mrows && n < N) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * CROW + ch * 16);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * N + n));
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(Cout + (size_t)r * N + n));
     }
   }
+}
+
+template <int WM, int WN, int MT, int NG, int PF, int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void k_gemm_tile(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
+                 int M, int N, int K, int GM) {
+  using S = TileShape<WM, WN, MT, NG>;
+  __shared__ __align__(16) uint8_t smem[S::SMEM];
+  const int tiles_m = (M + S::BM - 1) / S::BM, tiles_n = (N + S::BN - 1) / S::BN;
+  int bm, bn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, GM, bm, bn);
+  const int m0 = bm * S::BM;
+  const TileRowsDense rows{reinterpret_cast<const uint8_t*>(A) + (size_t)m0 * K * 2, K};
+  tile_core<WM, WN, MT, NG, PF>(rows, min(S::BM, M - m0), Wp, C + (size_t)m0 * N, N, K, bn, smem);
+}
+
+// ====================================================================== grouped MoE GEMM1, tiled
+//
+// For segments of tens of rows or more. Each expert's rows are cut into BM-row tiles and
+// every (expert, column tile, row tile) unit is one CTA running the tiled main loop with
+// its rows gathered by token index, so an expert's weight is streamed once per row tile
+// (once in all for a segment of at most BM rows) rather than once per 16 or 32 rows. The
+// grid is an upper bound on the units ((active experts + R_max / BM) x column tiles); each
+// CTA ranks the experts' unit counts with a block scan to find its unit, and the surplus
+// CTAs exit. One expert's units are consecutive and dealt to one XCD (as in tile_coords),
+// so its column tiles share the gathered rows and its row tiles the weight in that L2.
+template <int WM, int WN, int MT, int NG, int PF, int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+                         const int32_t* __restrict__ offs, int E, int R_max, const uint8_t* __restrict__ Wall,
+                         uint16_t* __restrict__ C, int Ttok, int N, int K) {
+  using S = TileShape<WM, WN, MT, NG>;
+  constexpr int NTH = S::NTH, BM = S::BM, BN = S::BN;
+  __shared__ __align__(16) uint8_t smem[S::SMEM];
+  __shared__ int s_scan[NTH];
+  __shared__ int s_unit[4];  // expert, segment start, segment rows, its first unit
+  const int tid = threadIdx.x;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int total = gridDim.x;
+  const int L = (blockIdx.x % 8) * (total / 8) + min((int)(blockIdx.x % 8), total % 8) + blockIdx.x / 8;
+
+  auto seg = [&](int e, int& lo, int& hi) {
+    lo = min(max(offs[e], 0), R_max);
+    hi = min(max(offs[e + 1], lo), R_max);
+  };
+  const int ept = (E + NTH - 1) / NTH;
+  int local = 0;
+  for (int i = 0; i < ept; ++i) {
+    const int e = tid * ept + i;
+    if (e < E) { int lo, hi; seg(e, lo, hi); local += (hi - lo + BM - 1) / BM * tiles_n; }
+  }
+  s_scan[tid] = local;
+  if (tid == 0) s_unit[0] = -1;
+  __syncthreads();
+  for (int d = 1; d < NTH; d <<= 1) {
+    const int v = (tid >= d) ? s_scan[tid - d] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  {
+    int u = s_scan[tid] - local;  // units before this thread's experts
+    if (L >= u && L < u + local) {
+      for (int i = 0; i < ept; ++i) {
+        const int e = tid * ept + i;
+        if (e >= E) break;
+        int lo, hi; seg(e, lo, hi);
+        const int units = (hi - lo + BM - 1) / BM * tiles_n;
+        if (L < u + units) { s_unit[0] = e; s_unit[1] = lo; s_unit[2] = hi - lo; s_unit[3] = u; break; }
+        u += units;
+      }
+    }
+  }
+  __syncthreads();
+  const int e = s_unit[0];
+  if (e < 0) return;  // surplus CTA: the grid over-counts the units
+  const int lo = s_unit[1], cnt = s_unit[2];
+  const int tiles_e = (cnt + BM - 1) / BM;
+  const int rem = L - s_unit[3], bn = rem / tiles_e, mt = rem % tiles_e;
+  const int r0 = lo + mt * BM, Mrows = min(BM, cnt - mt * BM);
+  uint16_t* Cout = C + (size_t)r0 * N;
+
+  if (Ttok <= 0) {  // no activations at all: every row is Q(0) W^T = 0
+    const int n0 = bn * BN, ncol = min(BN, N - n0);
+    for (int i = tid; i < Mrows * (ncol / 8); i += NTH) {
+      const int r = i / (ncol / 8), ch = i % (ncol / 8);
+      *reinterpret_cast<uint4*>(Cout + (size_t)r * N + n0 + 8 * ch) = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
+  const TileRowsGather rows{reinterpret_cast<const uint8_t*>(A), row_token + r0, Ttok, K};
+  tile_core<WM, WN, MT, NG, PF>(rows, Mrows, Wall + (size_t)e * prepared_bytes(N, K), Cout, N, K, bn, smem);
 }
 
 // ====================================================================== wide-tile GEMM (large M)
@@ -862,14 +990,18 @@ struct GemmConfig {
   X(1, 4, 4, 4, 1, 2) X(1, 4, 4, 4, 2, 2) X(2, 4, 4, 4, 1, 1) X(1, 4, 4, 2, 2, 2)
 
 // Weight prefetch depth: enough registers for a wave's whole K share when it fits (4, 8 or
-// 16 steps of NG operands, at most 16 operands), so no registers go to duplicate loads.
-template <int NG>
-int pick_pd(int steps_per_wave) {
-  constexpr int cap = kSkinnyPD / NG;
+// 16 steps of NG operands, at most kSkinnyPD operands), so no registers go to duplicate
+// loads. This is the PD the streaming and grouped launchers instantiate.
+int pick_pd(int NG, int steps_per_wave) {
+  const int cap = kSkinnyPD / NG;
   int pd = 4;
   while (pd < steps_per_wave && pd < cap) pd *= 2;
   return pd > cap ? cap : pd;
 }
+
+// Activation quant batch of the streaming kernel: one batch when a wave's blocks fit one
+// per lane, otherwise four blocks per lane in flight per batch.
+int stream_qb(int M, int steps_per_wave) { return M * 4 * steps_per_wave <= 64 ? 1 : 4; }
 
 template <int MT, int NG, int WK, int PD, int QB>
 hipError_t launch_stream(const void* a, const void* wp, void* c, float* P, int M, int N, int K, int S,
@@ -904,11 +1036,9 @@ hipError_t run_stream(const void* a, const void* wp, void* c, float* P, int M, i
   const size_t lds = stream_lds_bytes(16 * MT, TS, MT, NG, WK);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   const int per = (TS + WK - 1) / WK;
-  const int pd = pick_pd<NG>(per);
-  // a wave's activation blocks fit one lane each: one quant batch, fewer registers;
-  // otherwise four blocks per lane in flight per batch
-  hipError_t e = M * 4 * per <= 64 ? launch_stream_pd<MT, NG, WK, 1>(pd, a, wp, c, P, M, N, K, S, TS, lds, st)
-                                   : launch_stream_pd<MT, NG, WK, 4>(pd, a, wp, c, P, M, N, K, S, TS, lds, st);
+  const int pd = pick_pd(NG, per);
+  hipError_t e = stream_qb(M, per) == 1 ? launch_stream_pd<MT, NG, WK, 1>(pd, a, wp, c, P, M, N, K, S, TS, lds, st)
+                                        : launch_stream_pd<MT, NG, WK, 4>(pd, a, wp, c, P, M, N, K, S, TS, lds, st);
   if (e != hipSuccess || S == 1) return e;
   const int64_t MN = (int64_t)M * N;
   hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, st, P,
@@ -1067,26 +1197,53 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (!c.tile && c.S > 1) ? (size_t)c.S * (size_t)M * (size_t)N * 4 : 0;
 }
 
-hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M64, int64_t N64, int64_t K64,
-                       void* ws, size_t ws_bytes, hipStream_t st) {
-  const int M = (int)M64, N = (int)N64, K = (int)K64;
-  if (!ws) ws_bytes = 0;
-  GemmConfig cfg = select_config(M, N, K, ws_bytes);
+namespace {
+
+// The configuration a dense call runs: the default choice or the tuning override. False
+// when the override names nothing compiled or cannot run this call (a streaming choice
+// must cover M, fit its K slice in LDS and its partials in the workspace).
+bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
+  cfg = select_config(M, N, K, ws_bytes);
   const int ov = override_config(cfg);
-  if (ov < 0) return hipErrorInvalidValue;
+  if (ov < 0) return false;
   if (ov > 0 && !cfg.tile) {
-    // an overriding streaming choice must fit its slice in LDS and its partials in the
-    // workspace, and cover M
     const int T = steps_of(K);
     if (cfg.S > T) cfg.S = T;
     const size_t need = cfg.S > 1 ? (size_t)cfg.S * M * N * 4 : 0;
     const int TS = (T + cfg.S - 1) / cfg.S;
     if (M > 16 * cfg.MT || need > ws_bytes || (N / 16) % cfg.NG != 0 ||
         stream_lds_bytes(16 * cfg.MT, TS, cfg.MT, cfg.NG, cfg.WK) > kMaxLds)
-      return hipErrorInvalidValue;
+      return false;
   }
+  return true;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M64, int64_t N64, int64_t K64,
+                       void* ws, size_t ws_bytes, hipStream_t st) {
+  const int M = (int)M64, N = (int)N64, K = (int)K64;
+  if (!ws) ws_bytes = 0;
+  GemmConfig cfg;
+  if (!resolve_config(M, N, K, ws_bytes, cfg)) return hipErrorInvalidValue;
   return run_config(cfg, a, wp, c, cfg.tile ? nullptr : (cfg.S > 1 ? static_cast<float*>(ws) : nullptr),
                     M, N, K, st);
+}
+
+bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf, size_t len) {
+  const int M = (int)M64, N = (int)N64, K = (int)K64;
+  GemmConfig c;
+  if (!resolve_config(M, N, K, ws_bytes, c)) return false;
+  if (c.wide) {
+    std::snprintf(buf, len, "k_gemm_wide<%d, %d> GM=%d", c.MT, c.NG, c.GM);
+  } else if (c.tile) {
+    std::snprintf(buf, len, "k_gemm_tile<%d, %d, %d, %d, %d, %d> GM=%d", c.WM, c.WN, c.MT, c.NG, c.PF, c.OCC, c.GM);
+  } else {
+    const int T = steps_of(K), TS = (T + c.S - 1) / c.S, per = (TS + c.WK - 1) / c.WK;
+    std::snprintf(buf, len, "k_gemm_stream<%d, %d, %d, %d, %d> S=%d%s", c.MT, c.NG, c.WK, pick_pd(c.NG, per),
+                  stream_qb(M, per), c.S, c.S > 1 ? " + k_splitk_reduce" : "");
+  }
+  return true;
 }
 
 namespace {
@@ -1114,7 +1271,7 @@ hipError_t run_grouped(const void* a, const int32_t* rt, const int32_t* offs, in
   const size_t lds = stream_lds_bytes(16 * MT, steps, MT, NG, WK);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   const int per = (steps + WK - 1) / WK;
-  const int pd = pick_pd<NG>(per);
+  const int pd = pick_pd(NG, per);
   if (per > pd) return launch_grouped<MT, NG, WK, kSkinnyPD / NG, false>(a, rt, offs, E, R_max, wp, c, T, N, K, lds, st);
   if constexpr (kSkinnyPD / NG >= 16)
     if (pd >= 16) return launch_grouped<MT, NG, WK, 16, true>(a, rt, offs, E, R_max, wp, c, T, N, K, lds, st);
@@ -1123,22 +1280,109 @@ hipError_t run_grouped(const void* a, const int32_t* rt, const int32_t* offs, in
   return launch_grouped<MT, NG, WK, 4, true>(a, rt, offs, E, R_max, wp, c, T, N, K, lds, st);
 }
 
+// Tiled grouped configurations (WM, WN, MT, NG, PF, OCC).
+#define MX_GROUPED_TILE_CONFIGS(X) \
+  X(1, 4, 4, 4, 1, 2)              \
+  X(2, 4, 4, 4, 1, 1)              \
+  X(1, 4, 4, 4, 2, 2)
+
+template <int WM, int WN, int MT, int NG, int PF, int OCC>
+hipError_t run_grouped_tile(const void* a, const int32_t* rt, const int32_t* offs, int E, int R_max,
+                            const void* wp, void* c, int T, int N, int K, hipStream_t st) {
+  using S = TileShape<WM, WN, MT, NG>;
+  const int64_t active = E < R_max ? E : R_max;
+  const int64_t grid = (active + R_max / S::BM) * ((N + S::BN - 1) / S::BN);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm_grouped_tile<WM, WN, MT, NG, PF, OCC>), dim3((unsigned)grid), dim3(S::NTH), 0, st,
+                     static_cast<const uint16_t*>(a), rt, offs, E, R_max, static_cast<const uint8_t*>(wp),
+                     static_cast<uint16_t*>(c), T, N, K);
+  return hipGetLastError();
+}
+
+struct GroupedConfig {
+  bool tile = false;
+  int WM = 1, WN = 4, MT = 1, NG = 1, PF = 1, OCC = 2;
+};
+
+bool grouped_tile_supported(const GroupedConfig& g) {
+#define X(wm, wn, mt, ng, pf, occ) \
+  if (g.WM == wm && g.WN == wn && g.MT == mt && g.NG == ng && g.PF == pf && g.OCC == occ) return true;
+  MX_GROUPED_TILE_CONFIGS(X)
+#undef X
+  return false;
+}
+
+// The configuration a grouped call runs. Tuning only: MX_GROUPED_CONFIG="gs,MT,NG"
+// (streaming, four waves) or "gt,WM,WN,MT,NG,PF,OCC" (tiled) replaces the default choice;
+// false when it names no compiled configuration (the call then fails).
+bool resolve_grouped(int E, int R_max, int N, int64_t rows_hint, GroupedConfig& g) {
+  const int G = N / 16;
+  const int64_t active = E < R_max ? E : R_max;
+  const char* s = std::getenv("MX_GROUPED_CONFIG");
+  if (s && *s) {
+    int v[6] = {0, 0, 0, 0, 0, 0};
+    if (std::sscanf(s, "gt,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5]) == 6) {
+      g.tile = true; g.WM = v[0]; g.WN = v[1]; g.MT = v[2]; g.NG = v[3]; g.PF = v[4]; g.OCC = v[5];
+      return grouped_tile_supported(g);
+    }
+    if (std::sscanf(s, "gs,%d,%d", &v[0], &v[1]) == 2) {
+      g.tile = false; g.MT = v[0]; g.NG = v[1];
+      return (g.MT == 1 || g.MT == 2) && (g.NG == 1 || (g.NG == 4 && G % 4 == 0));
+    }
+    return false;
+  }
+  // Tiled (the weight streamed once per 64-row tile) whenever its grid, one CTA per active
+  // expert and 256-column tile, can fill the chip; the streaming kernel (more, narrower
+  // CTAs) only for a handful of active experts. Streaming widens to four column groups per
+  // CTA as segments grow, amortizing each CTA's serial segment-lookup -> token ->
+  // activation chain over more streamed weight.
+  if (G % 16 == 0 && active * (G / 16) >= 512) {
+    g = GroupedConfig{true, 1, 4, 4, 4, 1, 2};
+    return true;
+  }
+  g.tile = false;
+  if (rows_hint <= 16) { g.MT = 1; g.NG = (active < 128 || G % 4 != 0) ? 1 : 4; }
+  else { g.MT = 2; g.NG = (rows_hint <= 32 || G % 4 != 0) ? 1 : 4; }
+  return true;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const int32_t* offsets, int64_t E,
                                int64_t R_max, const void* wp, void* c, int64_t T, int64_t N, int64_t K,
                                int64_t rows_hint, hipStream_t st) {
   const int e = (int)E, r = (int)R_max, t = (int)T, n = (int)N, k = (int)K;
-  const int G = n / 16;
-  // more weight columns per CTA as segments grow, to amortize each CTA's serial
-  // segment-lookup -> token -> activation latency chain over more streamed weight
-  const int64_t active = e < r ? e : r;
-  if (rows_hint <= 16) {
-    if (active < 128 || G % 4 != 0) return run_grouped<1, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
-    return run_grouped<1, 4, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+  GroupedConfig g;
+  if (!resolve_grouped(e, r, n, rows_hint, g)) return hipErrorInvalidValue;
+  if (g.tile) {
+#define X(wm, wn, mt, ng, pf, occ)                                                                 \
+    if (g.WM == wm && g.WN == wn && g.MT == mt && g.NG == ng && g.PF == pf && g.OCC == occ)         \
+      return run_grouped_tile<wm, wn, mt, ng, pf, occ>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+    MX_GROUPED_TILE_CONFIGS(X)
+#undef X
+    return hipErrorInvalidValue;
   }
-  if (rows_hint <= 32 || G % 4 != 0) return run_grouped<2, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
-  return run_grouped<2, 4, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+  if (g.MT == 1 && g.NG == 1) return run_grouped<1, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+  if (g.MT == 1 && g.NG == 4) return run_grouped<1, 4, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+  if (g.MT == 2 && g.NG == 1) return run_grouped<2, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+  if (g.MT == 2 && g.NG == 4) return run_grouped<2, 4, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
+  return hipErrorInvalidValue;
+}
+
+bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t rows_hint, char* buf, size_t len) {
+  GroupedConfig g;
+  if (!resolve_grouped((int)E, (int)R_max, (int)N, rows_hint, g)) return false;
+  if (g.tile) {
+    std::snprintf(buf, len, "k_gemm_grouped_tile<%d, %d, %d, %d, %d, %d>", g.WM, g.WN, g.MT, g.NG, g.PF, g.OCC);
+  } else {
+    constexpr int WK = 4;
+    const int per = (steps_of((int)K) + WK - 1) / WK, pd = pick_pd(g.NG, per);
+    const bool res = per <= pd;
+    std::snprintf(buf, len, "k_gemm_grouped<%d, %d, %d, %d, %d, %s>", g.MT, g.NG, WK, res ? pd : kSkinnyPD / g.NG,
+                  g.MT == 1 ? 1 : 4, res ? "true" : "false");
+  }
+  return true;
 }
 
 }  // namespace mx

@@ -100,3 +100,44 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mx, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         mx.lib()
+
+
+def test_gemm_plan_names_the_selected_kernel(monkeypatch):
+    monkeypatch.delenv("MX_GEMM_CONFIG", raising=False)
+    assert mx.mx_a4w4_gemm_plan(0, 7168, 768) == "none"
+    assert mx.mx_a4w4_gemm_plan(1, 7168, 768).startswith("k_gemm_stream<1, 1, ")
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 768) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
+    # split K only with a workspace; the streaming kernels never need one otherwise
+    with_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168)
+    no_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168, workspace_bytes=0)
+    assert "k_splitk_reduce" in with_ws and "S=1" in no_ws and "k_splitk_reduce" not in no_ws
+    monkeypatch.setenv("MX_GEMM_CONFIG", "t,1,4,4,4,2,16,2")
+    assert mx.mx_a4w4_gemm_plan(64, 7168, 768) == "k_gemm_tile<1, 4, 4, 4, 2, 2> GM=16"
+    monkeypatch.setenv("MX_GEMM_CONFIG", "t,9,9,9,9,9,9")
+    with pytest.raises(mx.MxError):
+        mx.mx_a4w4_gemm_plan(64, 7168, 768)
+
+
+def test_grouped_plan_names_the_selected_kernel(monkeypatch):
+    monkeypatch.delenv("MX_GROUPED_CONFIG", raising=False)
+    N, K, E = 1536, 3584, 896
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 0, N, K) == "none"
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 16, N, K).startswith("k_gemm_grouped<1, 1, 4, ")
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, N, K, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 1, 2>"
+    monkeypatch.setenv("MX_GROUPED_CONFIG", "gs,2,4")
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, N, K).startswith("k_gemm_grouped<2, 4, 4, ")
+    monkeypatch.setenv("MX_GROUPED_CONFIG", "gt,1,4,4,4,3,2")
+    with pytest.raises(mx.MxError):
+        mx.mx_a4w4_gemm_grouped_plan(E, 65536, N, K)
+
+
+def test_plan_argument_errors():
+    f, g = mx.lib().mx_a4w4_gemm_plan, mx.lib().mx_a4w4_gemm_grouped_plan
+    buf = ctypes.create_string_buffer(64)
+    assert f(16, 100, 256, 0, buf, 64) == mx.MX_ERR_SHAPE
+    assert f(16, 256, 256, 0, None, 64) == mx.MX_ERR_NULL
+    assert f(16, 256, 256, 0, buf, 0) == mx.MX_ERR_NULL
+    assert g(0, 16, 256, 256, 1, buf, 64) == mx.MX_ERR_SHAPE
+    assert g(4, 16, 256, 256, 1, None, 64) == mx.MX_ERR_NULL
+    tiny = ctypes.create_string_buffer(8)  # truncated, still NUL-terminated
+    assert f(2048, 7168, 768, 0, tiny, 8) == mx.MX_OK and tiny.value == b"k_gemm_"

@@ -73,8 +73,10 @@ def test_grouped_tiling_hint_only_changes_tiling(hint):
     check_gemm(c[rows], exact, what=f"grouped hint={hint}")
 
 
-def test_grouped_malformed_table_is_clamped():
-    """Out-of-range tokens read as zero rows; segments are clamped to [0, R_max]."""
+@pytest.mark.parametrize("hint", [2, 64])
+def test_grouped_malformed_table_is_clamped(hint):
+    """Out-of-range tokens read as zero rows; segments are clamped to [0, R_max] (both the
+    streaming and the tiled kernels)."""
     torch = torch_or_skip()
     mx = lib_or_fail()
     E, N, K, T = 4, 256, 256, 3
@@ -86,7 +88,7 @@ def test_grouped_malformed_table_is_clamped():
     row_token = np.array([0, 2, 1, 7, -1, 2], dtype=np.int32)  # 7 and -1 are out of range
     R_max = 6
     c = host_bits(mx.mx_a4w4_gemm_grouped(dev_bf16(a), torch.from_numpy(row_token).cuda(),
-                                          torch.from_numpy(offs).cuda(), E, R_max, wst, N, rows_hint=2))
+                                          torch.from_numpy(offs).cuda(), E, R_max, wst, N, rows_hint=hint))
     torch.cuda.synchronize()
     expert_of = [0, 0, 2, 2, 2, 3]
     for r in range(R_max):
@@ -96,3 +98,66 @@ def test_grouped_malformed_table_is_clamped():
             check_gemm(c[r:r + 1], want[None, :], what=f"row {r}")
         else:
             assert np.all(O.bf16_to_f64(c[r]) == 0.0), r
+
+
+GROUPED_CONFIGS = ["gs,1,1", "gs,1,4", "gs,2,1", "gs,2,4",
+                   "gt,1,4,4,4,1,2", "gt,2,4,4,4,1,1", "gt,1,4,4,4,2,2"]
+
+
+def _ragged_case():
+    """Six experts with segments of 0, 1, 63, 64, 130 and 200 rows (ragged tails, segments
+    spanning several 64- and 128-row tiles), N = 512, K = 768, tokens drawn from T = 50."""
+    E, N, K, T = 6, 512, 768, 50
+    sizes = [0, 1, 63, 64, 130, 200]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rng = np.random.default_rng(7)
+    row_token = rng.integers(0, T, size=int(offs[-1])).astype(np.int32)
+    a = W.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    ws = [W.dense_weight(N, K, seed=80 + e) for e in range(E)]
+    return E, N, K, T, offs, row_token, a, ws
+
+
+@pytest.mark.parametrize("cfg", GROUPED_CONFIGS)
+def test_grouped_every_config_matches_oracle(cfg, monkeypatch):
+    """Each compiled grouped kernel (forced through the tuning override) matches the oracle
+    on every row of a ragged segment table."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    E, N, K, T, offs, row_token, a, ws = _ragged_case()
+    wst = torch.cat([mx.mx_prepare_weight(dev_bf16(w)) for w in ws])
+    R = int(offs[-1])
+    monkeypatch.setenv("MX_GROUPED_CONFIG", cfg)
+    c = host_bits(mx.mx_a4w4_gemm_grouped(dev_bf16(a), torch.from_numpy(row_token).cuda(),
+                                          torch.from_numpy(offs).cuda(), E, R, wst, N, rows_hint=1))
+    torch.cuda.synchronize()
+    exact = O.grouped_gemm_ref(a, row_token, offs, lambda e: ws[e])
+    check_gemm(c, exact, what=f"grouped {cfg}")
+
+
+@pytest.mark.parametrize("hint", [2, 64])
+def test_grouped_without_tokens_writes_zero_rows(hint):
+    """T = 0: every output row is Q(0) W^T = 0 (and no activation is read)."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    E, N, K, _, offs, _, _, ws = _ragged_case()
+    wst = torch.cat([mx.mx_prepare_weight(dev_bf16(w)) for w in ws])
+    R = int(offs[-1])
+    row_token = torch.zeros(R, dtype=torch.int32, device="cuda")
+    out = torch.full((R, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    empty = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    mx.mx_a4w4_gemm_grouped(empty, row_token, torch.from_numpy(offs).cuda(), E, R, wst, N,
+                            rows_hint=hint, out=out)
+    torch.cuda.synchronize()
+    assert np.all(O.bf16_to_f64(host_bits(out)) == 0.0)
+
+
+@pytest.mark.parametrize("bad", ["gt,1,4,4,4,3,2", "gs,3,1", "gx", "gt,1,4"])
+def test_grouped_unknown_override_fails(bad, monkeypatch):
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    E, N, K, T, offs, row_token, a, ws = _ragged_case()
+    wst = torch.cat([mx.mx_prepare_weight(dev_bf16(w)) for w in ws])
+    monkeypatch.setenv("MX_GROUPED_CONFIG", bad)
+    with pytest.raises(mx.MxError):
+        mx.mx_a4w4_gemm_grouped(dev_bf16(a), torch.from_numpy(row_token).cuda(), torch.from_numpy(offs).cuda(),
+                                E, int(offs[-1]), wst, N)
