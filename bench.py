@@ -160,12 +160,19 @@ KERNEL_SOURCES = ["mxfp4_quantized_gemm_inline_amd/csrc/mx_kernels.hip",
                   "mxfp4_quantized_gemm_inline_amd/csrc/mx_device.h"]
 
 
+LAUNCHERS_MARK = b"// ====================================================================== launchers"
+
+
 def kernel_source_hash():
+    """Hash of the device code: mx_device.h and mx_kernels.hip up to its host launchers
+    (configuration selection there does not change a kernel)."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+            src = f.read()
+        cut = src.find(LAUNCHERS_MARK)
+        h.update(src if cut < 0 else src[:cut])
     return h.hexdigest()[:16]
 
 

@@ -1134,15 +1134,19 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
     GemmConfig s;
     s.tile = false;
     s.MT = round_up_pow2((M + 15) / 16);
+    // long K: eight waves share a CTA's K range, more weight bytes in flight per column
+    const bool longk = T >= 16;
     if (M <= 4) {
-      s.NG = 1;
-      s.WK = G >= 256 ? 2 : 4;
+      s.NG = (G >= 256 && G < 512) ? 2 : 1;
+      s.WK = longk ? 8 : 4;
     } else if (M <= 16) {
-      s.NG = G >= 512 ? 4 : (G >= 256 ? 2 : 1);
-      s.WK = (G >= 256 && G < 512) ? 8 : 4;
+      s.NG = G >= 256 ? 2 : 1;
+      s.WK = longk ? 8 : 4;
+      if (G >= 512 && T >= 32) s.S = 2;
     } else if (M <= 32) {
       s.NG = G >= 512 ? 4 : 2;
-      s.WK = 4;
+      s.WK = (longk && G < 512) ? 8 : 4;
+      if (G >= 512 && T >= 32) s.S = 4;
     } else {
       s.NG = 2;
       s.WK = 4;
@@ -1153,12 +1157,13 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
     if (!stream_fits(s)) s.S = 1;
     if (stream_fits(s)) return s;
   }
-  // tiled kernel: 64 x 256 tiles when there are enough of them, else 64 x 128
+  // tiled kernel: 64 x 256 tiles when there are enough of them (two steps of prefetch only
+  // for long K at moderate sizes), else 64 x 128 tiles at one CTA per SIMD set
   c.tile = true;
-  c.WM = 1; c.WN = 4; c.MT = 4; c.OCC = 2;
+  c.WM = 1; c.WN = 4; c.MT = 4;
   const int64_t tiles256 = (int64_t)((M + 63) / 64) * ((N + 255) / 256);
-  if (tiles256 >= 150) { c.NG = 4; c.PF = M >= 1024 || G >= 512 ? 1 : 2; c.GM = 8; }
-  else { c.NG = 2; c.PF = 2; c.GM = 16; }
+  if (tiles256 >= 150) { c.NG = 4; c.PF = K <= 1024 || M >= 1024 || G >= 512 ? 1 : 2; c.GM = 8; c.OCC = 2; }
+  else { c.NG = 2; c.PF = 2; c.GM = 16; c.OCC = 1; }
   return c;
 }
 
