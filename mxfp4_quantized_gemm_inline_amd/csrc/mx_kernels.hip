@@ -395,11 +395,10 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
 
   // Loads are branch-free so the compiler can count them: tile rows past Mrows re-read the
   // last valid row and column groups past N re-read the last group; neither result is ever
-  // stored. The quad of lanes 4r..4r+3 of wave v quantizes, for i < BPT, row r of the
-  // 16-row tile v + NW i: lane 4r+j holds the 16-byte chunk j of each of the step's four
-  // 32-blocks, so every load instruction of the quad reads one block's 64 contiguous bytes.
-  // In LDS a tile holds its 16 x 4 operand blocks row-major with the block index
-  // XOR-swizzled by the row; the quant stores (one word per lane and block) and the MFMA
+  // stored. Lane 4r+j of wave v quantizes, for i < BPT, the whole 32-block j of row r of
+  // the 16-row tile v + NW i (four 16-byte loads; a quad covers the row's 256 contiguous
+  // bytes of the step). In LDS a tile holds its 16 x 4 operand blocks row-major with the
+  // block index XOR-swizzled by the row; the quant stores (16 bytes per lane) and the MFMA
   // reads (lane = row + 16 block) then fall on distinct banks.
   uint32_t aoff[BPT];
   const uint8_t* aptr[BPT];
@@ -408,18 +407,16 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
   for (int i = 0; i < BPT; ++i) {
     const int r = min(16 * (w + NW * i) + (lane >> 2), Mrows - 1);
     if constexpr (!Rows::kGather) {
-      aoff[i] = (uint32_t)r * (uint32_t)rows.K * 2u + (uint32_t)(lane & 3) * 16u;
+      aoff[i] = (uint32_t)r * (uint32_t)rows.K * 2u + (uint32_t)(lane & 3) * (kBlock * 2);
     } else {
       const int tk = rows.tok[r];
       avalid[i] = tk >= 0 && tk < rows.T;
-      aptr[i] = rows.A + (size_t)(avalid[i] ? tk : 0) * rows.K * 2 + (lane & 3) * 16;
+      aptr[i] = rows.A + (size_t)(avalid[i] ? tk : 0) * rows.K * 2 + (lane & 3) * (kBlock * 2);
     }
   }
   auto swz = [](int rr) { return ((rr >> 1) ^ (rr >> 2)) & 3; };
-  // LDS byte of this lane's word of block c within a tile is st_off ^ (c << 4) (bits 4-5
-  // of the unswizzled offset are zero, so the XOR applies the block swizzle)
-  const uint32_t st_off = (uint32_t)((lane >> 2) * 64 + (swz(lane >> 2) << 4) + (lane & 3) * 4);
-  const uint32_t st_sc = (uint32_t)(((lane >> 2) + 16 * (lane & 3)) * MTC);  // scale of block lane % 4
+  const uint32_t st_off = (uint32_t)(((lane >> 2) * 4 + ((lane & 3) ^ swz(lane >> 2))) * 16);
+  const uint32_t st_sc = (uint32_t)(((lane >> 2) + 16 * (lane & 3)) * MTC);  // this block's operand lane
   const uint32_t ld_off = (uint32_t)(((lane & 15) * 4 + ((lane >> 4) ^ swz(lane & 15))) * 16);
   constexpr int NQ = (NG + 3) / 4;  // scale words per step: one per column-group quad
   const uint8_t* wbase[NG];
@@ -440,10 +437,10 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
     if constexpr (!Rows::kGather) {
       const uint8_t* base = rows.base + (size_t)t * kStepK * 2;
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) load_quad_at(base, aoff[i], areg[SL][i]);
+      for (int i = 0; i < BPT; ++i) load_block_at(base, aoff[i], areg[SL][i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) load_quad_at(aptr[i] + (size_t)t * kStepK * 2, 0u, areg[SL][i]);
+      for (int i = 0; i < BPT; ++i) load_block_at(aptr[i] + (size_t)t * kStepK * 2, 0u, areg[SL][i]);
     }
   };
   auto load_w = [&](int t, auto slot_c) {
@@ -476,15 +473,14 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
     for (int i = 0; i < BPT; ++i) {
       const int tile = w + NW * i;
       uint32_t q[4];
-      uint32_t sc = quant_quad4(areg[SA][i], q);
+      uint32_t sc = quant_block(areg[SA][i], q);
       if constexpr (Rows::kGather) {  // a row with no valid token quantizes to zero
 #pragma unroll
         for (int c = 0; c < 4; ++c) q[c] = avalid[i] ? q[c] : 0u;
         sc = avalid[i] ? sc : 0u;
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint32_t*>(sq(buf, tile * 1024 + (st_off ^ (c << 4)))) = q[c];
-      *ss(buf, st_sc + tile) = (uint8_t)(sc >> (8 * (lane & 3)));
+      *reinterpret_cast<uint4*>(sq(buf, tile * 1024 + st_off)) = make_uint4(q[0], q[1], q[2], q[3]);
+      *ss(buf, st_sc + tile) = (uint8_t)sc;
     }
     const int tn = min(t + PF, T - 1);  // past the end: a harmless re-load of the last step
     load_a(tn, sa_c);
