@@ -147,11 +147,12 @@ mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_by
                             size_t buf_len);
 
 /*
- * The same for mx_a4w4_gemm_grouped (tuning override MX_GROUPED_CONFIG); "none" for
- * R_max == 0. Same shape rules and errors as the grouped GEMM, plus MX_ERR_NULL for buf.
+ * The same for mx_a4w4_gemm_grouped with E experts, R_max rows and T tokens (the choice
+ * may depend on any of them; tuning override MX_GROUPED_CONFIG); "none" for R_max == 0. Same shape rules and errors as the grouped
+ * GEMM, plus MX_ERR_NULL for buf.
  */
-mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t rows_hint,
-                                    char* buf, size_t buf_len);
+mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t T, int64_t N, int64_t K,
+                                    int64_t rows_hint, char* buf, size_t buf_len);
 
 #ifdef __cplusplus
 }

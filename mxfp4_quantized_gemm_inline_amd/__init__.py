@@ -28,7 +28,8 @@ SIGNATURES = {
     "mx_a4w4_gemm_grouped": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _c_i64,
                                       _c_i64, _c_i64, _vp]),
     "mx_a4w4_gemm_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_sz, ctypes.c_char_p, _c_sz]),
-    "mx_a4w4_gemm_grouped_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
+    "mx_a4w4_gemm_grouped_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_char_p,
+                                           _c_sz]),
 }
 
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE, MX_ERR_WORKSPACE, MX_ERR_HIP = range(7)
@@ -192,11 +193,11 @@ def mx_a4w4_gemm_plan(M: int, N: int, K: int, workspace_bytes=None) -> str:
     return buf.value.decode()
 
 
-def mx_a4w4_gemm_grouped_plan(E: int, R_max: int, N: int, K: int, rows_hint: int = 1) -> str:
-    """Kernel mx_a4w4_gemm_grouped launches for this table size and hint."""
+def mx_a4w4_gemm_grouped_plan(E: int, R_max: int, T: int, N: int, K: int, rows_hint: int = 1) -> str:
+    """Kernel mx_a4w4_gemm_grouped launches for this table size, token count and hint."""
     buf = ctypes.create_string_buffer(256)
-    _check(lib().mx_a4w4_gemm_grouped_plan(int(E), int(R_max), int(N), int(K), int(rows_hint), buf, len(buf)),
-           "mx_a4w4_gemm_grouped_plan")
+    _check(lib().mx_a4w4_gemm_grouped_plan(int(E), int(R_max), int(T), int(N), int(K), int(rows_hint), buf,
+                                           len(buf)), "mx_a4w4_gemm_grouped_plan")
     return buf.value.decode()
 
 

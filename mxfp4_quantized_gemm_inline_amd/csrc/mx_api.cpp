@@ -143,16 +143,17 @@ mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_by
   return MX_OK;
 }
 
-mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t rows_hint,
-                                    char* buf, size_t buf_len) {
-  if (E < 1 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1)
+mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t T, int64_t N, int64_t K,
+                                    int64_t rows_hint, char* buf, size_t buf_len) {
+  if (E < 1 || T < 0 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1 ||
+      T > (1ll << 31) - 1)
     return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;
   if (R_max == 0) {
     std::snprintf(buf, buf_len, "none");
     return MX_OK;
   }
-  if (!mx::grouped_plan(E, R_max, N, K, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
+  if (!mx::grouped_plan(E, R_max, N, K, T, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
     buf[0] = '\0';
     return MX_ERR_HIP;
   }

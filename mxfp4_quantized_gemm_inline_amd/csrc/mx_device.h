@@ -106,52 +106,6 @@ __device__ __forceinline__ uint32_t quant_block(const uint32_t (&x)[16], uint32_
   return s;
 }
 
-// Quad-split quantizer. The four lanes 4r..4r+3 of a quad share four consecutive 32-blocks
-// of one row: lane 4r+j holds in x[4c..4c+3] elements 8j..8j+7 of block c (a 16-byte chunk),
-// so each of the quad's four loads covers one block's 64 contiguous bytes. The block
-// exponent is reduced across the quad with DPP; q[c] receives this lane's four E2M1 bytes
-// of block c (bytes 4j..4j+3 of the block in canonical order). Returns the four scale
-// bytes packed (byte c = block c), the same value in all four lanes of the quad.
-__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
-  // quad_perm [1,0,3,2] then [2,3,0,1]: every lane ends with the maximum of its quad
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t quant_quad4(const uint32_t (&x)[16], uint32_t (&q)[4]) {
-  uint32_t packed = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, x[4 * c + 0] & 0x7F807F80u),
-                                              __builtin_bit_cast(u16x2, x[4 * c + 1] & 0x7F807F80u));
-    const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, x[4 * c + 2] & 0x7F807F80u),
-                                              __builtin_bit_cast(u16x2, x[4 * c + 3] & 0x7F807F80u));
-    const u16x2 m = __builtin_elementwise_max(a, b);
-    const uint32_t E = quad_max_u32(m.x > m.y ? (uint32_t)m.x : (uint32_t)m.y) >> 7;
-    const uint32_t s = E > 2u ? E - 2u : 0u;
-    const float sc = __builtin_bit_cast(float, s ? (s << 23) : 0x00400000u);
-    uint32_t r = 0;
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x[4 * c + 0]), sc, 0);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x[4 * c + 1]), sc, 1);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x[4 * c + 2]), sc, 2);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x[4 * c + 3]), sc, 3);
-    q[c] = r;
-    packed |= s << (8 * c);
-  }
-  return packed;
-}
-
-// Load the quad-split share of four consecutive 32-blocks: x[4c..4c+3] = the 16 bytes at
-// base + off + 64 c (off already includes the lane's 16-byte chunk offset).
-__device__ __forceinline__ void load_quad_at(const uint8_t* __restrict__ base, uint32_t off, uint32_t (&x)[16]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint4 u = *reinterpret_cast<const uint4*>(base + off + 64 * c);
-    x[4 * c + 0] = u.x; x[4 * c + 1] = u.y; x[4 * c + 2] = u.z; x[4 * c + 3] = u.w;
-  }
-}
-
 // Load one 32-element bf16 block (64 bytes, 16-byte aligned) into 16 words.
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ p, uint32_t (&x)[16]) {
   const uint4* v = reinterpret_cast<const uint4*>(p);

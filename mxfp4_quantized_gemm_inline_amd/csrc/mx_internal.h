@@ -18,6 +18,7 @@ hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const in
                                int64_t N, int64_t K, int64_t rows_hint, hipStream_t st);
 // Name the kernel(s) the launchers above would run (false: the tuning override is invalid).
 bool gemm_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes, char* buf, size_t len);
-bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t rows_hint, char* buf, size_t len);
+bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t T, int64_t rows_hint, char* buf,
+                  size_t len);
 
 }  // namespace mx

@@ -621,11 +621,12 @@ void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restri
     }
   }
   __syncthreads();
-  const int e = s_unit[0];
+  // uniform across the CTA: keep them (and every address derived from them) scalar
+  const int e = __builtin_amdgcn_readfirstlane(s_unit[0]);
   if (e < 0) return;  // surplus CTA: the grid over-counts the units
-  const int lo = s_unit[1], cnt = s_unit[2];
+  const int lo = __builtin_amdgcn_readfirstlane(s_unit[1]), cnt = __builtin_amdgcn_readfirstlane(s_unit[2]);
   const int tiles_e = (cnt + BM - 1) / BM;
-  const int rem = L - s_unit[3], bn = rem / tiles_e, mt = rem % tiles_e;
+  const int rem = L - __builtin_amdgcn_readfirstlane(s_unit[3]), bn = rem / tiles_e, mt = rem % tiles_e;
   const int r0 = lo + mt * BM, Mrows = min(BM, cnt - mt * BM);
   uint16_t* Cout = C + (size_t)r0 * N;
 
@@ -1317,7 +1318,7 @@ bool grouped_tile_supported(const GroupedConfig& g) {
 // The configuration a grouped call runs. Tuning only: MX_GROUPED_CONFIG="gs,MT,NG"
 // (streaming, four waves) or "gt,WM,WN,MT,NG,PF,OCC" (tiled) replaces the default choice;
 // false when it names no compiled configuration (the call then fails).
-bool resolve_grouped(int E, int R_max, int N, int64_t rows_hint, GroupedConfig& g) {
+bool resolve_grouped(int E, int R_max, int N, int64_t rows_hint, GroupedConfig& g) {  // any T
   const int G = N / 16;
   const int64_t active = E < R_max ? E : R_max;
   const char* s = std::getenv("MX_GROUPED_CONFIG");
@@ -1371,7 +1372,8 @@ hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const in
   return hipErrorInvalidValue;
 }
 
-bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t rows_hint, char* buf, size_t len) {
+bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t /*T*/, int64_t rows_hint, char* buf,
+                  size_t len) {
   GroupedConfig g;
   if (!resolve_grouped((int)E, (int)R_max, (int)N, rows_hint, g)) return false;
   if (g.tile) {

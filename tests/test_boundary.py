@@ -121,14 +121,14 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
 def test_grouped_plan_names_the_selected_kernel(monkeypatch):
     monkeypatch.delenv("MX_GROUPED_CONFIG", raising=False)
     N, K, E = 1536, 3584, 896
-    assert mx.mx_a4w4_gemm_grouped_plan(E, 0, N, K) == "none"
-    assert mx.mx_a4w4_gemm_grouped_plan(E, 16, N, K).startswith("k_gemm_grouped<1, 1, 4, ")
-    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, N, K, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 1, 2>"
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 0, 0, N, K) == "none"
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 16, 1, N, K).startswith("k_gemm_grouped<1, 1, 4, ")
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 1, 2>"
     monkeypatch.setenv("MX_GROUPED_CONFIG", "gs,2,4")
-    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, N, K).startswith("k_gemm_grouped<2, 4, 4, ")
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K).startswith("k_gemm_grouped<2, 4, 4, ")
     monkeypatch.setenv("MX_GROUPED_CONFIG", "gt,1,4,4,4,3,2")
     with pytest.raises(mx.MxError):
-        mx.mx_a4w4_gemm_grouped_plan(E, 65536, N, K)
+        mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K)
 
 
 def test_plan_argument_errors():
@@ -137,7 +137,8 @@ def test_plan_argument_errors():
     assert f(16, 100, 256, 0, buf, 64) == mx.MX_ERR_SHAPE
     assert f(16, 256, 256, 0, None, 64) == mx.MX_ERR_NULL
     assert f(16, 256, 256, 0, buf, 0) == mx.MX_ERR_NULL
-    assert g(0, 16, 256, 256, 1, buf, 64) == mx.MX_ERR_SHAPE
-    assert g(4, 16, 256, 256, 1, None, 64) == mx.MX_ERR_NULL
+    assert g(0, 16, 1, 256, 256, 1, buf, 64) == mx.MX_ERR_SHAPE
+    assert g(4, 16, -1, 256, 256, 1, buf, 64) == mx.MX_ERR_SHAPE
+    assert g(4, 16, 1, 256, 256, 1, None, 64) == mx.MX_ERR_NULL
     tiny = ctypes.create_string_buffer(8)  # truncated, still NUL-terminated
     assert f(2048, 7168, 768, 0, tiny, 8) == mx.MX_OK and tiny.value == b"k_gemm_"
