@@ -9,6 +9,7 @@
 // the quantized activations are the "B" operand (16 output rows m as columns), so lane l's
 // accumulator element r is C[m = l % 16][n = 4 * (l / 16) + r]: four consecutive columns of
 // one output row, stored as one 8-byte write.
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -97,8 +98,9 @@ __global__ __launch_bounds__(256) void k_unprepare(const uint8_t* __restrict__ W
 // never multiplied), and the first activation batch is issued before them, so the compiler's
 // in-order wait counts let the weight stream stay in flight while the quantizer runs.
 //
-// LDS: quantized activations [16 MT][TS * 64 + 16] (the 16-byte pad staggers rows across
-// banks), then their scales [16 MT][4 TS]; reused for the cross-wave reduction.
+// LDS: quantized activations [R][TS * 64 + 16] (the 16-byte pad staggers rows across banks),
+// then their scales [R][4 TS], R = the rows a launch stages (at most 16 MT; reads of rows
+// past the valid count are clamped to the last one); reused for the cross-wave reduction.
 constexpr int kSkinnyPD = 16;
 
 // Rows of a dense row-major A.
@@ -135,7 +137,7 @@ struct StreamCTA {
   uint32_t wsb[PD][NG];
 
   __device__ __forceinline__ void init(const uint8_t* wp, int N, int K, int g0_, int ks0_, int ks1, int TS,
-                                       uint8_t* smem) {
+                                       int R, uint8_t* smem) {
     lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     T = steps_of(K);
@@ -151,7 +153,7 @@ struct StreamCTA {
     Wp = wp;
     Wsc = wp + payload_bytes(N, K);
     aq = smem;
-    as = smem + (size_t)(16 * MT) * RS;
+    as = smem + (size_t)R * RS;
   }
 
   __device__ __forceinline__ void load_w(int tb) {
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restr
   const int T = steps_of(K);
   const int ks0 = min(T, (int)blockIdx.y * TS), ks1 = min(T, ks0 + TS);
   StreamCTA<MT, NG, WK, PD, QB> cta;
-  cta.init(Wp, N, K, blockIdx.x * NG, ks0, ks1, TS, smem);
+  cta.init(Wp, N, K, blockIdx.x * NG, ks0, ks1, TS, min(M, 16 * MT), smem);
   const DenseRows rows{A, K};
   cta.quant(rows, M, [&] { if (cta.S > 0) cta.load_w(cta.t0); });
   __syncthreads();
@@ -893,7 +895,7 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_grouped(const uint16_t* __rest
   const int T = steps_of(K);
   const uint8_t* __restrict__ Wp = Wall + (size_t)e * prepared_bytes(N, K);
   StreamCTA<MT, NG, WK, PD, QB> cta;
-  cta.init(Wp, N, K, g0, 0, T, T, smem);
+  cta.init(Wp, N, K, g0, 0, T, T, 16 * MT, smem);
   // RES: every wave's whole K share fits in its PD weight registers (checked by the host),
   // so the weight is loaded once and reused for every row chunk.
 
@@ -958,8 +960,8 @@ hipError_t ensure_lds_limit(const void* kern, std::atomic<uint64_t>& done) {
   return e;
 }
 
-// LDS of a StreamCTA with room for 16 * MT rows of a slice of TS steps: quantized rows, their
-// scales, or the cross-wave reduction, whichever is larger.
+// LDS of a StreamCTA staging M rows of a slice of TS steps: quantized rows, their scales, or
+// the cross-wave reduction, whichever is larger.
 size_t stream_lds_bytes(int M, int TS, int MT, int NG, int WK) {
   const size_t act = (size_t)M * (TS * 64 + 16) + (size_t)M * 4 * TS;
   const size_t red = (size_t)WK * NG * MT * 64 * 16;
@@ -976,8 +978,8 @@ struct GemmConfig {
 };
 
 #define MX_STREAM_CONFIGS(X) \
-  X(1, 1, 2) X(1, 1, 4) X(1, 1, 8) X(1, 2, 4) X(1, 2, 8) X(1, 4, 4) \
-  X(2, 1, 2) X(2, 1, 4) X(2, 1, 8) X(2, 2, 4) X(2, 2, 8) X(2, 4, 4) \
+  X(1, 1, 2) X(1, 1, 4) X(1, 1, 8) X(1, 2, 4) X(1, 2, 8) X(1, 4, 4) X(1, 4, 8) \
+  X(2, 1, 2) X(2, 1, 4) X(2, 1, 8) X(2, 2, 4) X(2, 2, 8) X(2, 4, 4) X(2, 4, 8) \
   X(4, 1, 4) X(4, 1, 8) X(4, 2, 4) X(4, 4, 4) X(8, 1, 4) X(8, 2, 4)
 
 #define MX_WIDE_CONFIGS(X) X(8, 2) X(8, 4) X(4, 4) X(4, 8)
@@ -1030,7 +1032,7 @@ hipError_t run_stream(const void* a, const void* wp, void* c, float* P, int M, i
                       hipStream_t st) {
   const int T = steps_of(K);
   const int TS = (T + S - 1) / S;
-  const size_t lds = stream_lds_bytes(16 * MT, TS, MT, NG, WK);
+  const size_t lds = stream_lds_bytes(min(M, 16 * MT), TS, MT, NG, WK);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   const int per = (TS + WK - 1) / WK;
   const int pd = pick_pd(NG, per);
@@ -1124,7 +1126,8 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   auto stream_fits = [&](const GemmConfig& s) {
     const int TS = (T + s.S - 1) / s.S;
     const size_t need = s.S > 1 ? (size_t)s.S * M * N * 4 : 0;
-    return need <= ws_bytes && stream_lds_bytes(16 * s.MT, TS, s.MT, s.NG, s.WK) <= kMaxLds && G % s.NG == 0;
+    return need <= ws_bytes && stream_lds_bytes(std::min(M, 16 * s.MT), TS, s.MT, s.NG, s.WK) <= kMaxLds &&
+           G % s.NG == 0;
   };
   if (M <= 32 || (M <= 128 && G <= 96)) {
     // weight-streaming kernel: the weight is read once, straight into registers
@@ -1137,13 +1140,20 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
       s.NG = (G >= 256 && G < 512) ? 2 : 1;
       s.WK = longk ? 8 : 4;
     } else if (M <= 16) {
-      s.NG = G >= 256 ? 2 : 1;
+      // four column groups share each scale word the CTA loads (one scale request per four
+      // weight requests instead of one per request)
+      s.NG = G >= 512 ? 4 : (G >= 256 ? 2 : 1);
       s.WK = longk ? 8 : 4;
-      if (G >= 512 && T >= 32) s.S = 2;
     } else if (M <= 32) {
-      s.NG = G >= 512 ? 4 : 2;
-      s.WK = (longk && G < 512) ? 8 : 4;
-      if (G >= 512 && T >= 32) s.S = 4;
+      s.WK = longk ? 8 : 4;
+      if (G >= 512) {
+        s.NG = 4;
+      } else if (G >= 256 && longk && (size_t)2 * M * N * 4 <= ws_bytes) {
+        s.NG = 4;
+        s.S = 2;
+      } else {
+        s.NG = 2;
+      }
     } else {
       s.NG = 2;
       s.WK = 4;
@@ -1214,7 +1224,7 @@ bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
     const size_t need = cfg.S > 1 ? (size_t)cfg.S * M * N * 4 : 0;
     const int TS = (T + cfg.S - 1) / cfg.S;
     if (M > 16 * cfg.MT || need > ws_bytes || (N / 16) % cfg.NG != 0 ||
-        stream_lds_bytes(16 * cfg.MT, TS, cfg.MT, cfg.NG, cfg.WK) > kMaxLds)
+        stream_lds_bytes(std::min(M, 16 * cfg.MT), TS, cfg.MT, cfg.NG, cfg.WK) > kMaxLds)
       return false;
   }
   return true;

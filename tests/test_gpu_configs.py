@@ -17,8 +17,8 @@ from gpu_util import check_gemm, dev_bf16, host_bits, lib_or_fail, torch_or_skip
 pytestmark = pytest.mark.gpu
 
 # mirrors MX_STREAM_CONFIGS / MX_TILE_CONFIGS in the kernels
-STREAM = [(1, 1, 2), (1, 1, 4), (1, 1, 8), (1, 2, 4), (1, 2, 8), (1, 4, 4),
-          (2, 1, 2), (2, 1, 4), (2, 1, 8), (2, 2, 4), (2, 2, 8), (2, 4, 4),
+STREAM = [(1, 1, 2), (1, 1, 4), (1, 1, 8), (1, 2, 4), (1, 2, 8), (1, 4, 4), (1, 4, 8),
+          (2, 1, 2), (2, 1, 4), (2, 1, 8), (2, 2, 4), (2, 2, 8), (2, 4, 4), (2, 4, 8),
           (4, 1, 4), (4, 1, 8), (4, 2, 4), (4, 4, 4), (8, 1, 4), (8, 2, 4)]
 TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8, 1, 1), (1, 4, 4, 2, 2, 1),
         (1, 4, 4, 4, 1, 2), (1, 4, 4, 4, 2, 2), (2, 4, 4, 4, 1, 1), (1, 4, 4, 2, 2, 2)]
@@ -52,7 +52,7 @@ def _run(cfg, a, wp, ws):
 
 
 def _stream_lds(M, TS, MT, NG, WK):
-    R = 16 * MT
+    R = min(M, 16 * MT)
     return max(R * (TS * 64 + 16) + R * 4 * TS, WK * NG * MT * 1024)
 
 
