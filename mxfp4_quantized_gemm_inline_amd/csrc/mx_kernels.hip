@@ -1350,7 +1350,7 @@ bool resolve_grouped(int E, int R_max, int N, int64_t rows_hint, GroupedConfig& 
   // CTA as segments grow, amortizing each CTA's serial segment-lookup -> token ->
   // activation chain over more streamed weight.
   if (G % 16 == 0 && active * (G / 16) >= 512) {
-    g = GroupedConfig{true, 1, 4, 4, 4, 1, 2};
+    g = GroupedConfig{true, 1, 4, 4, 4, 2, 2};
     return true;
   }
   g.tile = false;

@@ -123,7 +123,7 @@ def test_grouped_plan_names_the_selected_kernel(monkeypatch):
     N, K, E = 1536, 3584, 896
     assert mx.mx_a4w4_gemm_grouped_plan(E, 0, 0, N, K) == "none"
     assert mx.mx_a4w4_gemm_grouped_plan(E, 16, 1, N, K).startswith("k_gemm_grouped<1, 1, 4, ")
-    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 1, 2>"
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2>"
     monkeypatch.setenv("MX_GROUPED_CONFIG", "gs,2,4")
     assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K).startswith("k_gemm_grouped<2, 4, 4, ")
     monkeypatch.setenv("MX_GROUPED_CONFIG", "gt,1,4,4,4,3,2")
