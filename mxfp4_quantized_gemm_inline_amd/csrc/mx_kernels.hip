@@ -986,7 +986,7 @@ struct GemmConfig {
 
 #define MX_TILE_CONFIGS(X) \
   X(1, 4, 4, 4, 2, 1) X(2, 4, 4, 4, 2, 1) X(1, 4, 8, 4, 1, 1) X(2, 2, 4, 8, 1, 1) X(1, 4, 4, 2, 2, 1) \
-  X(1, 4, 4, 4, 1, 2) X(1, 4, 4, 4, 2, 2) X(2, 4, 4, 4, 1, 1) X(1, 4, 4, 2, 2, 2)
+  X(1, 4, 4, 4, 1, 2) X(1, 4, 4, 4, 2, 2) X(2, 4, 4, 4, 1, 1) X(1, 4, 4, 2, 2, 2) X(1, 8, 8, 4, 1, 2)
 
 // Weight prefetch depth: enough registers for a wave's whole K share when it fits (4, 8 or
 // 16 steps of NG operands, at most kSkinnyPD operands), so no registers go to duplicate
@@ -1167,9 +1167,19 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   // tiled kernel: 64 x 256 tiles when there are enough of them (two steps of prefetch only
   // for long K at moderate sizes), else 64 x 128 tiles at one CTA per SIMD set
   c.tile = true;
+  // 128 x 512 tiles (eight waves of 128 x 64) halve the load instructions per output; they
+  // pay when one round of them (at most one per CU) nearly fills the chip
+  const int64_t tiles512 = (int64_t)((M + 127) / 128) * (N / 512);
+  if (N % 512 == 0 && tiles512 >= 160 && tiles512 <= 256) {
+    c.WM = 1; c.WN = 8; c.MT = 8; c.NG = 4; c.PF = 1; c.GM = 8; c.OCC = 2;
+    return c;
+  }
   c.WM = 1; c.WN = 4; c.MT = 4;
   const int64_t tiles256 = (int64_t)((M + 63) / 64) * ((N + 255) / 256);
-  if (tiles256 >= 150) { c.NG = 4; c.PF = K <= 1024 || M >= 1024 || G >= 512 ? 1 : 2; c.GM = 8; c.OCC = 2; }
+  if (tiles256 >= 150) {
+    c.NG = 4; c.GM = 8; c.OCC = 2;
+    c.PF = K <= 1024 || G >= 512 || (M >= 1024 && G >= 256) ? 1 : 2;
+  }
   else { c.NG = 2; c.PF = 2; c.GM = 16; c.OCC = 1; }
   return c;
 }

@@ -106,7 +106,8 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     monkeypatch.delenv("MX_GEMM_CONFIG", raising=False)
     assert mx.mx_a4w4_gemm_plan(0, 7168, 768) == "none"
     assert mx.mx_a4w4_gemm_plan(1, 7168, 768).startswith("k_gemm_stream<1, ")
-    assert mx.mx_a4w4_gemm_plan(2048, 7168, 768) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 768) == "k_gemm_tile<1, 8, 8, 4, 1, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
     # split K only with a workspace; the streaming kernels never need one otherwise
     with_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168)
     no_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168, workspace_bytes=0)
