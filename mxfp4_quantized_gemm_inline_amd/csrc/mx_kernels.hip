@@ -377,11 +377,12 @@ struct TileRowsGather {
 
 // The tiled main loop and epilogue for one BM x BN output tile: Mrows (1..BM) valid rows
 // from `rows`, weight column tile bn of the prepared weight Wp, output rows written at
-// Cout + r * N for r < Mrows (columns past N masked).
+// Cout + r * N for r < Mrows (columns past N masked). Only K steps [tb, te) are summed; with
+// Pout the FP32 sums go to Pout + r * N (one K slice's partial tile) instead of bf16 to Cout.
 template <int WM, int WN, int MT, int NG, int PF, class Rows>
 __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uint8_t* __restrict__ Wp,
-                                          uint16_t* __restrict__ Cout, int N, int K, int bn,
-                                          uint8_t* __restrict__ smem) {
+                                          uint16_t* __restrict__ Cout, float* __restrict__ Pout, int N,
+                                          int K, int bn, int tb, int te, uint8_t* __restrict__ smem) {
   using S = TileShape<WM, WN, MT, NG>;
   constexpr int MTC = S::MTC, BM = S::BM, BN = S::BN, NW = S::NW, BPT = S::BPT;
   constexpr int SQ = S::SQ, SS = S::SS, CROW = S::CROW;
@@ -461,8 +462,8 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
 
   // prologue: steps 0 .. PF-1 in flight (clamped to the last step when T < PF)
   static_for<PF>([&](auto p) {
-    load_a(min((int)decltype(p)::value, T - 1), p);
-    load_w(min((int)decltype(p)::value, T - 1), p);
+    load_a(min(tb + (int)decltype(p)::value, te - 1), p);
+    load_w(min(tb + (int)decltype(p)::value, te - 1), p);
   });
 
   auto step = [&](int t, auto sa_c, auto sw_c) {
@@ -484,7 +485,7 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
       *reinterpret_cast<uint4*>(sq(buf, tile * 1024 + st_off)) = make_uint4(q[0], q[1], q[2], q[3]);
       *ss(buf, st_sc + tile) = (uint8_t)sc;
     }
-    const int tn = min(t + PF, T - 1);  // past the end: a harmless re-load of the last step
+    const int tn = min(t + PF, te - 1);  // past the end: a harmless re-load of the last step
     load_a(tn, sa_c);
     load_w(tn, std::integral_constant<int, (SW + PF) % (PF + 1)>{});
     __syncthreads();
@@ -511,8 +512,8 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
   };
 
   constexpr int U = PF * (PF + 1);
-  int t = 0;
-  for (; t + U <= T; t += U) {
+  int t = tb;
+  for (; t + U <= te; t += U) {
     static_for<U>([&](auto i) {
       constexpr int I = decltype(i)::value;
       step(t + I, std::integral_constant<int, I % PF>{}, std::integral_constant<int, I % (PF + 1)>{});
@@ -520,8 +521,20 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
   }
   static_for<U - 1>([&](auto i) {
     constexpr int I = decltype(i)::value;
-    if (t + I < T) step(t + I, std::integral_constant<int, I % PF>{}, std::integral_constant<int, I % (PF + 1)>{});
+    if (t + I < te) step(t + I, std::integral_constant<int, I % PF>{}, std::integral_constant<int, I % (PF + 1)>{});
   });
+
+  if (Pout) {  // a K slice: FP32 partial sums, 16 bytes per lane (four columns of one row)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = 16 * (wm * MT + mt) + (lane & 15);
+        if (r < Mrows && gw0 + g < G)
+          *reinterpret_cast<v4f*>(Pout + (size_t)r * N + 16 * (gw0 + g) + 4 * (lane >> 4)) = acc[g][mt];
+      }
+    return;
+  }
 
   // Epilogue: each lane holds four consecutive columns of one row per MFMA tile; stage the
   // tile in LDS as bf16, then every wave store writes 16 bytes per lane along whole rows.
@@ -554,15 +567,18 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
 template <int WM, int WN, int MT, int NG, int PF, int OCC>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void k_gemm_tile(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
-                 int M, int N, int K, int GM) {
+                 float* __restrict__ P, int M, int N, int K, int GM, int TS) {
   using S = TileShape<WM, WN, MT, NG>;
   __shared__ __align__(16) uint8_t smem[S::SMEM];
   const int tiles_m = (M + S::BM - 1) / S::BM, tiles_n = (N + S::BN - 1) / S::BN;
   int bm, bn;
   tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, GM, bm, bn);
   const int m0 = bm * S::BM;
+  // K slice blockIdx.y of TS steps; with P, its FP32 partial tile goes to P[slice]
+  const int T = steps_of(K), tb = min(T, (int)blockIdx.y * TS), te = min(T, tb + TS);
+  float* Pout = P ? P + ((size_t)blockIdx.y * M + m0) * N : nullptr;
   const TileRowsDense rows{reinterpret_cast<const uint8_t*>(A) + (size_t)m0 * K * 2, K};
-  tile_core<WM, WN, MT, NG, PF>(rows, min(S::BM, M - m0), Wp, C + (size_t)m0 * N, N, K, bn, smem);
+  tile_core<WM, WN, MT, NG, PF>(rows, min(S::BM, M - m0), Wp, C + (size_t)m0 * N, Pout, N, K, bn, tb, te, smem);
 }
 
 // ====================================================================== grouped MoE GEMM1, tiled
@@ -641,7 +657,8 @@ void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restri
     return;
   }
   const TileRowsGather rows{reinterpret_cast<const uint8_t*>(A), row_token + r0, Ttok, K};
-  tile_core<WM, WN, MT, NG, PF>(rows, Mrows, Wall + (size_t)e * prepared_bytes(N, K), Cout, N, K, bn, smem);
+  tile_core<WM, WN, MT, NG, PF>(rows, Mrows, Wall + (size_t)e * prepared_bytes(N, K), Cout, nullptr, N, K, bn, 0,
+                                steps_of(K), smem);
 }
 
 // ====================================================================== wide-tile GEMM (large M)
@@ -1046,12 +1063,22 @@ hipError_t run_stream(const void* a, const void* wp, void* c, float* P, int M, i
 }
 
 template <int WM, int WN, int MT, int NG, int PF, int OCC>
-hipError_t run_tile(const void* a, const void* wp, void* c, int M, int N, int K, int GM, hipStream_t st) {
+hipError_t run_tile(const void* a, const void* wp, void* c, float* P, int M, int N, int K, int GM, int S,
+                    hipStream_t st) {
   constexpr int BM = 16 * MT * WM, BN = 16 * NG * WN;
   const int64_t grid = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((k_gemm_tile<WM, WN, MT, NG, PF, OCC>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, st,
-                     static_cast<const uint16_t*>(a), static_cast<const uint8_t*>(wp),
-                     static_cast<uint16_t*>(c), M, N, K, GM);
+  const int T = steps_of(K);
+  if (!P) S = 1;
+  const int TS = (T + S - 1) / S;
+  S = (T + TS - 1) / TS;  // no empty slices
+  hipLaunchKernelGGL((k_gemm_tile<WM, WN, MT, NG, PF, OCC>), dim3((unsigned)grid, (unsigned)S), dim3(64 * WM * WN),
+                     0, st, static_cast<const uint16_t*>(a), static_cast<const uint8_t*>(wp),
+                     static_cast<uint16_t*>(c), S > 1 ? P : nullptr, M, N, K, GM, TS);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t MN = (int64_t)M * N;
+  hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, st, P,
+                     static_cast<uint16_t*>(c), MN, S);
   return hipGetLastError();
 }
 
@@ -1104,7 +1131,7 @@ hipError_t run_config(const GemmConfig& c, const void* a, const void* wp, void* 
   } else {
 #define X(wm, wn, mt, ng, pf, occ) \
   if (c.WM == wm && c.WN == wn && c.MT == mt && c.NG == ng && c.PF == pf && c.OCC == occ) \
-    return run_tile<wm, wn, mt, ng, pf, occ>(a, wp, out, M, N, K, c.GM, st);
+    return run_tile<wm, wn, mt, ng, pf, occ>(a, wp, out, P, M, N, K, c.GM, c.S, st);
     MX_TILE_CONFIGS(X)
 #undef X
   }
@@ -1129,7 +1156,9 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
     return need <= ws_bytes && stream_lds_bytes(std::min(M, 16 * s.MT), TS, s.MT, s.NG, s.WK) <= kMaxLds &&
            G % s.NG == 0;
   };
-  if (M <= 32 || (M <= 128 && G <= 96)) {
+  // long K: the tiled kernel with K slices when the caller offers room for the partials
+  const bool split_ok = T >= 16 && (size_t)2 * M * N * 4 <= ws_bytes;
+  if (M <= 32 || (M <= 128 && G <= 96 && !split_ok)) {
     // weight-streaming kernel: the weight is read once, straight into registers
     GemmConfig s;
     s.tile = false;
@@ -1176,16 +1205,31 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   }
   c.WM = 1; c.WN = 4; c.MT = 4;
   const int64_t tiles256 = (int64_t)((M + 63) / 64) * ((N + 255) / 256);
+  const int64_t tiles128 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
   if (tiles256 >= 150) {
     c.NG = 4; c.GM = 8; c.OCC = 2;
     c.PF = K <= 1024 || G >= 512 || (M >= 1024 && G >= 256) ? 1 : 2;
+    return c;
   }
-  else { c.NG = 2; c.PF = 2; c.GM = 16; c.OCC = 1; }
+  if (split_ok) {
+    // Few tiles at long K: split K into S slices (at least 6 steps each) so that about 200
+    // CTAs run, one per CU or fewer; FP32 partials go to the workspace and k_splitk_reduce
+    // adds them in slice order. 64 x 256 tiles unless even eight slices of them are too few.
+    const int64_t tiles = tiles256 * 8 >= 150 ? tiles256 : tiles128;
+    if (tiles == tiles256) { c.NG = 4; c.PF = 2; c.GM = 8; c.OCC = 2; }
+    else { c.NG = 2; c.PF = 2; c.GM = 8; c.OCC = 2; }
+    int sk = (int)std::min<int64_t>(8, (200 + tiles / 2) / tiles);
+    sk = std::max(1, std::min(sk, T / 6));
+    while (sk > 1 && (size_t)sk * M * N * 4 > ws_bytes) --sk;
+    c.S = sk;
+    return c;
+  }
+  c.NG = 2; c.PF = 2; c.GM = 16; c.OCC = 1;
   return c;
 }
 
-// Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming), "t,WM,WN,MT,NG,PF,GM[,OCC]" (tiled)
-// or "w,MT,NG,GM" (wide-tile)
+// Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming), "t,WM,WN,MT,NG,PF,GM[,OCC[,S]]" (tiled,
+// S = K slices) or "w,MT,NG,GM" (wide-tile)
 // replaces the default choice. Returns 0 when unset, 1 when applied, -1 when the string
 // does not name a compiled configuration (the call then fails rather than silently
 // running something else).
@@ -1193,16 +1237,18 @@ int override_config(GemmConfig& c) {
   const char* e = std::getenv("MX_GEMM_CONFIG");
   if (!e || !*e) return 0;
   GemmConfig o;
-  int v[7] = {0, 0, 0, 0, 0, 0, 0};
+  int v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (e[0] == 's' && std::sscanf(e, "s,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) == 4) {
     o.tile = false; o.MT = v[0]; o.NG = v[1]; o.WK = v[2]; o.S = v[3];
     if (!stream_supported(o.MT, o.NG, o.WK) || o.S < 1) return -1;
   } else if (e[0] == 'w' && std::sscanf(e, "w,%d,%d,%d", &v[0], &v[1], &v[2]) == 3) {
     o.tile = true; o.wide = true; o.MT = v[0]; o.NG = v[1]; o.GM = v[2] < 1 ? 1 : v[2];
     if (!wide_supported(o.MT, o.NG)) return -1;
-  } else if (e[0] == 't' && std::sscanf(e, "t,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6]) >= 6) {
+  } else if (e[0] == 't' && std::sscanf(e, "t,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5],
+                                         &v[6], &v[7]) >= 6) {
     o.tile = true; o.WM = v[0]; o.WN = v[1]; o.MT = v[2]; o.NG = v[3]; o.PF = v[4]; o.GM = v[5] < 1 ? 1 : v[5];
     o.OCC = v[6] < 1 ? 1 : v[6];
+    o.S = v[7] < 1 ? 1 : v[7];
     if (!tile_supported(o)) return -1;
   } else {
     return -1;
@@ -1216,18 +1262,24 @@ int override_config(GemmConfig& c) {
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0) return 0;
   const GemmConfig c = select_config((int)M, (int)N, (int)K, (size_t)-1);
-  return (!c.tile && c.S > 1) ? (size_t)c.S * (size_t)M * (size_t)N * 4 : 0;
+  return c.S > 1 ? (size_t)c.S * (size_t)M * (size_t)N * 4 : 0;
 }
 
 namespace {
 
 // The configuration a dense call runs: the default choice or the tuning override. False
 // when the override names nothing compiled or cannot run this call (a streaming choice
-// must cover M, fit its K slice in LDS and its partials in the workspace).
+// must cover M, fit its K slice in LDS and its partials in the workspace; a sliced tiled
+// choice must fit its partials).
 bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
   cfg = select_config(M, N, K, ws_bytes);
   const int ov = override_config(cfg);
   if (ov < 0) return false;
+  if (ov > 0 && cfg.tile && !cfg.wide && cfg.S > 1) {
+    const int T = steps_of(K);
+    if (cfg.S > T) cfg.S = T;
+    if ((size_t)cfg.S * M * N * 4 > ws_bytes) return false;
+  }
   if (ov > 0 && !cfg.tile) {
     const int T = steps_of(K);
     if (cfg.S > T) cfg.S = T;
@@ -1248,8 +1300,7 @@ hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M64, int6
   if (!ws) ws_bytes = 0;
   GemmConfig cfg;
   if (!resolve_config(M, N, K, ws_bytes, cfg)) return hipErrorInvalidValue;
-  return run_config(cfg, a, wp, c, cfg.tile ? nullptr : (cfg.S > 1 ? static_cast<float*>(ws) : nullptr),
-                    M, N, K, st);
+  return run_config(cfg, a, wp, c, cfg.S > 1 ? static_cast<float*>(ws) : nullptr, M, N, K, st);
 }
 
 bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf, size_t len) {
@@ -1259,7 +1310,11 @@ bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf
   if (c.wide) {
     std::snprintf(buf, len, "k_gemm_wide<%d, %d> GM=%d", c.MT, c.NG, c.GM);
   } else if (c.tile) {
-    std::snprintf(buf, len, "k_gemm_tile<%d, %d, %d, %d, %d, %d> GM=%d", c.WM, c.WN, c.MT, c.NG, c.PF, c.OCC, c.GM);
+    const int T = steps_of(K), TS = (T + c.S - 1) / c.S, S = (T + TS - 1) / TS;  // as run_tile slices
+    char split[40] = "";
+    if (S > 1) std::snprintf(split, sizeof split, " S=%d + k_splitk_reduce", S);
+    std::snprintf(buf, len, "k_gemm_tile<%d, %d, %d, %d, %d, %d> GM=%d%s", c.WM, c.WN, c.MT, c.NG, c.PF, c.OCC,
+                  c.GM, split);
   } else {
     const int T = steps_of(K), TS = (T + c.S - 1) / c.S, per = (TS + c.WK - 1) / c.WK;
     std::snprintf(buf, len, "k_gemm_stream<%d, %d, %d, %d, %d> S=%d%s", c.MT, c.NG, c.WK, pick_pd(c.NG, per),

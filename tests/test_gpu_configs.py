@@ -82,6 +82,26 @@ def test_tile_config(cfg, K):
         c = _run("t," + ",".join(map(str, cfg[:5])) + f",{gm},{cfg[5]}", a[:M], wp, False)
         torch.cuda.synchronize()
         check_gemm(c, exact[:M], what=f"tile {cfg} GM={gm} M={M} K={K}")
+    # K slices (FP32 partials in the workspace, reduced in slice order); 4 slices of 6 steps
+    # leave an uneven last slice at K = 4224
+    for M, S in ((100, 3), (37, 4)):
+        ws = torch.empty(S * M * N_TEST * 4, dtype=torch.uint8, device="cuda")
+        c = _run("t," + ",".join(map(str, cfg[:5])) + f",8,{cfg[5]},{S}", a[:M], wp, ws)
+        torch.cuda.synchronize()
+        check_gemm(c, exact[:M], what=f"tile {cfg} S={S} M={M} K={K}")
+
+
+def test_tile_split_needs_workspace():
+    """A sliced tiled override without room for its partials fails instead of running."""
+    torch_or_skip()
+    mx = lib_or_fail()
+    a, wp, _ = _case(4224)
+    os.environ["MX_GEMM_CONFIG"] = "t,1,4,4,4,1,8,2,3"
+    try:
+        with pytest.raises(mx.MxError):
+            mx.mx_a4w4_gemm(dev_bf16(a[:64]), wp, N_TEST, workspace=False)
+    finally:
+        del os.environ["MX_GEMM_CONFIG"]
 
 
 @pytest.mark.parametrize("K", K_TESTS)
