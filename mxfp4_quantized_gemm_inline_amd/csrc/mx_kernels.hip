@@ -1361,7 +1361,8 @@ hipError_t run_grouped(const void* a, const int32_t* rt, const int32_t* offs, in
 #define MX_GROUPED_TILE_CONFIGS(X) \
   X(1, 4, 4, 4, 1, 2)              \
   X(2, 4, 4, 4, 1, 1)              \
-  X(1, 4, 4, 4, 2, 2)
+  X(1, 4, 4, 4, 2, 2)              \
+  X(1, 8, 8, 4, 1, 2)
 
 template <int WM, int WN, int MT, int NG, int PF, int OCC>
 hipError_t run_grouped_tile(const void* a, const int32_t* rt, const int32_t* offs, int E, int R_max,
@@ -1411,11 +1412,13 @@ bool resolve_grouped(int E, int R_max, int N, int64_t rows_hint, GroupedConfig& 
   }
   // Tiled (the weight streamed once per 64-row tile) whenever its grid, one CTA per active
   // expert and 256-column tile, can fill the chip; the streaming kernel (more, narrower
-  // CTAs) only for a handful of active experts. Streaming widens to four column groups per
+  // CTAs) only for a handful of active experts. Segments longer than 64 rows take the
+  // 128 x 512 tile, so that one row tile still covers a typical segment and each expert's
+  // weight is streamed once rather than twice. Streaming widens to four column groups per
   // CTA as segments grow, amortizing each CTA's serial segment-lookup -> token ->
   // activation chain over more streamed weight.
   if (G % 16 == 0 && active * (G / 16) >= 512) {
-    g = GroupedConfig{true, 1, 4, 4, 4, 2, 2};
+    g = (rows_hint > 64 && G % 32 == 0) ? GroupedConfig{true, 1, 8, 8, 4, 1, 2} : GroupedConfig{true, 1, 4, 4, 4, 2, 2};
     return true;
   }
   g.tile = false;

@@ -124,7 +124,11 @@ def test_grouped_plan_names_the_selected_kernel(monkeypatch):
     N, K, E = 1536, 3584, 896
     assert mx.mx_a4w4_gemm_grouped_plan(E, 0, 0, N, K) == "none"
     assert mx.mx_a4w4_gemm_grouped_plan(E, 16, 1, N, K).startswith("k_gemm_grouped<1, 1, 4, ")
-    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2>"
+    # segments of about 5 rows (256 tokens): 64 x 256 tiles; about 73 rows (4096 tokens): 128 x 512
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 4096, 256, N, K, 5) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2>"
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K, 73) == "k_gemm_grouped_tile<1, 8, 8, 4, 1, 2>"
+    # N = 768 is no multiple of 512: long segments stay on 64 x 256 tiles
+    assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, 768, K, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2>"
     monkeypatch.setenv("MX_GROUPED_CONFIG", "gs,2,4")
     assert mx.mx_a4w4_gemm_grouped_plan(E, 65536, 4096, N, K).startswith("k_gemm_grouped<2, 4, 4, ")
     monkeypatch.setenv("MX_GROUPED_CONFIG", "gt,1,4,4,4,3,2")

@@ -54,7 +54,7 @@ def test_grouped_matches_oracle(T):
     check_gemm(c[rows], exact, what=f"grouped T={T}")
 
 
-@pytest.mark.parametrize("hint", [1, 20, 64])
+@pytest.mark.parametrize("hint", [1, 20, 64, 100])
 def test_grouped_tiling_hint_only_changes_tiling(hint):
     """The rows-per-expert hint selects the tiling; every choice meets the tolerance."""
     torch = torch_or_skip()
@@ -101,7 +101,8 @@ def test_grouped_malformed_table_is_clamped(hint):
 
 
 GROUPED_CONFIGS = ["gs,1,1", "gs,1,4", "gs,2,1", "gs,2,4",
-                   "gt,1,4,4,4,1,2", "gt,2,4,4,4,1,1", "gt,1,4,4,4,2,2"]
+                   "gt,1,4,4,4,1,2", "gt,2,4,4,4,1,1", "gt,1,4,4,4,2,2",
+                   "gt,1,8,8,4,1,2"]
 
 
 def _ragged_case():
