@@ -130,6 +130,36 @@ def time_point(timer, pt, launches=200):
     return ms * 1e3 / launches  # us per launch
 
 
+def calibrate(torch, mx, timer):
+    """Measured ceilings on this device: a plain streaming read of 1 GiB (4x the Infinity
+    Cache, so it comes from HBM) and an MFMA-only FP4 loop; best of a few launch shapes."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    buf = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+    read = []
+    for per_cu in (2, 4, 8):
+        g = timer.graph([lambda c=cus * per_cu: mx.mx_calib_read(buf, c, sink)] * 10)
+        ms = timer.replay_ms(g, reps=2) / 10
+        del g
+        read.append((buf.numel() / ms / 1e6, per_cu))
+    del buf
+    torch.cuda.empty_cache()
+    mfma = []
+    iters = 2048
+    for per_cu in (2, 4):
+        ctas = cus * per_cu
+        g = timer.graph([lambda c=ctas: mx.mx_calib_mfma(c, iters, sink)] * 5)
+        ms = timer.replay_ms(g, reps=2) / 5
+        del g
+        mfma.append((mx.mx_calib_mfma_flops(ctas, iters) / ms / 1e9, per_cu))
+    best_r, best_m = max(read), max(mfma)
+    return {"hbm_read_GBps": round(best_r[0], 1), "mfma_fp4_TFLOPs": round(best_m[0], 1),
+            "read": "1 GiB streaming read, 16-byte coalesced loads, %d CTAs of 256 threads per CU" % best_r[1],
+            "mfma": "16x16x128 block-scaled FP4 MFMA on registers, 8 chains per wave, %d CTAs of 4 waves "
+                    "per CU" % best_m[1],
+            "cus": cus}
+
+
 def point_record(name, N, K, M, us_cold, us_warm, kernel=None):
     B, F = algo_bytes(M, N, K), algo_flops(M, N, K)
     t_hbm, t_mfma = B / HBM_PEAK * 1e6, F / MFMA_FP4_PEAK * 1e6
@@ -328,6 +358,9 @@ def main():
     torch.cuda.set_device(0)
     mx.lib()  # fail loudly if the HIP library is missing
     timer = Timer(torch)
+    calib = calibrate(torch, mx, timer)
+    log(f"calibration: {calib['hbm_read_GBps']:.0f} GB/s streaming read, "
+        f"{calib['mfma_fp4_TFLOPs']:.0f} TFLOP/s FP4 MFMA")
 
     # ---------------- headline: N=7168 K=768 M sweep, one call per M per step
     N, K, ms, structure = W.DENSE_CONFIGS[HEADLINE]
@@ -384,6 +417,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(Fd / dom["us"] / 1e6, 1), "peak": MFMA_FP4_PEAK / 1e12,
                 "unit": "TFLOP/s", "frac": dom["frac_mfma"], "traffic": traffic}
+    cal_peak = calib["hbm_read_GBps"] if roof["bound"] == "hbm" else calib["mfma_fp4_TFLOPs"]
+    roof["peak_calibrated"] = cal_peak
+    roof["frac_calibrated"] = round(roof["achieved"] / cal_peak, 4)
     roof["kernel"] = f"{dom['kernel']} (N={N} K={K} M={dom['M']})"
     roof["launch_us"] = dom["us"]
     roof["traffic_note"] = ("HBM bytes per launch: rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by "
@@ -416,6 +452,17 @@ def main():
         if not args.no_grouped:
             sweep["grouped"] = grouped_sweep(torch, mx, W, timer)
 
+    # every point's binding fraction against the measured ceilings as well
+    for p in [*head_points, *sweep["dense"], *sweep["grouped"]]:
+        if "us" in p and "N" in p and "K" in p and "M" in p:
+            Bp, Fp = algo_bytes(p["M"], p["N"], p["K"]), algo_flops(p["M"], p["N"], p["K"])
+        elif "bytes" in p and "flops" in p:
+            Bp, Fp = p["bytes"], p["flops"]
+        else:
+            continue
+        p["frac_binding_calibrated"] = round(max(Bp / calib["hbm_read_GBps"] / 1e3,
+                                                 Fp / calib["mfma_fp4_TFLOPs"] / 1e6) / p["us"], 4)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(a_by_m, w_bits, ms)
@@ -443,6 +490,7 @@ def main():
         "baseline_note": f"vs_baseline = value / {page_total:.3f} us, the sum of the pages' direct-kernel "
                          f"medians for this sweep on MI355X (lower is better)",
         "roofline": roof,
+        "calibration": calib,
         "cpu_baseline": cpu,
         "points": head_points,
         "sweep": sweep,
@@ -478,7 +526,7 @@ def grouped_sweep(torch, mx, W, timer):
         B = active * per + 2 * T * K + 2 * R * N
         F = 2 * R * N * K
         recs.append({"workload": "grouped_moe_gemm1_e896_top16_k3584_n1536", "T": T, "rows": R,
-                     "active_experts": active, "us": round(us, 3),
+                     "active_experts": active, "us": round(us, 3), "bytes": B, "flops": F,
                      "tflops": round(F / us / 1e6, 2), "gbps": round(B / us / 1e3, 1),
                      "frac_hbm": round(B / HBM_PEAK * 1e6 / us, 4),
                      "frac_mfma": round(F / MFMA_FP4_PEAK * 1e6 / us, 4)})

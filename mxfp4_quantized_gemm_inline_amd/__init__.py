@@ -30,6 +30,9 @@ SIGNATURES = {
     "mx_a4w4_gemm_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_sz, ctypes.c_char_p, _c_sz]),
     "mx_a4w4_gemm_grouped_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_char_p,
                                            _c_sz]),
+    "mx_calib_read": (_c_int, [_vp, _c_sz, _c_i64, _vp, _vp]),
+    "mx_calib_mfma": (_c_int, [_c_i64, _c_i64, _vp, _vp]),
+    "mx_calib_mfma_flops": (ctypes.c_double, [_c_i64, _c_i64]),
 }
 
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE, MX_ERR_WORKSPACE, MX_ERR_HIP = range(7)
@@ -201,9 +204,34 @@ def mx_a4w4_gemm_grouped_plan(E: int, R_max: int, T: int, N: int, K: int, rows_h
     return buf.value.decode()
 
 
+def mx_calib_read(buf, ctas: int, sink, stream=None) -> None:
+    """One streaming-read launch over the whole of `buf` (a contiguous device tensor whose
+    byte size is a multiple of 16); `sink` is a device tensor of at least 4 bytes."""
+    _dev(buf, None, "buf")
+    _dev(sink, None, "sink")
+    nbytes = buf.numel() * buf.element_size()
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    _check(lib().mx_calib_read(buf.data_ptr(), nbytes, int(ctas), sink.data_ptr(), _stream_ptr(stream)),
+           "mx_calib_read")
+
+
+def mx_calib_mfma(ctas: int, iters: int, sink, stream=None) -> None:
+    """One MFMA-only launch (ctas x 4 waves x iters x 8 FP4 MFMAs)."""
+    _dev(sink, None, "sink")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    _check(lib().mx_calib_mfma(int(ctas), int(iters), sink.data_ptr(), _stream_ptr(stream)), "mx_calib_mfma")
+
+
+def mx_calib_mfma_flops(ctas: int, iters: int) -> float:
+    return float(lib().mx_calib_mfma_flops(int(ctas), int(iters)))
+
+
 __all__ = [
     "LIB_PATH", "MxError", "lib", "status_string", "mx_prepared_layout_version",
     "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
     "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
-    "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan",
+    "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_calib_read", "mx_calib_mfma",
+    "mx_calib_mfma_flops",
 ]

@@ -1,7 +1,8 @@
-"""The C ABI boundary on the host: the library loads, exports every function that
-include/mx.h declares, sizes its buffers as documented, and rejects bad arguments
+"""The C ABI boundary on the host: the library loads, exports every function that the
+headers under include/ declare, sizes its buffers as documented, and rejects bad arguments
 synchronously (before any HIP call, so these run without a GPU)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,7 +11,7 @@ import pytest
 import mxfp4_quantized_gemm_inline_amd as mx
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mx.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(mx.LIB_PATH), reason="libmxgemm.so not built")
 
@@ -21,14 +22,17 @@ MIS = 0x10008  # 8-byte aligned only
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
+    assert [os.path.basename(h) for h in HEADERS] == ["mx.h", "mx_calib.h"]
     names = declared_functions()
-    assert len(names) >= 9
+    assert len(names) >= 12 and "mx_calib_mfma" in names
     lib = mx.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -147,3 +151,21 @@ def test_plan_argument_errors():
     assert g(4, 16, 1, 256, 256, 1, None, 64) == mx.MX_ERR_NULL
     tiny = ctypes.create_string_buffer(8)  # truncated, still NUL-terminated
     assert f(2048, 7168, 768, 0, tiny, 8) == mx.MX_OK and tiny.value == b"k_gemm_"
+
+
+def test_calibration_argument_errors():
+    L = mx.lib()
+    sink = 0x40000
+    assert L.mx_calib_read(None, 1024, 8, sink, None) == mx.MX_ERR_NULL
+    assert L.mx_calib_read(A, 1024, 8, None, None) == mx.MX_ERR_NULL
+    assert L.mx_calib_read(A, 0, 8, sink, None) == mx.MX_ERR_SHAPE
+    assert L.mx_calib_read(A, 1000, 8, sink, None) == mx.MX_ERR_SHAPE      # not a multiple of 16
+    assert L.mx_calib_read(A, 1024, 0, sink, None) == mx.MX_ERR_SHAPE
+    assert L.mx_calib_read(A, 1024, (1 << 20) + 1, sink, None) == mx.MX_ERR_SHAPE
+    assert L.mx_calib_read(MIS, 1024, 8, sink, None) == mx.MX_ERR_ALIGN
+    assert L.mx_calib_mfma(8, 16, None, None) == mx.MX_ERR_NULL
+    assert L.mx_calib_mfma(0, 16, sink, None) == mx.MX_ERR_SHAPE
+    assert L.mx_calib_mfma(8, 0, sink, None) == mx.MX_ERR_SHAPE
+    assert L.mx_calib_mfma(8, (1 << 24) + 1, sink, None) == mx.MX_ERR_SHAPE
+    # 256 CTAs x 4 waves x 100 rounds x 8 MFMAs x 65,536 flop
+    assert mx.mx_calib_mfma_flops(256, 100) == 256 * 4 * 100 * 8 * 65536
