@@ -75,6 +75,21 @@ mx_status mx_prepare_weight(const void* w_bf16, int64_t N, int64_t K, void* w_pr
                             hipStream_t stream);
 
 /*
+ * Weight preparation from an already-quantized weight: the caller's packed E2M1 codes and
+ * E8M0 scales are preshuffled once, as they are ("[gfx950][FlyDSL] Add direct dense A4W4
+ * MXFP4 GEMM", Scope: packed E2M1 weights and E8M0 scales, preshuffled once).
+ * w_fp4: [N, K/2] bytes, row n holding W[n, 2i] in the low nibble and W[n, 2i+1] in the
+ * high nibble of byte i. w_scale: [N, K/32] bytes, the E8M0 scale of each 32-block along
+ * K (value 2^(byte - 127)). Both read only. w_prep: mx_prepared_weight_bytes(N, K) bytes,
+ * written completely. Every byte is copied as given; a scale byte of 255 (NaN in the OCP
+ * MX encoding) is outside the contract. For a weight quantized by the rule above, the
+ * result is identical to mx_prepare_weight's, and mx_unprepare_weight returns the inputs
+ * unchanged. Same shape rules and errors as mx_prepare_weight.
+ */
+mx_status mx_prepare_weight_packed(const void* w_fp4, const void* w_scale, int64_t N, int64_t K,
+                                   void* w_prep, hipStream_t stream);
+
+/*
  * Test support: the inverse of the preshuffle. Writes the canonical MXFP4 form of a
  * prepared weight: w_fp4 [N, K/2] (element at even k in the low nibble) and
  * w_scale [N, K/32] (one E8M0 byte per 32-block). Same shape rules and errors as

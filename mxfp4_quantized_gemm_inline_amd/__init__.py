@@ -21,6 +21,7 @@ SIGNATURES = {
     "mx_prepared_layout_version": (_c_int, []),
     "mx_prepared_weight_bytes": (_c_sz, [_c_i64, _c_i64]),
     "mx_prepare_weight": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp]),
+    "mx_prepare_weight_packed": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _vp]),
     "mx_unprepare_weight": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "mx_quant_act": (_c_int, [_vp, _c_i64, _c_i64, _vp, _vp, _vp]),
     "mx_a4w4_gemm_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64]),
@@ -119,6 +120,26 @@ def mx_prepare_weight(w_bf16, out=None, stream=None):
     _check(lib().mx_prepare_weight(_dev(w_bf16, torch.bfloat16, "w_bf16"), N, K,
                                    _dev(out, torch.uint8, "w_prep"), _stream_ptr(stream)),
            "mx_prepare_weight")
+    return out
+
+
+def mx_prepare_weight_packed(w_fp4, w_scale, out=None, stream=None):
+    """Caller-quantized weight -> prepared blob: w_fp4 uint8 [N, K/2] (low nibble = even k),
+    w_scale uint8 [N, K/32] (E8M0)."""
+    torch = _torch()
+    if w_fp4.dim() != 2 or w_scale.dim() != 2:
+        raise ValueError("w_fp4 and w_scale must be 2-D")
+    N, K = w_fp4.shape[0], 2 * w_fp4.shape[1]
+    if tuple(w_scale.shape) != (N, K // 32):
+        raise ValueError(f"w_scale must be [{N}, {K // 32}], got {tuple(w_scale.shape)}")
+    nbytes = mx_prepared_weight_bytes(N, K)
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w_fp4.device)
+    elif out.numel() * out.element_size() < nbytes:
+        raise ValueError("out is too small")
+    _check(lib().mx_prepare_weight_packed(_dev(w_fp4, torch.uint8, "w_fp4"), _dev(w_scale, torch.uint8, "w_scale"),
+                                          N, K, _dev(out, torch.uint8, "w_prep"), _stream_ptr(stream)),
+           "mx_prepare_weight_packed")
     return out
 
 
@@ -231,7 +252,7 @@ def mx_calib_mfma_flops(ctas: int, iters: int) -> float:
 __all__ = [
     "LIB_PATH", "MxError", "lib", "status_string", "mx_prepared_layout_version",
     "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
-    "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
+    "mx_prepare_weight_packed", "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
     "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_calib_read", "mx_calib_mfma",
     "mx_calib_mfma_flops",
 ]

@@ -72,6 +72,16 @@ mx_status mx_prepare_weight(const void* w_bf16, int64_t N, int64_t K, void* w_pr
   return from_hip(mx::launch_prepare(w_bf16, N, K, w_prep, stream));
 }
 
+mx_status mx_prepare_weight_packed(const void* w_fp4, const void* w_scale, int64_t N, int64_t K, void* w_prep,
+                                   hipStream_t stream) {
+  if (!w_fp4 || !w_scale || !w_prep) return MX_ERR_NULL;
+  if (!gemm_shape_ok(N, K)) return MX_ERR_SHAPE;
+  if (!aligned16(w_fp4) || !aligned16(w_scale) || !aligned16(w_prep)) return MX_ERR_ALIGN;
+  mx_status d = check_device();
+  if (d != MX_OK) return d;
+  return from_hip(mx::launch_prepare_packed(w_fp4, w_scale, N, K, w_prep, stream));
+}
+
 mx_status mx_unprepare_weight(const void* w_prep, int64_t N, int64_t K, void* w_fp4, void* w_scale,
                               hipStream_t stream) {
   if (!w_prep || !w_fp4 || !w_scale) return MX_ERR_NULL;

@@ -9,6 +9,7 @@ namespace mx {
 
 hipError_t launch_quant_act(const void* a, int64_t M, int64_t K, void* q, void* s, hipStream_t st);
 hipError_t launch_prepare(const void* w, int64_t N, int64_t K, void* wp, hipStream_t st);
+hipError_t launch_prepare_packed(const void* q, const void* s, int64_t N, int64_t K, void* wp, hipStream_t st);
 hipError_t launch_unprepare(const void* wp, int64_t N, int64_t K, void* q, void* s, hipStream_t st);
 hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K,
                        void* workspace, size_t workspace_bytes, hipStream_t st);

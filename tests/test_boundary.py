@@ -84,6 +84,17 @@ def test_quant_and_prepare_argument_errors():
     u = mx.lib().mx_unprepare_weight
     assert u(A, 256, 128 + 64, B, Cp, None) == mx.MX_ERR_SHAPE
     assert u(A, 256, 256, None, Cp, None) == mx.MX_ERR_NULL
+    pk = mx.lib().mx_prepare_weight_packed
+    #         fp4 scale N    K    prep stream
+    assert pk(None, B, 256, 256, Cp, None) == mx.MX_ERR_NULL
+    assert pk(A, None, 256, 256, Cp, None) == mx.MX_ERR_NULL
+    assert pk(A, B, 256, 256, None, None) == mx.MX_ERR_NULL
+    assert pk(A, B, 512 + 64, 256, Cp, None) == mx.MX_ERR_SHAPE
+    assert pk(A, B, 256, 128 + 32, Cp, None) == mx.MX_ERR_SHAPE
+    assert pk(A, B, 256, 0, Cp, None) == mx.MX_ERR_SHAPE
+    assert pk(MIS, B, 256, 256, Cp, None) == mx.MX_ERR_ALIGN
+    assert pk(A, MIS, 256, 256, Cp, None) == mx.MX_ERR_ALIGN
+    assert pk(A, B, 256, 256, MIS, None) == mx.MX_ERR_ALIGN
 
 
 def test_grouped_argument_errors():
