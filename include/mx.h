@@ -148,6 +148,31 @@ mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token,
                                const void* w_prep_stacked, void* c_bf16, int64_t T, int64_t N,
                                int64_t K, int64_t rows_hint, hipStream_t stream);
 
+/* Activation of the fused GEMM1 epilogue. */
+enum { MX_ACT_SILU = 0, MX_ACT_SWIGLU = 1 };
+
+/*
+ * Grouped MoE GEMM1 with the activation and the MXFP4 quantization for the second GEMM
+ * fused into its epilogue ("[gfx1250] Fuse A4W4 stage1 FP4 quantization", Summary: the
+ * GEMM1 epilogue emits packed MXFP4 payloads and E8M0 scales directly after SiLU or
+ * SwiGLU, the scale computed from the FP32 activation value). Routing, segments and
+ * weights are those of mx_a4w4_gemm_grouped; for output row r with GEMM1 row c (FP32):
+ *   act == MX_ACT_SWIGLU: h[j] = SiLU(c[j]) * c[N/2 + j], j < Nh = N/2 (gate columns first);
+ *   act == MX_ACT_SILU:   h[j] = SiLU(c[j]), j < Nh = N;  SiLU(x) = x / (1 + exp(-x)).
+ * h is quantized along its columns with the rule at the top of this file applied to the
+ * FP32 value of h (E8M0 scale from the FP32 block amax, one conversion to E2M1) and written
+ * in canonical form: h_fp4 [R_max, Nh/2] bytes (element at even j in the low nibble),
+ * h_scale [R_max, Nh/32] bytes; rows >= R are untouched. Because h is formed in FP32 from
+ * FP32 accumulators, a code or scale whose exact value lies at a rounding boundary may
+ * differ from the exact product's by one step. Requirements and errors as for
+ * mx_a4w4_gemm_grouped, plus act in {MX_ACT_SILU, MX_ACT_SWIGLU} (else MX_ERR_SHAPE).
+ */
+mx_status mx_a4w4_gemm_grouped_act_quant(const void* a_bf16, const int32_t* row_token,
+                                         const int32_t* expert_offsets, int64_t E, int64_t R_max,
+                                         const void* w_prep_stacked, int64_t T, int64_t N, int64_t K,
+                                         int32_t act, int64_t rows_hint, void* h_fp4, void* h_scale,
+                                         hipStream_t stream);
+
 /*
  * Introspection (host only, no GPU needed): the kernel instantiation(s) mx_a4w4_gemm
  * would launch for (M, N, K) with a workspace of workspace_bytes, e.g.
@@ -168,6 +193,14 @@ mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_by
  */
 mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t T, int64_t N, int64_t K,
                                     int64_t rows_hint, char* buf, size_t buf_len);
+
+/*
+ * The same for mx_a4w4_gemm_grouped_act_quant (its kernel depends on N, act and the hint;
+ * tuning override MX_GROUPED_CONFIG="gt,..."). Errors: MX_ERR_SHAPE (shape or act),
+ * MX_ERR_NULL (buf), MX_ERR_HIP (the override names no fused configuration for N).
+ */
+mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t N, int64_t K, int32_t act, int64_t rows_hint,
+                                              char* buf, size_t buf_len);
 
 #ifdef __cplusplus
 }

@@ -31,12 +31,17 @@ SIGNATURES = {
     "mx_a4w4_gemm_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_sz, ctypes.c_char_p, _c_sz]),
     "mx_a4w4_gemm_grouped_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_char_p,
                                            _c_sz]),
+    "mx_a4w4_gemm_grouped_act_quant": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _c_i64,
+                                                ctypes.c_int32, _c_i64, _vp, _vp, _vp]),
+    "mx_a4w4_gemm_grouped_act_quant_plan": (_c_int, [_c_i64, _c_i64, ctypes.c_int32, _c_i64, ctypes.c_char_p,
+                                                     _c_sz]),
     "mx_calib_read": (_c_int, [_vp, _c_sz, _c_i64, _vp, _vp]),
     "mx_calib_mfma": (_c_int, [_c_i64, _c_i64, _vp, _vp]),
     "mx_calib_mfma_flops": (ctypes.c_double, [_c_i64, _c_i64]),
 }
 
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE, MX_ERR_WORKSPACE, MX_ERR_HIP = range(7)
+MX_ACT_SILU, MX_ACT_SWIGLU = 0, 1
 
 _lib = None
 
@@ -206,6 +211,38 @@ def mx_a4w4_gemm_grouped(a_bf16, row_token, expert_offsets, E: int, R_max: int, 
     return c
 
 
+def mx_a4w4_gemm_grouped_act_quant(a_bf16, row_token, expert_offsets, E: int, R_max: int, w_prep_stacked,
+                                   N: int, act: int = MX_ACT_SWIGLU, rows_hint: int = 1, h_fp4=None, h_scale=None,
+                                   stream=None):
+    """Grouped GEMM1 with fused SiLU / SwiGLU + MXFP4 quantization: returns (h_fp4 uint8
+    [R_max, Nh/2], h_scale uint8 [R_max, Nh/32]) with Nh = N/2 (SwiGLU) or N (SiLU)."""
+    torch = _torch()
+    T, K = a_bf16.shape
+    Nh = N // 2 if act == MX_ACT_SWIGLU else N
+    if h_fp4 is None:
+        h_fp4 = torch.empty((R_max, Nh // 2), dtype=torch.uint8, device=a_bf16.device)
+    if h_scale is None:
+        h_scale = torch.empty((R_max, Nh // 32), dtype=torch.uint8, device=a_bf16.device)
+    if h_fp4.numel() < R_max * (Nh // 2) or h_scale.numel() < R_max * (Nh // 32):
+        raise ValueError("h_fp4 / h_scale are too small")
+    _check(lib().mx_a4w4_gemm_grouped_act_quant(
+        _dev(a_bf16, torch.bfloat16, "a_bf16") if T > 0 else None,
+        _dev(row_token, torch.int32, "row_token") if R_max > 0 else None,
+        _dev(expert_offsets, torch.int32, "expert_offsets"), int(E), int(R_max),
+        _dev(w_prep_stacked, torch.uint8, "w_prep_stacked"), T, int(N), K, int(act), int(rows_hint),
+        _dev(h_fp4, torch.uint8, "h_fp4") if R_max > 0 else None,
+        _dev(h_scale, torch.uint8, "h_scale") if R_max > 0 else None, _stream_ptr(stream)),
+        "mx_a4w4_gemm_grouped_act_quant")
+    return h_fp4, h_scale
+
+
+def mx_a4w4_gemm_grouped_act_quant_plan(N: int, K: int, act: int = MX_ACT_SWIGLU, rows_hint: int = 1) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().mx_a4w4_gemm_grouped_act_quant_plan(int(N), int(K), int(act), int(rows_hint), buf, len(buf)),
+           "mx_a4w4_gemm_grouped_act_quant_plan")
+    return buf.value.decode()
+
+
 def mx_a4w4_gemm_plan(M: int, N: int, K: int, workspace_bytes=None) -> str:
     """Kernel(s) mx_a4w4_gemm launches for this shape; workspace_bytes defaults to what
     mx_a4w4_gemm allocates when given no workspace."""
@@ -253,6 +290,7 @@ __all__ = [
     "LIB_PATH", "MxError", "lib", "status_string", "mx_prepared_layout_version",
     "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
     "mx_prepare_weight_packed", "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
-    "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_calib_read", "mx_calib_mfma",
+    "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_a4w4_gemm_grouped_act_quant",
+    "mx_a4w4_gemm_grouped_act_quant_plan", "MX_ACT_SILU", "MX_ACT_SWIGLU", "mx_calib_read", "mx_calib_mfma",
     "mx_calib_mfma_flops",
 ]

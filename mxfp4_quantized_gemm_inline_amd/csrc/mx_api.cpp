@@ -139,6 +139,38 @@ mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token, con
                                           c_bf16, T, N, K, rows_hint < 1 ? 1 : rows_hint, stream));
 }
 
+mx_status mx_a4w4_gemm_grouped_act_quant(const void* a_bf16, const int32_t* row_token,
+                                         const int32_t* expert_offsets, int64_t E, int64_t R_max,
+                                         const void* w_prep_stacked, int64_t T, int64_t N, int64_t K, int32_t act,
+                                         int64_t rows_hint, void* h_fp4, void* h_scale, hipStream_t stream) {
+  if (E < 1 || T < 0 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1 ||
+      T > (1ll << 31) - 1 || (act != MX_ACT_SILU && act != MX_ACT_SWIGLU))
+    return MX_ERR_SHAPE;
+  if (!expert_offsets || !w_prep_stacked) return MX_ERR_NULL;
+  if (R_max > 0 && (!row_token || !h_fp4 || !h_scale)) return MX_ERR_NULL;
+  if (T > 0 && !a_bf16) return MX_ERR_NULL;
+  if ((a_bf16 && !aligned16(a_bf16)) || !aligned16(w_prep_stacked) || (h_fp4 && !aligned16(h_fp4)) ||
+      (h_scale && !aligned16(h_scale)) || (reinterpret_cast<uintptr_t>(expert_offsets) & 3u) ||
+      (reinterpret_cast<uintptr_t>(row_token) & 3u))
+    return MX_ERR_ALIGN;
+  if (R_max == 0) return MX_OK;
+  mx_status d = check_device();
+  if (d != MX_OK) return d;
+  return from_hip(mx::launch_gemm_grouped_act(a_bf16, row_token, expert_offsets, E, R_max, w_prep_stacked, h_fp4,
+                                              h_scale, T, N, K, act, rows_hint < 1 ? 1 : rows_hint, stream));
+}
+
+mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t N, int64_t K, int32_t act, int64_t rows_hint, char* buf,
+                                              size_t buf_len) {
+  if (!gemm_shape_ok(N, K) || (act != MX_ACT_SILU && act != MX_ACT_SWIGLU)) return MX_ERR_SHAPE;
+  if (!buf || buf_len == 0) return MX_ERR_NULL;
+  if (!mx::grouped_act_plan(N, act, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
+    buf[0] = '\0';
+    return MX_ERR_HIP;
+  }
+  return MX_OK;
+}
+
 mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_bytes, char* buf, size_t buf_len) {
   if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;

@@ -17,6 +17,11 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const int32_t* offsets,
                                int64_t E, int64_t R_max, const void* wp, void* c, int64_t T,
                                int64_t N, int64_t K, int64_t rows_hint, hipStream_t st);
+// act: 0 = SiLU, 1 = SwiGLU (gate columns first). Outputs hq [R_max, Nh/2], hs [R_max, Nh/32].
+hipError_t launch_gemm_grouped_act(const void* a, const int32_t* row_token, const int32_t* offsets, int64_t E,
+                                   int64_t R_max, const void* wp, void* hq, void* hs, int64_t T, int64_t N,
+                                   int64_t K, int act, int64_t rows_hint, hipStream_t st);
+bool grouped_act_plan(int64_t N, int act, int64_t rows_hint, char* buf, size_t len);
 // Name the kernel(s) the launchers above would run (false: the tuning override is invalid).
 bool gemm_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes, char* buf, size_t len);
 bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t T, int64_t rows_hint, char* buf,

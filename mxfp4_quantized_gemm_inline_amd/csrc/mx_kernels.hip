@@ -375,14 +375,31 @@ struct TileRowsGather {
   static constexpr bool kGather = true;
 };
 
+// Fused GEMM1 epilogue ("[gfx1250] Fuse A4W4 stage1 FP4 quantization", Summary): the
+// activation h = SiLU(c), or SiLU(gate) * up with the gate columns in the first half of the
+// GEMM1 output and the up columns in the second, formed in FP32 from the accumulators and
+// quantized to MXFP4 along its columns (32-blocks, E8M0 scale from the FP32 block amax),
+// written as canonical payload [rows, Nh/2] and scales [rows, Nh/32].
+constexpr int kActSilu = 0, kActSwiglu = 1;
+struct ActOut {
+  uint8_t* q = nullptr;  // packed E2M1 of the tile's first row
+  uint8_t* s = nullptr;  // E8M0 scales of the tile's first row
+  int Nh = 0;            // columns of h
+};
+
 // The tiled main loop and epilogue for one BM x BN output tile: Mrows (1..BM) valid rows
 // from `rows`, weight column tile bn of the prepared weight Wp, output rows written at
 // Cout + r * N for r < Mrows (columns past N masked). Only K steps [tb, te) are summed; with
 // Pout the FP32 sums go to Pout + r * N (one K slice's partial tile) instead of bf16 to Cout.
-template <int WM, int WN, int MT, int NG, int PF, class Rows>
+// With ACT >= 0 the tile's output is the fused activation + quantization into `ao` instead:
+// for SwiGLU the first WN/2 waves compute gate columns and the others the matching up
+// columns, so the CTA's BN weight columns yield BN/2 columns of h (h tile bn); for SiLU the
+// column mapping is the plain one and h tile bn is output tile bn.
+template <int WM, int WN, int MT, int NG, int PF, int ACT = -1, class Rows>
 __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uint8_t* __restrict__ Wp,
                                           uint16_t* __restrict__ Cout, float* __restrict__ Pout, int N,
-                                          int K, int bn, int tb, int te, uint8_t* __restrict__ smem) {
+                                          int K, int bn, int tb, int te, uint8_t* __restrict__ smem,
+                                          const ActOut& ao = ActOut{}) {
   using S = TileShape<WM, WN, MT, NG>;
   constexpr int MTC = S::MTC, BM = S::BM, BN = S::BN, NW = S::NW, BPT = S::BPT;
   constexpr int SQ = S::SQ, SS = S::SS, CROW = S::CROW;
@@ -393,7 +410,10 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / WN, wn = w % WN;
-  const int gw0 = bn * (BN / 16) + wn * NG;
+  static_assert(ACT < 0 || WN % 2 == 0, "the fused epilogue pairs the two halves of the waves");
+  const int gw0 = ACT == kActSwiglu
+                      ? (wn < WN / 2 ? bn * (BN / 32) + wn * NG : G / 2 + bn * (BN / 32) + (wn - WN / 2) * NG)
+                      : bn * (BN / 16) + wn * NG;
   const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
 
   // Loads are branch-free so the compiler can count them: tile rows past Mrows re-read the
@@ -524,6 +544,91 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
     if (t + I < te) step(t + I, std::integral_constant<int, I % PF>{}, std::integral_constant<int, I % (PF + 1)>{});
   });
 
+  if constexpr (ACT >= 0) {
+    // Stage FP32 values in LDS as [BM][HC + 4] (16-byte row pad), half of the tile's
+    // columns at a time (the same bytes as the bf16 output staging), then each thread
+    // quantizes one 32-column block of one row.
+    constexpr int HC = BN / 2, HROW = HC + 4, NB = HC / 32;
+    static_assert(BM * HROW * 4 <= S::SMEM, "the staged half tile fits the LDS");
+    float* hb = reinterpret_cast<float*>(smem);
+    const int half = wn / (WN / 2), cw = (wn % (WN / 2)) * NG;
+    auto at = [&](int g, int mt) {
+      return hb + (16 * (wm * MT + mt) + (lane & 15)) * HROW + 16 * (cw + g) + 4 * (lane >> 4);
+    };
+    auto silu = [](float x) { return x / (1.0f + expf(-x)); };
+    auto quantize = [&](int col0) {  // h columns [col0, col0 + HC) of this tile's rows
+      for (int id = threadIdx.x; id < BM * NB; id += 64 * NW) {
+        const int r = id / NB, b = id % NB;
+        if (r >= Mrows) continue;
+        const float* p = hb + r * HROW + 32 * b;
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const v4f x = *reinterpret_cast<const v4f*>(p + 4 * i);
+          v[4 * i] = x[0]; v[4 * i + 1] = x[1]; v[4 * i + 2] = x[2]; v[4 * i + 3] = x[3];
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const uint32_t ex = (__builtin_bit_cast(uint32_t, amax) >> 23) & 0xffu;
+        const uint32_t sb = ex > 2u ? ex - 2u : 0u;  // e = floor(log2 amax) - 2, clamped at -127
+        const float sc = __builtin_bit_cast(float, sb ? (sb << 23) : 0x00400000u);
+        uint32_t q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t w4 = 0;
+          w4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w4, v[8 * j + 0], v[8 * j + 1], sc, 0);
+          w4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w4, v[8 * j + 2], v[8 * j + 3], sc, 1);
+          w4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w4, v[8 * j + 4], v[8 * j + 5], sc, 2);
+          w4 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w4, v[8 * j + 6], v[8 * j + 7], sc, 3);
+          q[j] = w4;
+        }
+        *reinterpret_cast<uint4*>(ao.q + (size_t)r * (ao.Nh / 2) + (col0 + 32 * b) / 2) = make_uint4(q[0], q[1], q[2], q[3]);
+        ao.s[(size_t)r * (ao.Nh / 32) + col0 / 32 + b] = (uint8_t)sb;
+      }
+    };
+    __syncthreads();  // every wave has finished reading the operand buffers
+    if constexpr (ACT == kActSwiglu) {
+      if (half == 1)  // up columns
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<v4f*>(at(g, mt)) = acc[g][mt];
+      __syncthreads();
+      if (half == 0)  // gate columns: h = SiLU(gate) * up, in place
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            float* p = at(g, mt);
+            const v4f u = *reinterpret_cast<const v4f*>(p);
+            v4f h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = silu(acc[g][mt][j]) * u[j];
+            *reinterpret_cast<v4f*>(p) = h;
+          }
+      __syncthreads();
+      quantize(bn * HC);
+    } else {
+      for (int ph = 0; ph < 2; ++ph) {
+        if (half == ph)
+#pragma unroll
+          for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              v4f h;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) h[j] = silu(acc[g][mt][j]);
+              *reinterpret_cast<v4f*>(at(g, mt)) = h;
+            }
+        __syncthreads();
+        quantize(bn * BN + ph * HC);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+
   if (Pout) {  // a K slice: FP32 partial sums, 16 bytes per lane (four columns of one row)
 #pragma unroll
     for (int g = 0; g < NG; ++g)
@@ -591,11 +696,14 @@ void k_gemm_tile(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp,
 // CTA ranks the experts' unit counts with a block scan to find its unit, and the surplus
 // CTAs exit. One expert's units are consecutive and dealt to one XCD (as in tile_coords),
 // so its column tiles share the gathered rows and its row tiles the weight in that L2.
-template <int WM, int WN, int MT, int NG, int PF, int OCC>
+// With ACT >= 0 the output is the fused activation + MXFP4 quantization (tile_core) into
+// Hq [R_max, Nh/2] and Hs [R_max, Nh/32] instead of C.
+template <int WM, int WN, int MT, int NG, int PF, int OCC, int ACT = -1>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
 void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
                          const int32_t* __restrict__ offs, int E, int R_max, const uint8_t* __restrict__ Wall,
-                         uint16_t* __restrict__ C, int Ttok, int N, int K) {
+                         uint16_t* __restrict__ C, int Ttok, int N, int K, uint8_t* __restrict__ Hq,
+                         uint8_t* __restrict__ Hs, int Nh) {
   using S = TileShape<WM, WN, MT, NG>;
   constexpr int NTH = S::NTH, BM = S::BM, BN = S::BN;
   __shared__ __align__(16) uint8_t smem[S::SMEM];
@@ -646,9 +754,20 @@ void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restri
   const int tiles_e = (cnt + BM - 1) / BM;
   const int rem = L - __builtin_amdgcn_readfirstlane(s_unit[3]), bn = rem / tiles_e, mt = rem % tiles_e;
   const int r0 = lo + mt * BM, Mrows = min(BM, cnt - mt * BM);
-  uint16_t* Cout = C + (size_t)r0 * N;
+  uint16_t* Cout = ACT >= 0 ? nullptr : C + (size_t)r0 * N;
+  ActOut ao;
+  if constexpr (ACT >= 0) ao = ActOut{Hq + (size_t)r0 * (Nh / 2), Hs + (size_t)r0 * (Nh / 32), Nh};
 
   if (Ttok <= 0) {  // no activations at all: every row is Q(0) W^T = 0
+    if constexpr (ACT >= 0) {  // and h = 0: zero codes, zero scales
+      const int hc = ACT == kActSwiglu ? BN / 2 : BN, c0 = bn * hc;
+      for (int i = tid; i < Mrows * (hc / 32); i += NTH) {
+        const int r = i / (hc / 32), b = i % (hc / 32);
+        *reinterpret_cast<uint4*>(ao.q + (size_t)r * (Nh / 2) + (c0 + 32 * b) / 2) = make_uint4(0u, 0u, 0u, 0u);
+        ao.s[(size_t)r * (Nh / 32) + c0 / 32 + b] = 0;
+      }
+      return;
+    }
     const int n0 = bn * BN, ncol = min(BN, N - n0);
     for (int i = tid; i < Mrows * (ncol / 8); i += NTH) {
       const int r = i / (ncol / 8), ch = i % (ncol / 8);
@@ -657,8 +776,8 @@ void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restri
     return;
   }
   const TileRowsGather rows{reinterpret_cast<const uint8_t*>(A), row_token + r0, Ttok, K};
-  tile_core<WM, WN, MT, NG, PF>(rows, Mrows, Wall + (size_t)e * prepared_bytes(N, K), Cout, nullptr, N, K, bn, 0,
-                                steps_of(K), smem);
+  tile_core<WM, WN, MT, NG, PF, ACT>(rows, Mrows, Wall + (size_t)e * prepared_bytes(N, K), Cout, nullptr, N, K, bn,
+                                     0, steps_of(K), smem, ao);
 }
 
 // ====================================================================== wide-tile GEMM (large M)
@@ -1374,7 +1493,22 @@ hipError_t run_grouped_tile(const void* a, const int32_t* rt, const int32_t* off
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_gemm_grouped_tile<WM, WN, MT, NG, PF, OCC>), dim3((unsigned)grid), dim3(S::NTH), 0, st,
                      static_cast<const uint16_t*>(a), rt, offs, E, R_max, static_cast<const uint8_t*>(wp),
-                     static_cast<uint16_t*>(c), T, N, K);
+                     static_cast<uint16_t*>(c), T, N, K, nullptr, nullptr, 0);
+  return hipGetLastError();
+}
+
+template <int WM, int WN, int MT, int NG, int PF, int OCC, int ACT>
+hipError_t run_grouped_tile_act(const void* a, const int32_t* rt, const int32_t* offs, int E, int R_max,
+                                const void* wp, void* hq, void* hs, int T, int N, int K, hipStream_t st) {
+  using S = TileShape<WM, WN, MT, NG>;
+  const int64_t active = E < R_max ? E : R_max;
+  const int64_t grid = (active + R_max / S::BM) * (N / S::BN);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const int Nh = ACT == kActSwiglu ? N / 2 : N;
+  hipLaunchKernelGGL((k_gemm_grouped_tile<WM, WN, MT, NG, PF, OCC, ACT>), dim3((unsigned)grid), dim3(S::NTH), 0, st,
+                     static_cast<const uint16_t*>(a), rt, offs, E, R_max, static_cast<const uint8_t*>(wp), nullptr, T,
+                     N, K, static_cast<uint8_t*>(hq), static_cast<uint8_t*>(hs), Nh);
   return hipGetLastError();
 }
 
@@ -1448,6 +1582,62 @@ hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const in
   if (g.MT == 2 && g.NG == 1) return run_grouped<2, 1, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
   if (g.MT == 2 && g.NG == 4) return run_grouped<2, 4, 4>(a, row_token, offsets, e, r, wp, c, t, n, k, st);
   return hipErrorInvalidValue;
+}
+
+namespace {
+
+// Fused activation + quantization variants of the tiled grouped kernel (WM, WN, MT, NG, PF, OCC).
+#define MX_GROUPED_ACT_CONFIGS(X) \
+  X(1, 4, 4, 4, 2, 2)             \
+  X(1, 8, 8, 4, 1, 2)
+
+// The fused call always runs the tiled grouped kernel (its epilogue needs a whole row tile
+// of gate and up columns in one CTA): 128 x 512 tiles for segments longer than 64 rows when
+// N is a multiple of 512, 64 x 256 otherwise; MX_GROUPED_CONFIG="gt,..." may force another
+// fused-capable configuration (tuning only).
+bool resolve_grouped_act(int N, int64_t rows_hint, GroupedConfig& g) {
+  const char* s = std::getenv("MX_GROUPED_CONFIG");
+  if (s && *s) {
+    int v[6] = {0, 0, 0, 0, 0, 0};
+    if (std::sscanf(s, "gt,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5]) != 6) return false;
+    g = GroupedConfig{true, v[0], v[1], v[2], v[3], v[4], v[5]};
+  } else {
+    g = (rows_hint > 64 && N % 512 == 0) ? GroupedConfig{true, 1, 8, 8, 4, 1, 2} : GroupedConfig{true, 1, 4, 4, 4, 2, 2};
+  }
+  const int BN = 16 * g.NG * g.WN;
+#define X(wm, wn, mt, ng, pf, occ) \
+  if (g.WM == wm && g.WN == wn && g.MT == mt && g.NG == ng && g.PF == pf && g.OCC == occ) return N % BN == 0;
+  MX_GROUPED_ACT_CONFIGS(X)
+#undef X
+  return false;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_grouped_act(const void* a, const int32_t* row_token, const int32_t* offsets, int64_t E,
+                                   int64_t R_max, const void* wp, void* hq, void* hs, int64_t T, int64_t N,
+                                   int64_t K, int act, int64_t rows_hint, hipStream_t st) {
+  const int e = (int)E, r = (int)R_max, t = (int)T, n = (int)N, k = (int)K;
+  GroupedConfig g;
+  if (!resolve_grouped_act(n, rows_hint, g)) return hipErrorInvalidValue;
+#define X(wm, wn, mt, ng, pf, occ)                                                                        \
+  if (g.WM == wm && g.WN == wn && g.MT == mt && g.NG == ng && g.PF == pf && g.OCC == occ)                \
+    return act == kActSwiglu                                                                              \
+               ? run_grouped_tile_act<wm, wn, mt, ng, pf, occ, kActSwiglu>(a, row_token, offsets, e, r, wp, hq, \
+                                                                            hs, t, n, k, st)                   \
+               : run_grouped_tile_act<wm, wn, mt, ng, pf, occ, kActSilu>(a, row_token, offsets, e, r, wp, hq, hs, \
+                                                                          t, n, k, st);
+  MX_GROUPED_ACT_CONFIGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+bool grouped_act_plan(int64_t N, int act, int64_t rows_hint, char* buf, size_t len) {
+  GroupedConfig g;
+  if (!resolve_grouped_act((int)N, rows_hint, g)) return false;
+  std::snprintf(buf, len, "k_gemm_grouped_tile<%d, %d, %d, %d, %d, %d, %s>", g.WM, g.WN, g.MT, g.NG, g.PF, g.OCC,
+                act == kActSwiglu ? "swiglu" : "silu");
+  return true;
 }
 
 bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t /*T*/, int64_t rows_hint, char* buf,

@@ -180,3 +180,27 @@ def test_calibration_argument_errors():
     assert L.mx_calib_mfma(8, (1 << 24) + 1, sink, None) == mx.MX_ERR_SHAPE
     # 256 CTAs x 4 waves x 100 rounds x 8 MFMAs x 65,536 flop
     assert mx.mx_calib_mfma_flops(256, 100) == 256 * 4 * 100 * 8 * 65536
+
+
+def test_fused_act_quant_argument_errors_and_plan(monkeypatch):
+    monkeypatch.delenv("MX_GROUPED_CONFIG", raising=False)
+    f = mx.lib().mx_a4w4_gemm_grouped_act_quant
+    #        a  rt  offs E  Rmax w  T  N     K    act hint hq  hs  stream
+    assert f(A, B, Cp, 4, 16, A, 1, 1536, 3584, 2, 1, A, B, None) == mx.MX_ERR_SHAPE     # unknown act
+    assert f(A, B, Cp, 4, 16, A, 1, 1000, 3584, 1, 1, A, B, None) == mx.MX_ERR_SHAPE
+    assert f(A, B, Cp, 0, 16, A, 1, 1536, 3584, 1, 1, A, B, None) == mx.MX_ERR_SHAPE
+    assert f(A, B, Cp, 4, 16, A, 1, 1536, 3584, 1, 1, None, B, None) == mx.MX_ERR_NULL
+    assert f(A, B, Cp, 4, 16, A, 1, 1536, 3584, 1, 1, A, None, None) == mx.MX_ERR_NULL
+    assert f(None, B, Cp, 4, 16, A, 1, 1536, 3584, 1, 1, A, B, None) == mx.MX_ERR_NULL
+    assert f(A, B, Cp, 4, 16, A, 1, 1536, 3584, 1, 1, MIS, B, None) == mx.MX_ERR_ALIGN
+    assert f(A, B, Cp, 4, 16, A, 1, 1536, 3584, 1, 1, A, MIS, None) == mx.MX_ERR_ALIGN
+    assert f(A, B, Cp, 4, 0, A, 1, 1536, 3584, 1, 1, None, None, None) == mx.MX_OK       # no rows: no-op
+    plan = mx.mx_a4w4_gemm_grouped_act_quant_plan
+    assert plan(1536, 3584, mx.MX_ACT_SWIGLU, 73) == "k_gemm_grouped_tile<1, 8, 8, 4, 1, 2, swiglu>"
+    assert plan(1536, 3584, mx.MX_ACT_SWIGLU, 5) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2, swiglu>"
+    assert plan(768, 3584, mx.MX_ACT_SILU, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2, silu>"   # 768 % 512
+    with pytest.raises(mx.MxError):
+        plan(1536, 3584, 2, 1)
+    monkeypatch.setenv("MX_GROUPED_CONFIG", "gt,1,4,4,4,1,2")   # compiled, but not with the fused epilogue
+    with pytest.raises(mx.MxError):
+        plan(1536, 3584, mx.MX_ACT_SWIGLU, 1)
