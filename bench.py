@@ -531,6 +531,22 @@ def grouped_sweep(torch, mx, W, timer):
                      "frac_hbm": round(B / HBM_PEAK * 1e6 / us, 4),
                      "frac_mfma": round(F / MFMA_FP4_PEAK * 1e6 / us, 4)})
         log(f"  grouped T={T}: {us:.2f} us ({active} experts, {R} rows)")
+        # the same GEMM1 with the fused SwiGLU + MXFP4 epilogue: h [R, N/2] as E2M1 + E8M0
+        Nh = N // 2
+        hq = torch.empty((R, Nh // 2), dtype=torch.uint8, device="cuda")
+        hs = torch.empty((R, Nh // 32), dtype=torch.uint8, device="cuda")
+        g = timer.graph([lambda: mx.mx_a4w4_gemm_grouped_act_quant(a, rt, of, E, R, stack, N, act=mx.MX_ACT_SWIGLU,
+                                                                   rows_hint=hint, h_fp4=hq, h_scale=hs)] * n)
+        us_f = timer.replay_ms(g, reps=2) * 1e3 / n
+        del g, hq, hs
+        Bf = active * per + 2 * T * K + R * (Nh // 2 + Nh // 32)
+        recs.append({"workload": "grouped_moe_gemm1_swiglu_mxfp4_e896_top16_k3584_n1536", "T": T, "rows": R,
+                     "active_experts": active, "us": round(us_f, 3), "bytes": Bf, "flops": F,
+                     "tflops": round(F / us_f / 1e6, 2), "gbps": round(Bf / us_f / 1e3, 1),
+                     "frac_hbm": round(Bf / HBM_PEAK * 1e6 / us_f, 4),
+                     "frac_mfma": round(F / MFMA_FP4_PEAK * 1e6 / us_f, 4),
+                     "kernel": mx.mx_a4w4_gemm_grouped_act_quant_plan(N, K, mx.MX_ACT_SWIGLU, hint)})
+        log(f"  grouped T={T} + fused SwiGLU/MXFP4 epilogue: {us_f:.2f} us")
     del stack
     torch.cuda.empty_cache()
     return recs

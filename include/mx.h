@@ -158,7 +158,9 @@ enum { MX_ACT_SILU = 0, MX_ACT_SWIGLU = 1 };
  * SwiGLU, the scale computed from the FP32 activation value). Routing, segments and
  * weights are those of mx_a4w4_gemm_grouped; for output row r with GEMM1 row c (FP32):
  *   act == MX_ACT_SWIGLU: h[j] = SiLU(c[j]) * c[N/2 + j], j < Nh = N/2 (gate columns first);
- *   act == MX_ACT_SILU:   h[j] = SiLU(c[j]), j < Nh = N;  SiLU(x) = x / (1 + exp(-x)).
+ *   act == MX_ACT_SILU:   h[j] = SiLU(c[j]), j < Nh = N;  SiLU(x) = x / (1 + exp(-x)),
+ * evaluated in FP32 with the hardware exponential and reciprocal (relative error at most
+ * (|x| + 8) * 2^-23).
  * h is quantized along its columns with the rule at the top of this file applied to the
  * FP32 value of h (E8M0 scale from the FP32 block amax, one conversion to E2M1) and written
  * in canonical form: h_fp4 [R_max, Nh/2] bytes (element at even j in the low nibble),

@@ -552,19 +552,30 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
     static_assert(BM * HROW * 4 <= S::SMEM, "the staged half tile fits the LDS");
     float* hb = reinterpret_cast<float*>(smem);
     const int half = wn / (WN / 2), cw = (wn % (WN / 2)) * NG;
+    // 16-byte chunk ch of a staged row sits at chunk position sw(ch): XOR-swizzled within
+    // its 32-float block by the block index, so the quantizer's lanes, which read chunk i
+    // of consecutive blocks together, mostly fall on distinct banks.
+    auto sw = [](int ch) { return (ch & ~7) | ((ch ^ (ch >> 3)) & 7); };
     auto at = [&](int g, int mt) {
-      return hb + (16 * (wm * MT + mt) + (lane & 15)) * HROW + 16 * (cw + g) + 4 * (lane >> 4);
+      return hb + (16 * (wm * MT + mt) + (lane & 15)) * HROW + 4 * sw(4 * (cw + g) + (lane >> 4));
     };
-    auto silu = [](float x) { return x / (1.0f + expf(-x)); };
+    // SiLU(x) = x * sigmoid(x) with e = exp(-|x|) in (0, 1] (no overflow): sigmoid is
+    // 1 / (1 + e) for x >= 0 and e / (1 + e) below; v_exp_f32 and v_rcp_f32 (1 ulp each),
+    // relative error at most (|x| + 8) * 2^-23 with the rounding of the exponent argument.
+    auto silu = [](float x) {
+      const float e = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);  // log2(e)
+      const float r = __builtin_amdgcn_rcpf(1.0f + e);
+      return x * (x >= 0.f ? r : e * r);
+    };
     auto quantize = [&](int col0) {  // h columns [col0, col0 + HC) of this tile's rows
       for (int id = threadIdx.x; id < BM * NB; id += 64 * NW) {
         const int r = id / NB, b = id % NB;
         if (r >= Mrows) continue;
-        const float* p = hb + r * HROW + 32 * b;
+        const float* p = hb + r * HROW;
         float v[32];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const v4f x = *reinterpret_cast<const v4f*>(p + 4 * i);
+          const v4f x = *reinterpret_cast<const v4f*>(p + 4 * sw(8 * b + i));
           v[4 * i] = x[0]; v[4 * i + 1] = x[1]; v[4 * i + 2] = x[2]; v[4 * i + 3] = x[3];
         }
         float amax = 0.f;
@@ -589,13 +600,21 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
     };
     __syncthreads();  // every wave has finished reading the operand buffers
     if constexpr (ACT == kActSwiglu) {
-      if (half == 1)  // up columns
+      if (half == 1) {  // up columns to LDS
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<v4f*>(at(g, mt)) = acc[g][mt];
+      } else {  // meanwhile the gate waves take SiLU of their accumulators in place
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[g][mt][j] = silu(acc[g][mt][j]);
+      }
       __syncthreads();
-      if (half == 0)  // gate columns: h = SiLU(gate) * up, in place
+      if (half == 0)  // h = SiLU(gate) * up, in place
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -604,7 +623,7 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
             const v4f u = *reinterpret_cast<const v4f*>(p);
             v4f h;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) h[j] = silu(acc[g][mt][j]) * u[j];
+            for (int j = 0; j < 4; ++j) h[j] = acc[g][mt][j] * u[j];
             *reinterpret_cast<v4f*>(p) = h;
           }
       __syncthreads();

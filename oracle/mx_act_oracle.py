@@ -32,8 +32,13 @@ rounding boundary its code or scale may legitimately differ from the exact one.
 within gamma_K * sum_k |a_k w_k| of the exact sum (the standard bound for K
 floating-point additions of exactly representable products, gamma_K =
 1.01 K 2^-24), the interval is carried through the activation exactly (SiLU's
-one minimum included), and widened by 2^-20 |h| for the FP32 evaluation of
-the activation itself. ``quantization_valid`` accepts a GPU scale byte only if
+one minimum included), and widened for the FP32 evaluation of the activation
+itself: (|g| + 16) 2^-23 |h|, with |g| the largest gate magnitude in the
+interval, covers an exponential and a reciprocal of 1 ulp each (the hardware
+v_exp_f32 and v_rcp_f32), the rounding of the exponential's argument
+-|g| log2(e) (relative error |g| 2^-24 in exp(-|g|)) and three roundings of
+products and sums; 2^-100 max|up| more covers an exponential that underflows
+to zero (|g| > 87, where the exact SiLU is below 2^-120). ``quantization_valid`` accepts a GPU scale byte only if
 it is the rule's scale of some block amax inside the intervals, and a GPU code
 only if it is the rule's code, at that scale, of some value in the element's
 interval. Where an interval holds a single code and scale, this is bit-exact
@@ -135,12 +140,17 @@ def grouped_gemm1_act_ref(a_bits: np.ndarray, row_token: np.ndarray, expert_offs
     lo, hi = c - d, c + d
     h = activation(c, act)
     if act == ACT_SILU:
+        glo, ghi = lo, hi
         h_lo, h_hi = _silu_range(lo, hi)
+        umax = np.ones_like(h)
     else:
         half = c.shape[1] // 2
-        slo, shi = _silu_range(lo[:, :half], hi[:, :half])
+        glo, ghi = lo[:, :half], hi[:, :half]
+        slo, shi = _silu_range(glo, ghi)
         h_lo, h_hi = _product_range(slo, shi, lo[:, half:], hi[:, half:])
-    w = 2.0 ** -20 * np.maximum(np.abs(h_lo), np.abs(h_hi)) + 1e-300
+        umax = np.maximum(np.abs(lo[:, half:]), np.abs(hi[:, half:]))
+    gmax = np.maximum(np.abs(glo), np.abs(ghi))
+    w = (gmax + 16.0) * 2.0 ** -23 * np.maximum(np.abs(h_lo), np.abs(h_hi)) + 2.0 ** -100 * umax + 1e-300
     return h, h_lo - w, h_hi + w
 
 
