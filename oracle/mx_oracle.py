@@ -33,6 +33,18 @@ The pages leave several steps open; the readings taken are:
 The GEMM result is the exact real sum of the dequantized products, evaluated
 in float64 (exact under the exponent-spread guard in ``_assert_exact``).
 
+The MoE layer's second GEMM and combine ("[HIP] [CK] [FlyDSL] [Kernel] Extend
+MXFP4 GEMM1 replacement to A4W4", Summary: the stage-2 GEMM that follows GEMM1)
+are read as follows, the pages giving no more than that stage's existence:
+
+8. GEMM2 takes its activation rows already in MXFP4 (canonical payload and
+   scales, as GEMM1's fused epilogue or the standalone quantizer emit them), in
+   expert-sorted order, and multiplies row r by the quantized weight of the
+   expert whose segment holds r; there is no inline quantization.
+9. The combine sums each token's top-k GEMM2 rows weighted by its routing
+   weights: out[t] = sum_k weights[t, k] * y[row of (t, k)]; a row index outside
+   the rows contributes nothing.
+
 Nothing here is blocked, fused or reordered beyond the definition: quantize
 each 32-element block, decode, then one float64 matrix product.
 """
@@ -246,6 +258,43 @@ def grouped_gemm_ref(a_bits: np.ndarray, row_token: np.ndarray, expert_offsets: 
         out[sel] = c
     if out is None:
         out = np.empty((0, 0), dtype=np.float64)
+    return out
+
+
+def grouped_gemm_mx_ref(a_payload: np.ndarray, a_scales: np.ndarray, expert_offsets: np.ndarray,
+                        expert_weight, rows=None) -> np.ndarray:
+    """Grouped GEMM on already-quantized rows (the second MoE GEMM).
+
+    Output row r (expert-sorted order) is the exact product of MXFP4 row r of A
+    (canonical payload and scales) and the quantized weight of the expert e with
+    expert_offsets[e] <= r < expert_offsets[e+1]. ``rows`` selects output rows.
+    """
+    offs = np.asarray(expert_offsets, dtype=np.int64)
+    R = int(offs[-1])
+    rows = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    expert_of = np.searchsorted(offs, rows, side="right") - 1
+    out = None
+    for e in np.unique(expert_of):
+        sel = np.flatnonzero(expert_of == e)
+        qw, sw = quantize_mx(expert_weight(int(e)))
+        c = gemm_from_mx(np.asarray(a_payload)[rows[sel]], np.asarray(a_scales)[rows[sel]], qw, sw)
+        if out is None:
+            out = np.empty((rows.size, c.shape[1]), dtype=np.float64)
+        out[sel] = c
+    return np.empty((0, 0)) if out is None else out
+
+
+def combine_ref(y: np.ndarray, token_rows: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """Top-k weighted combine: out[t] = sum_k weights[t, k] * y[token_rows[t, k]], float64;
+    a row index outside [0, len(y)) contributes nothing."""
+    y = np.asarray(y, dtype=np.float64)
+    tr = np.asarray(token_rows, dtype=np.int64)
+    w = np.asarray(weights, dtype=np.float64)
+    T, topk = tr.shape
+    out = np.zeros((T, y.shape[1]), dtype=np.float64)
+    for k in range(topk):
+        ok = (tr[:, k] >= 0) & (tr[:, k] < y.shape[0])
+        out[ok] += w[ok, k:k + 1] * y[tr[ok, k]]
     return out
 
 

@@ -168,6 +168,43 @@ def moe_expert_weight(e: int, N: int = MOE_N, K: int = MOE_K) -> np.ndarray:
     return normal_bf16((N, K), SEED_EXPERT_BASE + e, W_STD)
 
 
+# GEMM2 (down projection) of the same layer: h [rows, inter_dim] x W2_e [model_dim, inter_dim]
+MOE_N2 = 3584     # model_dim
+MOE_K2 = 768      # inter_dim
+SEED_EXPERT2_BASE = 2000
+SEED_COMBINE = 4
+
+
+def moe_expert_weight2(e: int, N: int = MOE_N2, K: int = MOE_K2) -> np.ndarray:
+    """W2_e [N, K] bf16 bits, ~N(0, 0.02)."""
+    return normal_bf16((N, K), SEED_EXPERT2_BASE + e, W_STD)
+
+
+def moe_token_rows(ids: np.ndarray) -> np.ndarray:
+    """[T, topk] int32: the expert-sorted row of token t's k-th expert (the inverse of the
+    stable sort moe_routing applies)."""
+    T, topk = ids.shape
+    order = np.argsort(ids.reshape(-1), kind="stable")
+    pos = np.empty_like(order)
+    pos[order] = np.arange(order.size)
+    return pos.reshape(T, topk).astype(np.int32)
+
+
+def moe_combine_weights(T: int, topk: int = MOE_TOPK, seed: int = SEED_COMBINE) -> np.ndarray:
+    """[T, topk] float32 routing weights: a softmax of standard-normal logits per token."""
+    z = np.random.default_rng(seed).standard_normal((T, topk)).astype(np.float32)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def mx_bytes(R: int, K: int, seed: int, scale_lo: int = 118, scale_hi: int = 130):
+    """Arbitrary MXFP4 rows in canonical form: uniform payload bytes [R, K/2] (every E2M1
+    code, both signs) and E8M0 scale bytes [R, K/32] uniform in [scale_lo, scale_hi)."""
+    rng = np.random.default_rng(seed)
+    return (rng.integers(0, 256, size=(R, K // 2), dtype=np.uint8),
+            rng.integers(scale_lo, scale_hi, size=(R, K // 32), dtype=np.uint8))
+
+
 def moe_expert_weights(experts, N: int = MOE_N, K: int = MOE_K, threads: int = 8):
     """Yield (e, W_e bits) for the given experts, generated on a thread pool.
 
