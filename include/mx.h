@@ -148,6 +148,37 @@ mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token,
                                const void* w_prep_stacked, void* c_bf16, int64_t T, int64_t N,
                                int64_t K, int64_t rows_hint, hipStream_t stream);
 
+/*
+ * Second MoE GEMM (the stage after GEMM1 in "[HIP] [CK] [FlyDSL] [Kernel] Extend MXFP4 GEMM1
+ * replacement to A4W4", Summary) on activation rows that are already MXFP4: output row r
+ * (expert-sorted order) is Q_r * Q(W_e)^T for the expert e with
+ * expert_offsets[e] <= r < expert_offsets[e+1], where Q_r is MXFP4 row r given in
+ * canonical form (a_fp4 [R_max, K/2] bytes, element at even k in the low nibble; a_scale
+ * [R_max, K/32] E8M0 bytes, 255 outside the contract), e.g. the output of
+ * mx_a4w4_gemm_grouped_act_quant or mx_quant_act. No quantization takes place; the sums
+ * accumulate in FP32 and are written as bf16 to c_bf16 [R_max, N] (rows >= R untouched).
+ * expert_offsets, w_prep_stacked and rows_hint as for mx_a4w4_gemm_grouped.
+ * Requires E >= 1, R_max >= 0, N % 256 == 0, K % 128 == 0. Errors: MX_ERR_NULL,
+ * MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE, MX_ERR_HIP.
+ */
+mx_status mx_a4w4_gemm_grouped_mx(const void* a_fp4, const void* a_scale, const int32_t* expert_offsets,
+                                  int64_t E, int64_t R_max, const void* w_prep_stacked, void* c_bf16,
+                                  int64_t N, int64_t K, int64_t rows_hint, hipStream_t stream);
+
+/*
+ * Top-k weighted combine of per-row outputs into per-token outputs:
+ * out[t, n] = sum over k < topk of token_weights[t, k] * y[token_rows[t, k], n], summed in
+ * FP32 in k order and rounded once to bf16 (round to nearest even); a row index outside
+ * [0, R) contributes nothing. y_bf16: [R, N] bf16 (e.g. the output of
+ * mx_a4w4_gemm_grouped_mx). token_rows: [T, topk] int32; token_weights: [T, topk] float32;
+ * out_bf16: [T, N] bf16. Requires R >= 0, T >= 0, 1 <= topk <= 1024, N > 0, N % 8 == 0.
+ * T == 0 is a no-op. Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN (y, out: 16 bytes;
+ * token_rows, token_weights: 4 bytes), MX_ERR_DEVICE, MX_ERR_HIP.
+ */
+mx_status mx_moe_combine(const void* y_bf16, int64_t R, const int32_t* token_rows,
+                         const float* token_weights, int64_t T, int64_t topk, int64_t N,
+                         void* out_bf16, hipStream_t stream);
+
 /* Activation of the fused GEMM1 epilogue. */
 enum { MX_ACT_SILU = 0, MX_ACT_SWIGLU = 1 };
 
@@ -203,6 +234,11 @@ mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t T, int64_t
  */
 mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t N, int64_t K, int32_t act, int64_t rows_hint,
                                               char* buf, size_t buf_len);
+
+/* The same for mx_a4w4_gemm_grouped_mx (its kernel depends on N and the hint). Errors as
+ * for mx_a4w4_gemm_grouped_act_quant_plan. */
+mx_status mx_a4w4_gemm_grouped_mx_plan(int64_t N, int64_t K, int64_t rows_hint, char* buf,
+                                       size_t buf_len);
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,9 @@ SIGNATURES = {
                                                 ctypes.c_int32, _c_i64, _vp, _vp, _vp]),
     "mx_a4w4_gemm_grouped_act_quant_plan": (_c_int, [_c_i64, _c_i64, ctypes.c_int32, _c_i64, ctypes.c_char_p,
                                                      _c_sz]),
+    "mx_a4w4_gemm_grouped_mx": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]),
+    "mx_a4w4_gemm_grouped_mx_plan": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
+    "mx_moe_combine": (_c_int, [_vp, _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
     "mx_calib_read": (_c_int, [_vp, _c_sz, _c_i64, _vp, _vp]),
     "mx_calib_mfma": (_c_int, [_c_i64, _c_i64, _vp, _vp]),
     "mx_calib_mfma_flops": (ctypes.c_double, [_c_i64, _c_i64]),
@@ -243,6 +246,47 @@ def mx_a4w4_gemm_grouped_act_quant_plan(N: int, K: int, act: int = MX_ACT_SWIGLU
     return buf.value.decode()
 
 
+def mx_a4w4_gemm_grouped_mx(a_fp4, a_scale, expert_offsets, E: int, R_max: int, w_prep_stacked, N: int,
+                            rows_hint: int = 1, out=None, stream=None):
+    """Second MoE GEMM on MXFP4 rows: a_fp4 uint8 [R_max, K/2], a_scale uint8 [R_max, K/32]
+    -> C [R_max, N] bf16 (rows >= R untouched)."""
+    torch = _torch()
+    K = 2 * a_fp4.shape[1]
+    if tuple(a_scale.shape) != (a_fp4.shape[0], K // 32) or a_fp4.shape[0] < R_max:
+        raise ValueError("a_fp4 / a_scale must be [>= R_max, K/2] and [same rows, K/32]")
+    c = out if out is not None else torch.empty((R_max, N), dtype=torch.bfloat16, device=a_fp4.device)
+    _check(lib().mx_a4w4_gemm_grouped_mx(
+        _dev(a_fp4, torch.uint8, "a_fp4") if R_max > 0 else None,
+        _dev(a_scale, torch.uint8, "a_scale") if R_max > 0 else None,
+        _dev(expert_offsets, torch.int32, "expert_offsets"), int(E), int(R_max),
+        _dev(w_prep_stacked, torch.uint8, "w_prep_stacked"), _dev(c, torch.bfloat16, "c_bf16") if R_max > 0 else None,
+        int(N), K, int(rows_hint), _stream_ptr(stream)), "mx_a4w4_gemm_grouped_mx")
+    return c
+
+
+def mx_a4w4_gemm_grouped_mx_plan(N: int, K: int, rows_hint: int = 1) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().mx_a4w4_gemm_grouped_mx_plan(int(N), int(K), int(rows_hint), buf, len(buf)),
+           "mx_a4w4_gemm_grouped_mx_plan")
+    return buf.value.decode()
+
+
+def mx_moe_combine(y_bf16, token_rows, token_weights, out=None, stream=None):
+    """out [T, N] bf16 = sum_k token_weights[t, k] * y[token_rows[t, k]] (FP32, k order)."""
+    torch = _torch()
+    R, N = y_bf16.shape
+    T, topk = token_rows.shape
+    if tuple(token_weights.shape) != (T, topk):
+        raise ValueError("token_weights must match token_rows")
+    o = out if out is not None else torch.empty((T, N), dtype=torch.bfloat16, device=token_rows.device)
+    _check(lib().mx_moe_combine(
+        _dev(y_bf16, torch.bfloat16, "y_bf16") if R > 0 else None, R,
+        _dev(token_rows, torch.int32, "token_rows") if T > 0 else None,
+        _dev(token_weights, torch.float32, "token_weights") if T > 0 else None, T, topk, N,
+        _dev(o, torch.bfloat16, "out_bf16") if T > 0 else None, _stream_ptr(stream)), "mx_moe_combine")
+    return o
+
+
 def mx_a4w4_gemm_plan(M: int, N: int, K: int, workspace_bytes=None) -> str:
     """Kernel(s) mx_a4w4_gemm launches for this shape; workspace_bytes defaults to what
     mx_a4w4_gemm allocates when given no workspace."""
@@ -291,6 +335,7 @@ __all__ = [
     "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
     "mx_prepare_weight_packed", "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
     "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_a4w4_gemm_grouped_act_quant",
-    "mx_a4w4_gemm_grouped_act_quant_plan", "MX_ACT_SILU", "MX_ACT_SWIGLU", "mx_calib_read", "mx_calib_mfma",
+    "mx_a4w4_gemm_grouped_act_quant_plan", "mx_a4w4_gemm_grouped_mx", "mx_a4w4_gemm_grouped_mx_plan",
+    "mx_moe_combine", "MX_ACT_SILU", "MX_ACT_SWIGLU", "mx_calib_read", "mx_calib_mfma",
     "mx_calib_mfma_flops",
 ]

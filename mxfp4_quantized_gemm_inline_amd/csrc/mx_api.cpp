@@ -160,6 +160,47 @@ mx_status mx_a4w4_gemm_grouped_act_quant(const void* a_bf16, const int32_t* row_
                                               h_scale, T, N, K, act, rows_hint < 1 ? 1 : rows_hint, stream));
 }
 
+mx_status mx_a4w4_gemm_grouped_mx(const void* a_fp4, const void* a_scale, const int32_t* expert_offsets, int64_t E,
+                                  int64_t R_max, const void* w_prep_stacked, void* c_bf16, int64_t N, int64_t K,
+                                  int64_t rows_hint, hipStream_t stream) {
+  if (E < 1 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (!expert_offsets || !w_prep_stacked) return MX_ERR_NULL;
+  if (R_max > 0 && (!a_fp4 || !a_scale || !c_bf16)) return MX_ERR_NULL;
+  if ((a_fp4 && !aligned16(a_fp4)) || (a_scale && !aligned16(a_scale)) || !aligned16(w_prep_stacked) ||
+      (c_bf16 && !aligned16(c_bf16)) || (reinterpret_cast<uintptr_t>(expert_offsets) & 3u))
+    return MX_ERR_ALIGN;
+  if (R_max == 0) return MX_OK;
+  mx_status d = check_device();
+  if (d != MX_OK) return d;
+  return from_hip(mx::launch_gemm_grouped_mx(a_fp4, a_scale, expert_offsets, E, R_max, w_prep_stacked, c_bf16, N,
+                                             K, rows_hint < 1 ? 1 : rows_hint, stream));
+}
+
+mx_status mx_a4w4_gemm_grouped_mx_plan(int64_t N, int64_t K, int64_t rows_hint, char* buf, size_t buf_len) {
+  if (!gemm_shape_ok(N, K)) return MX_ERR_SHAPE;
+  if (!buf || buf_len == 0) return MX_ERR_NULL;
+  if (!mx::grouped_mx_plan(N, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
+    buf[0] = '\0';
+    return MX_ERR_HIP;
+  }
+  return MX_OK;
+}
+
+mx_status mx_moe_combine(const void* y_bf16, int64_t R, const int32_t* token_rows, const float* token_weights,
+                         int64_t T, int64_t topk, int64_t N, void* out_bf16, hipStream_t stream) {
+  if (R < 0 || T < 0 || topk < 1 || topk > 1024 || N <= 0 || N % 8 != 0 || R > (1ll << 31) - 1 ||
+      T > (1ll << 31) - 1 || N > (1ll << 30) || T * (N / 8) > (1ll << 39))
+    return MX_ERR_SHAPE;
+  if (T == 0) return MX_OK;
+  if (!token_rows || !token_weights || !out_bf16 || (R > 0 && !y_bf16)) return MX_ERR_NULL;
+  if ((y_bf16 && !aligned16(y_bf16)) || !aligned16(out_bf16) ||
+      (reinterpret_cast<uintptr_t>(token_rows) & 3u) || (reinterpret_cast<uintptr_t>(token_weights) & 3u))
+    return MX_ERR_ALIGN;
+  mx_status d = check_device();
+  if (d != MX_OK) return d;
+  return from_hip(mx::launch_moe_combine(y_bf16, R, token_rows, token_weights, T, topk, N, out_bf16, stream));
+}
+
 mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t N, int64_t K, int32_t act, int64_t rows_hint, char* buf,
                                               size_t buf_len) {
   if (!gemm_shape_ok(N, K) || (act != MX_ACT_SILU && act != MX_ACT_SWIGLU)) return MX_ERR_SHAPE;

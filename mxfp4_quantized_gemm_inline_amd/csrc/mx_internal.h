@@ -22,6 +22,12 @@ hipError_t launch_gemm_grouped_act(const void* a, const int32_t* row_token, cons
                                    int64_t R_max, const void* wp, void* hq, void* hs, int64_t T, int64_t N,
                                    int64_t K, int act, int64_t rows_hint, hipStream_t st);
 bool grouped_act_plan(int64_t N, int act, int64_t rows_hint, char* buf, size_t len);
+// Second MoE GEMM on MXFP4 rows (aq [R_max, K/2], as [R_max, K/32]) and the top-k combine.
+hipError_t launch_gemm_grouped_mx(const void* aq, const void* as, const int32_t* offsets, int64_t E, int64_t R_max,
+                                  const void* wp, void* c, int64_t N, int64_t K, int64_t rows_hint, hipStream_t st);
+bool grouped_mx_plan(int64_t N, int64_t rows_hint, char* buf, size_t len);
+hipError_t launch_moe_combine(const void* y, int64_t R, const int32_t* rows, const float* w, int64_t T, int64_t topk,
+                              int64_t N, void* out, hipStream_t st);
 // Name the kernel(s) the launchers above would run (false: the tuning override is invalid).
 bool gemm_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes, char* buf, size_t len);
 bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t T, int64_t rows_hint, char* buf,

@@ -365,14 +365,22 @@ struct TileShape {
 struct TileRowsDense {
   const uint8_t* base;
   int K;
-  static constexpr bool kGather = false;
+  static constexpr bool kGather = false, kMx = false;
 };
 // Gathered: tile row r is A[tok[r]]; a token outside [0, T) reads as an all-zero row.
 struct TileRowsGather {
   const uint8_t* A;
   const int32_t* tok;
   int T, K;
-  static constexpr bool kGather = true;
+  static constexpr bool kGather = true, kMx = false;
+};
+// Already quantized: tile row r is MXFP4 row r (canonical payload q [rows, K/2] and scales
+// s [rows, K/32], both offset to the tile's first row); no quantization takes place.
+struct TileRowsMx {
+  const uint8_t* q;
+  const uint8_t* s;
+  int K;
+  static constexpr bool kGather = false, kMx = true;
 };
 
 // Fused GEMM1 epilogue ("[gfx1250] Fuse A4W4 stage1 FP4 quantization", Summary): the
@@ -429,7 +437,10 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     const int r = min(16 * (w + NW * i) + (lane >> 2), Mrows - 1);
-    if constexpr (!Rows::kGather) {
+    if constexpr (Rows::kMx) {  // payload byte offset of the lane's block at step 0; its scale follows from r
+      aoff[i] = (uint32_t)r * (uint32_t)(rows.K / 2) + (uint32_t)(lane & 3) * 16u;
+      aptr[i] = rows.s + (size_t)r * (rows.K / kBlock) + (lane & 3);
+    } else if constexpr (!Rows::kGather) {
       aoff[i] = (uint32_t)r * (uint32_t)rows.K * 2u + (uint32_t)(lane & 3) * (kBlock * 2);
     } else {
       const int tk = rows.tok[r];
@@ -451,13 +462,23 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
   const uint32_t wlane = lane * 16, slane = lane * 4;
   const int sbyte = gw0 & 3;  // byte of group gw0 in its scale word (0 when NG % 4 == 0)
 
-  uint32_t areg[PF][BPT][16];
+  // a lane's activation block per slot: 16 bf16 words, or (already quantized) 4 payload
+  // words and the scale byte
+  constexpr int AW = Rows::kMx ? 5 : 16;
+  uint32_t areg[PF][BPT][AW];
   uint4 wq[PF + 1][NG];
   uint32_t wsw[PF + 1][NQ];
 
   auto load_a = [&](int t, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
-    if constexpr (!Rows::kGather) {
+    if constexpr (Rows::kMx) {
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        const uint4 u = *reinterpret_cast<const uint4*>(rows.q + (size_t)t * (kStepK / 2) + aoff[i]);
+        areg[SL][i][0] = u.x; areg[SL][i][1] = u.y; areg[SL][i][2] = u.z; areg[SL][i][3] = u.w;
+        areg[SL][i][4] = aptr[i][(size_t)t * (kStepK / kBlock)];
+      }
+    } else if constexpr (!Rows::kGather) {
       const uint8_t* base = rows.base + (size_t)t * kStepK * 2;
 #pragma unroll
       for (int i = 0; i < BPT; ++i) load_block_at(base, aoff[i], areg[SL][i]);
@@ -496,7 +517,13 @@ __device__ __forceinline__ void tile_core(const Rows& rows, int Mrows, const uin
     for (int i = 0; i < BPT; ++i) {
       const int tile = w + NW * i;
       uint32_t q[4];
-      uint32_t sc = quant_block(areg[SA][i], q);
+      uint32_t sc;
+      if constexpr (Rows::kMx) {
+        q[0] = areg[SA][i][0]; q[1] = areg[SA][i][1]; q[2] = areg[SA][i][2]; q[3] = areg[SA][i][3];
+        sc = areg[SA][i][4];
+      } else {
+        sc = quant_block(areg[SA][i], q);
+      }
       if constexpr (Rows::kGather) {  // a row with no valid token quantizes to zero
 #pragma unroll
         for (int c = 0; c < 4; ++c) q[c] = avalid[i] ? q[c] : 0u;
@@ -715,24 +742,18 @@ void k_gemm_tile(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp,
 // CTA ranks the experts' unit counts with a block scan to find its unit, and the surplus
 // CTAs exit. One expert's units are consecutive and dealt to one XCD (as in tile_coords),
 // so its column tiles share the gathered rows and its row tiles the weight in that L2.
-// With ACT >= 0 the output is the fused activation + MXFP4 quantization (tile_core) into
-// Hq [R_max, Nh/2] and Hs [R_max, Nh/32] instead of C.
-template <int WM, int WN, int MT, int NG, int PF, int OCC, int ACT = -1>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
-void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
-                         const int32_t* __restrict__ offs, int E, int R_max, const uint8_t* __restrict__ Wall,
-                         uint16_t* __restrict__ C, int Ttok, int N, int K, uint8_t* __restrict__ Hq,
-                         uint8_t* __restrict__ Hs, int Nh) {
-  using S = TileShape<WM, WN, MT, NG>;
-  constexpr int NTH = S::NTH, BM = S::BM, BN = S::BN;
-  __shared__ __align__(16) uint8_t smem[S::SMEM];
-  __shared__ int s_scan[NTH];
-  __shared__ int s_unit[4];  // expert, segment start, segment rows, its first unit
+// The unit (expert, row tile, column tile) of this CTA: the grid is an upper bound on the
+// units; the CTA ranks the experts' unit counts with a block scan (s_scan: NTH ints, s_unit:
+// 4 ints of LDS) and finds its own. False for a surplus CTA. Every value is CTA-uniform.
+struct GroupedUnit {
+  int e, r0, Mrows, bn;
+};
+template <int NTH, int BM>
+__device__ __forceinline__ bool grouped_unit(const int32_t* __restrict__ offs, int E, int R_max, int tiles_n,
+                                             int* s_scan, int* s_unit, GroupedUnit& unit) {
   const int tid = threadIdx.x;
-  const int tiles_n = (N + BN - 1) / BN;
   const int total = gridDim.x;
   const int L = (blockIdx.x % 8) * (total / 8) + min((int)(blockIdx.x % 8), total % 8) + blockIdx.x / 8;
-
   auto seg = [&](int e, int& lo, int& hi) {
     lo = min(max(offs[e], 0), R_max);
     hi = min(max(offs[e + 1], lo), R_max);
@@ -768,11 +789,32 @@ void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restri
   __syncthreads();
   // uniform across the CTA: keep them (and every address derived from them) scalar
   const int e = __builtin_amdgcn_readfirstlane(s_unit[0]);
-  if (e < 0) return;  // surplus CTA: the grid over-counts the units
+  if (e < 0) return false;  // surplus CTA: the grid over-counts the units
   const int lo = __builtin_amdgcn_readfirstlane(s_unit[1]), cnt = __builtin_amdgcn_readfirstlane(s_unit[2]);
   const int tiles_e = (cnt + BM - 1) / BM;
   const int rem = L - __builtin_amdgcn_readfirstlane(s_unit[3]), bn = rem / tiles_e, mt = rem % tiles_e;
   const int r0 = lo + mt * BM, Mrows = min(BM, cnt - mt * BM);
+  unit = GroupedUnit{e, r0, Mrows, bn};
+  return true;
+}
+
+// With ACT >= 0 the output is the fused activation + MXFP4 quantization (tile_core) into
+// Hq [R_max, Nh/2] and Hs [R_max, Nh/32] instead of C.
+template <int WM, int WN, int MT, int NG, int PF, int OCC, int ACT = -1>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+                         const int32_t* __restrict__ offs, int E, int R_max, const uint8_t* __restrict__ Wall,
+                         uint16_t* __restrict__ C, int Ttok, int N, int K, uint8_t* __restrict__ Hq,
+                         uint8_t* __restrict__ Hs, int Nh) {
+  using S = TileShape<WM, WN, MT, NG>;
+  constexpr int NTH = S::NTH, BM = S::BM, BN = S::BN;
+  __shared__ __align__(16) uint8_t smem[S::SMEM];
+  __shared__ int s_scan[NTH];
+  __shared__ int s_unit[4];  // expert, segment start, segment rows, its first unit
+  const int tid = threadIdx.x;
+  GroupedUnit u;
+  if (!grouped_unit<NTH, BM>(offs, E, R_max, (N + BN - 1) / BN, s_scan, s_unit, u)) return;
+  const int e = u.e, r0 = u.r0, Mrows = u.Mrows, bn = u.bn;
   uint16_t* Cout = ACT >= 0 ? nullptr : C + (size_t)r0 * N;
   ActOut ao;
   if constexpr (ACT >= 0) ao = ActOut{Hq + (size_t)r0 * (Nh / 2), Hs + (size_t)r0 * (Nh / 32), Nh};
@@ -797,6 +839,52 @@ void k_gemm_grouped_tile(const uint16_t* __restrict__ A, const int32_t* __restri
   const TileRowsGather rows{reinterpret_cast<const uint8_t*>(A), row_token + r0, Ttok, K};
   tile_core<WM, WN, MT, NG, PF, ACT>(rows, Mrows, Wall + (size_t)e * prepared_bytes(N, K), Cout, nullptr, N, K, bn,
                                      0, steps_of(K), smem, ao);
+}
+
+// The second MoE GEMM: the same units over already-quantized MXFP4 rows (expert-sorted,
+// canonical payload Aq [R_max, K/2] and scales As [R_max, K/32]); bf16 rows of C.
+template <int WM, int WN, int MT, int NG, int PF, int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, 8)))
+void k_gemm_grouped_tile_mx(const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ As,
+                            const int32_t* __restrict__ offs, int E, int R_max, const uint8_t* __restrict__ Wall,
+                            uint16_t* __restrict__ C, int N, int K) {
+  using S = TileShape<WM, WN, MT, NG>;
+  __shared__ __align__(16) uint8_t smem[S::SMEM];
+  __shared__ int s_scan[S::NTH];
+  __shared__ int s_unit[4];
+  GroupedUnit u;
+  if (!grouped_unit<S::NTH, S::BM>(offs, E, R_max, (N + S::BN - 1) / S::BN, s_scan, s_unit, u)) return;
+  const TileRowsMx rows{Aq + (size_t)u.r0 * (K / 2), As + (size_t)u.r0 * (K / kBlock), K};
+  tile_core<WM, WN, MT, NG, PF>(rows, u.Mrows, Wall + (size_t)u.e * prepared_bytes(N, K), C + (size_t)u.r0 * N,
+                                nullptr, N, K, u.bn, 0, steps_of(K), smem);
+}
+
+// Top-k weighted combine: out[t, n] = sum_k w[t, k] * y[rows[t, k], n] in FP32 in k order,
+// rounded once to bf16; a row index outside [0, R) contributes nothing. One thread per token
+// and 8 columns (16-byte loads and store).
+__global__ __launch_bounds__(256) void k_moe_combine(const uint16_t* __restrict__ y, int R,
+                                                     const int32_t* __restrict__ rows,
+                                                     const float* __restrict__ wts, int T, int topk, int N,
+                                                     uint16_t* __restrict__ out) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = N / 8;
+  if (id >= (int64_t)T * cpr) return;
+  const int t = (int)(id / cpr), c = (int)(id % cpr) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < topk; ++k) {
+    const int r = rows[(size_t)t * topk + k];
+    if (r < 0 || r >= R) continue;
+    const float wk = wts[(size_t)t * topk + k];
+    const uint4 v = *reinterpret_cast<const uint4*>(y + (size_t)r * N + c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wk * __builtin_bit_cast(float, u[i] << 16);
+      acc[2 * i + 1] += wk * __builtin_bit_cast(float, u[i] & 0xffff0000u);
+    }
+  }
+  const uint2 lo = pack4_bf16(acc[0], acc[1], acc[2], acc[3]), hi = pack4_bf16(acc[4], acc[5], acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(out + (size_t)t * N + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 // ====================================================================== wide-tile GEMM (large M)
@@ -1516,6 +1604,20 @@ hipError_t run_grouped_tile(const void* a, const int32_t* rt, const int32_t* off
   return hipGetLastError();
 }
 
+template <int WM, int WN, int MT, int NG, int PF, int OCC>
+hipError_t run_grouped_tile_mx(const void* aq, const void* as, const int32_t* offs, int E, int R_max, const void* wp,
+                               void* c, int N, int K, hipStream_t st) {
+  using S = TileShape<WM, WN, MT, NG>;
+  const int64_t active = E < R_max ? E : R_max;
+  const int64_t grid = (active + R_max / S::BM) * ((N + S::BN - 1) / S::BN);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm_grouped_tile_mx<WM, WN, MT, NG, PF, OCC>), dim3((unsigned)grid), dim3(S::NTH), 0, st,
+                     static_cast<const uint8_t*>(aq), static_cast<const uint8_t*>(as), offs, E, R_max,
+                     static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), N, K);
+  return hipGetLastError();
+}
+
 template <int WM, int WN, int MT, int NG, int PF, int OCC, int ACT>
 hipError_t run_grouped_tile_act(const void* a, const int32_t* rt, const int32_t* offs, int E, int R_max,
                                 const void* wp, void* hq, void* hs, int T, int N, int K, hipStream_t st) {
@@ -1610,10 +1712,11 @@ namespace {
   X(1, 4, 4, 4, 2, 2)             \
   X(1, 8, 8, 4, 1, 2)
 
-// The fused call always runs the tiled grouped kernel (its epilogue needs a whole row tile
-// of gate and up columns in one CTA): 128 x 512 tiles for segments longer than 64 rows when
-// N is a multiple of 512, 64 x 256 otherwise; MX_GROUPED_CONFIG="gt,..." may force another
-// fused-capable configuration (tuning only).
+// The fused call and the second GEMM always run the tiled grouped kernel (the fused epilogue
+// needs a whole row tile of gate and up columns in one CTA; the second GEMM has no streaming
+// variant): 128 x 512 tiles for segments longer than 64 rows when N is a multiple of 512,
+// 64 x 256 otherwise; MX_GROUPED_CONFIG="gt,..." may force another of these configurations
+// (tuning only).
 bool resolve_grouped_act(int N, int64_t rows_hint, GroupedConfig& g) {
   const char* s = std::getenv("MX_GROUPED_CONFIG");
   if (s && *s) {
@@ -1649,6 +1752,36 @@ hipError_t launch_gemm_grouped_act(const void* a, const int32_t* row_token, cons
   MX_GROUPED_ACT_CONFIGS(X)
 #undef X
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_grouped_mx(const void* aq, const void* as, const int32_t* offsets, int64_t E, int64_t R_max,
+                                  const void* wp, void* c, int64_t N, int64_t K, int64_t rows_hint, hipStream_t st) {
+  const int e = (int)E, r = (int)R_max, n = (int)N, k = (int)K;
+  GroupedConfig g;
+  if (!resolve_grouped_act(n, rows_hint, g)) return hipErrorInvalidValue;
+#define X(wm, wn, mt, ng, pf, occ)                                                          \
+  if (g.WM == wm && g.WN == wn && g.MT == mt && g.NG == ng && g.PF == pf && g.OCC == occ)  \
+    return run_grouped_tile_mx<wm, wn, mt, ng, pf, occ>(aq, as, offsets, e, r, wp, c, n, k, st);
+  MX_GROUPED_ACT_CONFIGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+bool grouped_mx_plan(int64_t N, int64_t rows_hint, char* buf, size_t len) {
+  GroupedConfig g;
+  if (!resolve_grouped_act((int)N, rows_hint, g)) return false;
+  std::snprintf(buf, len, "k_gemm_grouped_tile_mx<%d, %d, %d, %d, %d, %d>", g.WM, g.WN, g.MT, g.NG, g.PF, g.OCC);
+  return true;
+}
+
+hipError_t launch_moe_combine(const void* y, int64_t R, const int32_t* rows, const float* w, int64_t T, int64_t topk,
+                              int64_t N, void* out, hipStream_t st) {
+  const int64_t n = T * (N / 8);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(y), (int)R, rows, w, (int)T, (int)topk, (int)N,
+                     static_cast<uint16_t*>(out));
+  return hipGetLastError();
 }
 
 bool grouped_act_plan(int64_t N, int act, int64_t rows_hint, char* buf, size_t len) {

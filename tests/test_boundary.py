@@ -204,3 +204,30 @@ def test_fused_act_quant_argument_errors_and_plan(monkeypatch):
     monkeypatch.setenv("MX_GROUPED_CONFIG", "gt,1,4,4,4,1,2")   # compiled, but not with the fused epilogue
     with pytest.raises(mx.MxError):
         plan(1536, 3584, mx.MX_ACT_SWIGLU, 1)
+
+
+def test_gemm2_and_combine_argument_errors_and_plan(monkeypatch):
+    monkeypatch.delenv("MX_GROUPED_CONFIG", raising=False)
+    g = mx.lib().mx_a4w4_gemm_grouped_mx
+    #        aq as  offs E  Rmax w  c   N     K    hint stream
+    assert g(A, B, Cp, 0, 16, A, B, 3584, 768, 1, None) == mx.MX_ERR_SHAPE
+    assert g(A, B, Cp, 4, 16, A, B, 3584, 700, 1, None) == mx.MX_ERR_SHAPE
+    assert g(None, B, Cp, 4, 16, A, B, 3584, 768, 1, None) == mx.MX_ERR_NULL
+    assert g(A, None, Cp, 4, 16, A, B, 3584, 768, 1, None) == mx.MX_ERR_NULL
+    assert g(A, B, None, 4, 16, A, B, 3584, 768, 1, None) == mx.MX_ERR_NULL
+    assert g(A, B, Cp, 4, 16, A, None, 3584, 768, 1, None) == mx.MX_ERR_NULL
+    assert g(MIS, B, Cp, 4, 16, A, B, 3584, 768, 1, None) == mx.MX_ERR_ALIGN
+    assert g(A, B, Cp, 4, 0, A, B, 3584, 768, 1, None) == mx.MX_OK          # no rows: no-op
+    c = mx.lib().mx_moe_combine
+    #        y  R   rows wts T  topk N   out stream
+    assert c(A, 8, B, Cp, 0, 2, 64, A, None) == mx.MX_OK                     # no tokens: no-op
+    assert c(A, 8, B, Cp, 4, 0, 64, A, None) == mx.MX_ERR_SHAPE
+    assert c(A, 8, B, Cp, 4, 2, 60, A, None) == mx.MX_ERR_SHAPE
+    assert c(A, -1, B, Cp, 4, 2, 64, A, None) == mx.MX_ERR_SHAPE
+    assert c(A, 8, None, Cp, 4, 2, 64, A, None) == mx.MX_ERR_NULL
+    assert c(None, 8, B, Cp, 4, 2, 64, A, None) == mx.MX_ERR_NULL
+    assert c(A, 8, B, Cp, 4, 2, 64, MIS, None) == mx.MX_ERR_ALIGN
+    assert c(A, 8, B + 2, Cp, 4, 2, 64, A, None) == mx.MX_ERR_ALIGN
+    assert mx.mx_a4w4_gemm_grouped_mx_plan(3584, 768, 73) == "k_gemm_grouped_tile_mx<1, 8, 8, 4, 1, 2>"
+    assert mx.mx_a4w4_gemm_grouped_mx_plan(3584, 768, 5) == "k_gemm_grouped_tile_mx<1, 4, 4, 4, 2, 2>"
+    assert mx.mx_a4w4_gemm_grouped_mx_plan(768, 768, 73) == "k_gemm_grouped_tile_mx<1, 4, 4, 4, 2, 2>"
