@@ -500,15 +500,23 @@ def main():
 
 
 def grouped_sweep(torch, mx, W, timer):
-    """Grouped MoE GEMM1 (E=896, top-16, K=3584, N=1536) at T = 1, 16, 256, 4096."""
+    """The MoE layer at T = 1, 16, 256, 4096 (E=896, top-16): grouped GEMM1 (K=3584, N=1536)
+    with bf16 output and with the fused SwiGLU + MXFP4 epilogue, the second GEMM on MXFP4 rows
+    (K=768, N=3584) and the top-16 combine."""
     N, K, E = W.MOE_N, W.MOE_K, W.MOE_E
     per = mx.mx_prepared_weight_bytes(N, K)
     stack = torch.empty(E * per, dtype=torch.uint8, device="cuda")
     t0 = time.perf_counter()
     for e, w in W.moe_expert_weights(range(E), threads=min(16, os.cpu_count() or 8)):
         mx.mx_prepare_weight(dev_bf16(torch, w), out=stack[e * per:(e + 1) * per])
+    per2 = mx.mx_prepared_weight_bytes(W.MOE_N2, W.MOE_K2)
+    stack2 = torch.empty(E * per2, dtype=torch.uint8, device="cuda")
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 8)) as ex:
+        for e, w2 in zip(range(E), ex.map(W.moe_expert_weight2, range(E))):
+            mx.mx_prepare_weight(dev_bf16(torch, w2), out=stack2[e * per2:(e + 1) * per2])
     torch.cuda.synchronize()
-    log(f"grouped: prepared {E} experts in {time.perf_counter() - t0:.1f} s")
+    log(f"grouped: prepared {E} experts (both GEMMs) in {time.perf_counter() - t0:.1f} s")
     recs = []
     for T in W.MOE_TOKENS:
         a = dev_bf16(torch, W.moe_activation(T))
@@ -529,7 +537,8 @@ def grouped_sweep(torch, mx, W, timer):
                      "active_experts": active, "us": round(us, 3), "bytes": B, "flops": F,
                      "tflops": round(F / us / 1e6, 2), "gbps": round(B / us / 1e3, 1),
                      "frac_hbm": round(B / HBM_PEAK * 1e6 / us, 4),
-                     "frac_mfma": round(F / MFMA_FP4_PEAK * 1e6 / us, 4)})
+                     "frac_mfma": round(F / MFMA_FP4_PEAK * 1e6 / us, 4),
+                     "kernel": mx.mx_a4w4_gemm_grouped_plan(E, R, T, N, K, hint)})
         log(f"  grouped T={T}: {us:.2f} us ({active} experts, {R} rows)")
         # the same GEMM1 with the fused SwiGLU + MXFP4 epilogue: h [R, N/2] as E2M1 + E8M0
         Nh = N // 2
@@ -547,7 +556,33 @@ def grouped_sweep(torch, mx, W, timer):
                      "frac_mfma": round(F / MFMA_FP4_PEAK * 1e6 / us_f, 4),
                      "kernel": mx.mx_a4w4_gemm_grouped_act_quant_plan(N, K, mx.MX_ACT_SWIGLU, hint)})
         log(f"  grouped T={T} + fused SwiGLU/MXFP4 epilogue: {us_f:.2f} us")
-    del stack
+        # the layer's second GEMM on MXFP4 rows (inter_dim 768 -> model_dim 3584), then the combine
+        N2, K2 = W.MOE_N2, W.MOE_K2
+        aq_h, as_h = W.mx_bytes(R, K2, seed=500 + T)
+        aq, as_ = torch.from_numpy(aq_h).cuda(), torch.from_numpy(as_h).cuda()
+        y = torch.empty((R, N2), dtype=torch.bfloat16, device="cuda")
+        g = timer.graph([lambda: mx.mx_a4w4_gemm_grouped_mx(aq, as_, of, E, R, stack2, N2, rows_hint=hint, out=y)] * n)
+        us2 = timer.replay_ms(g, reps=2) * 1e3 / n
+        del g
+        B2 = active * per2 + R * (K2 // 2 + K2 // 32) + 2 * R * N2
+        F2 = 2 * R * N2 * K2
+        recs.append({"workload": "moe_gemm2_mxfp4_e896_top16_k768_n3584", "T": T, "rows": R, "active_experts": active,
+                     "us": round(us2, 3), "bytes": B2, "flops": F2, "tflops": round(F2 / us2 / 1e6, 2),
+                     "gbps": round(B2 / us2 / 1e3, 1), "frac_hbm": round(B2 / HBM_PEAK * 1e6 / us2, 4),
+                     "frac_mfma": round(F2 / MFMA_FP4_PEAK * 1e6 / us2, 4),
+                     "kernel": mx.mx_a4w4_gemm_grouped_mx_plan(N2, K2, hint)})
+        tr = torch.from_numpy(W.moe_token_rows(W.moe_routing(T)[0])).cuda()
+        wt = torch.from_numpy(W.moe_combine_weights(T)).cuda()
+        o = torch.empty((T, N2), dtype=torch.bfloat16, device="cuda")
+        g = timer.graph([lambda: mx.mx_moe_combine(y, tr, wt, out=o)] * n)
+        us_c = timer.replay_ms(g, reps=2) * 1e3 / n
+        del g, y, o, aq, as_
+        Bc = 2 * R * N2 + 2 * T * N2 + 8 * R
+        recs.append({"workload": "moe_combine_top16_n3584", "T": T, "rows": R, "us": round(us_c, 3), "bytes": Bc,
+                     "flops": 2 * R * N2, "gbps": round(Bc / us_c / 1e3, 1),
+                     "frac_hbm": round(Bc / HBM_PEAK * 1e6 / us_c, 4), "kernel": "k_moe_combine"})
+        log(f"  T={T} second GEMM on MXFP4 rows: {us2:.2f} us; top-16 combine: {us_c:.2f} us")
+    del stack, stack2
     torch.cuda.empty_cache()
     return recs
 
