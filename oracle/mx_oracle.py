@@ -44,6 +44,10 @@ are read as follows, the pages giving no more than that stage's existence:
 9. The combine sums each token's top-k GEMM2 rows weighted by its routing
    weights: out[t] = sum_k weights[t, k] * y[row of (t, k)]; a row index outside
    the rows contributes nothing.
+10. The A16WFP4 variant ("[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM",
+    CI Guide: named as outside that change) keeps the activations in bf16 and
+    multiplies them by the MXFP4 weight decoded to real values (no activation
+    quantization).
 
 Nothing here is blocked, fused or reordered beyond the definition: quantize
 each 32-element block, decode, then one float64 matrix product.
@@ -259,6 +263,15 @@ def grouped_gemm_ref(a_bits: np.ndarray, row_token: np.ndarray, expert_offsets: 
     if out is None:
         out = np.empty((0, 0), dtype=np.float64)
     return out
+
+
+def gemm_a16w4_ref(a_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """A16WFP4: the bf16 activations A [M, K], unquantized, times the MXFP4-quantized
+    weight W [N, K] decoded to real values; one float64 matrix product. Each product of a
+    bf16 value and a decoded E2M1 value is exact; the float64 sum's rounding (at most
+    K 2^-53 sum |a w|) is negligible against any bf16-output tolerance."""
+    qw, sw = quantize_mx(w_bits)
+    return bf16_to_f64(a_bits) @ dequantize_mx(qw, sw).T
 
 
 def grouped_gemm_mx_ref(a_payload: np.ndarray, a_scales: np.ndarray, expert_offsets: np.ndarray,
