@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "A4W4 GEMM us + %HBM roofline (M<=32) / %MXFP4 MFMA peak (M>=512)"
 HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
 MFMA_FP4_PEAK = 10.1e15      # flop/s, MI355X dense MXFP4
+MFMA_BF16_PEAK = 2.5e15      # flop/s, MI355X dense bf16 (the A16WFP4 variant's MFMA)
 MALL_BYTES = 256 << 20       # Infinity Cache
 ROTATE_TARGET = 1 << 30      # bytes touched per rotation cycle (4x the Infinity Cache)
 HEADLINE = "n7168_k768"
@@ -429,7 +430,7 @@ def main():
     roof["algorithmic_flops"] = Fd
 
     # ---------------- full sweep (context)
-    sweep = {"dense": [], "grouped": []}
+    sweep = {"dense": [], "grouped": [], "a16w4": []}
     if not args.no_sweep:
         for name, (Nn, Kk, mss, st) in W.DENSE_CONFIGS.items():
             if name in ("smoke_16x256x256", HEADLINE):
@@ -449,6 +450,25 @@ def main():
             del wpn
             torch.cuda.empty_cache()
         sweep["dense"] = [*head_points, *sweep["dense"]]
+        # the A16WFP4 variant at the headline shape (bf16 activations x decoded weight on the
+        # bf16 MFMA): context, priced against the bf16 MFMA peak
+        sweep["a16w4"] = []
+        for m in ms:
+            cold = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=True)
+
+            def launch16(i, pt=cold):
+                a_r, w_r, c_r = pt.sets[i % pt.R]
+                return lambda: mx.mx_a16w4_gemm(a_r, w_r, N, out=c_r)
+            g = timer.graph([launch16(i) for i in range(args.launches)])
+            us16 = timer.replay_ms(g, reps=3) * 1e3 / args.launches
+            del g, cold
+            Bm, Fm = algo_bytes(m, N, K), algo_flops(m, N, K)
+            sweep["a16w4"].append({"workload": HEADLINE, "N": N, "K": K, "M": m, "us": round(us16, 3),
+                                   "tflops": round(Fm / us16 / 1e6, 2), "gbps": round(Bm / us16 / 1e3, 1),
+                                   "frac_hbm": round(Bm / HBM_PEAK * 1e6 / us16, 4),
+                                   "frac_mfma_bf16": round(Fm / MFMA_BF16_PEAK * 1e6 / us16, 4),
+                                   "kernel": "k_gemm_a16w4 (64 x 256 tiles)"})
+            log(f"  a16w4 {HEADLINE} M={m}: {us16:.2f} us cold")
         if not args.no_grouped:
             sweep["grouped"] = grouped_sweep(torch, mx, W, timer)
 

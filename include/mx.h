@@ -128,6 +128,17 @@ mx_status mx_a4w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int
                        hipStream_t stream);
 
 /*
+ * A16WFP4 variant (named in "[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", CI Guide, as
+ * outside that change): C[M, N] = A[M, K] x W^T with the bf16 activations NOT quantized and
+ * W the prepared MXFP4 weight decoded to real values (E2M1 value x 2^(scale - 127), exact
+ * in bf16; weight blocks with scale byte 0, block amax below 2^-125, may decode to zero);
+ * FP32 accumulation on the bf16 MFMA, bf16 output (round to nearest even); rows >= M are
+ * untouched. Same arguments, shape rules and errors as mx_a4w4_gemm, without a workspace.
+ */
+mx_status mx_a16w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int64_t M,
+                        int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * Grouped MoE GEMM1 (expert-segmented dense GEMM, "[HIP] [CK] [FlyDSL] [Kernel] Extend
  * MXFP4 GEMM1 replacement to A4W4", Summary; shape of "[gfx1250] Fuse A4W4 stage1 FP4
  * quantization", Performance). Output row r (expert-sorted order) is

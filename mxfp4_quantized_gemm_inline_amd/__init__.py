@@ -38,6 +38,7 @@ SIGNATURES = {
     "mx_a4w4_gemm_grouped_mx": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]),
     "mx_a4w4_gemm_grouped_mx_plan": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
     "mx_moe_combine": (_c_int, [_vp, _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
+    "mx_a16w4_gemm": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]),
     "mx_calib_read": (_c_int, [_vp, _c_sz, _c_i64, _vp, _vp]),
     "mx_calib_mfma": (_c_int, [_c_i64, _c_i64, _vp, _vp]),
     "mx_calib_mfma_flops": (ctypes.c_double, [_c_i64, _c_i64]),
@@ -287,6 +288,19 @@ def mx_moe_combine(y_bf16, token_rows, token_weights, out=None, stream=None):
     return o
 
 
+def mx_a16w4_gemm(a_bf16, w_prep, N: int, out=None, stream=None):
+    """A16WFP4: A [M, K] bf16 (not quantized) x decoded prepared weight -> C [M, N] bf16."""
+    torch = _torch()
+    M, K = a_bf16.shape
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_bf16.device)
+    if M == 0:
+        return c
+    _check(lib().mx_a16w4_gemm(_dev(a_bf16, torch.bfloat16, "a_bf16"), _dev(w_prep, torch.uint8, "w_prep"),
+                               _dev(c, torch.bfloat16, "c_bf16"), M, int(N), K, _stream_ptr(stream)),
+           "mx_a16w4_gemm")
+    return c
+
+
 def mx_a4w4_gemm_plan(M: int, N: int, K: int, workspace_bytes=None) -> str:
     """Kernel(s) mx_a4w4_gemm launches for this shape; workspace_bytes defaults to what
     mx_a4w4_gemm allocates when given no workspace."""
@@ -336,6 +350,6 @@ __all__ = [
     "mx_prepare_weight_packed", "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
     "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_a4w4_gemm_grouped_act_quant",
     "mx_a4w4_gemm_grouped_act_quant_plan", "mx_a4w4_gemm_grouped_mx", "mx_a4w4_gemm_grouped_mx_plan",
-    "mx_moe_combine", "MX_ACT_SILU", "MX_ACT_SWIGLU", "mx_calib_read", "mx_calib_mfma",
+    "mx_moe_combine", "mx_a16w4_gemm", "MX_ACT_SILU", "MX_ACT_SWIGLU", "mx_calib_read", "mx_calib_mfma",
     "mx_calib_mfma_flops",
 ]

@@ -1,0 +1,159 @@
+// mx_a16w4.hip - the A16WFP4 variant: bf16 activations, unquantized, times the prepared
+// MXFP4 weight decoded to bf16, on the gfx950 bf16 MFMA (16x16x32), FP32 accumulation,
+// bf16 output ("[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", CI Guide, names the
+// variant as outside that change; the weight is the same prepared blob).
+//
+// Tile: BM = 64 rows x BN = 256 columns, four waves side by side along N, each 64 x 64
+// (four 16-row tiles x four 16-column groups). Per 128-wide K step the CTA's bf16
+// activation tile (64 x 128, 16 KiB) goes to LDS, double buffered, its 16-byte chunks
+// XOR-swizzled by row so the operand reads are conflict-free; each wave loads its weight
+// operands (1 KiB per column group, as for the A4W4 kernels) and scale word straight into
+// registers and decodes them with v_cvt_scalef32_pk_bf16_fp4.
+//
+// K order inside a step: MFMA j (0..3) takes, from lane quarter q, the step's elements
+// 32q + 8j .. 32q + 8j + 7 for both operands (a common permutation of k leaves every sum
+// unchanged), so the 32 codes a lane loads for its column and 32-block are already in
+// operand position: sub-chunk j of the block is bytes 4j .. 4j+3.
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "mx_device.h"
+#include "mx_internal.h"
+
+namespace mx {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kA16BM = 64, kA16BN = 256, kA16Threads = 256;
+constexpr int kA16Row = 256;                                   // bytes of one staged activation row (128 bf16)
+constexpr int kA16Stage = 2 * kA16BM * kA16Row;                // double-buffered activation tile
+constexpr int kA16CRow = kA16BN * 2 + 16;                      // bf16 output staging row, padded
+constexpr int kA16Smem = kA16Stage > kA16BM * kA16CRow ? kA16Stage : kA16BM * kA16CRow;
+
+__device__ __forceinline__ int a16_chunk(int row, int chunk) { return chunk ^ (row & 15); }
+
+__global__ __launch_bounds__(kA16Threads, 2) void k_gemm_a16w4(const uint16_t* __restrict__ A,
+                                                               const uint8_t* __restrict__ Wp,
+                                                               uint16_t* __restrict__ C, int M, int N, int K) {
+  __shared__ __align__(16) uint8_t smem[kA16Smem];
+  const int T = K / kStepK, G = N / 16;
+  const int tiles_m = (M + kA16BM - 1) / kA16BM, tiles_n = N / kA16BN;
+  // XCD-aware order: blocks are dealt round-robin to the 8 XCDs; each XCD walks a
+  // contiguous share of the tiles, eight row tiles at a time down a column of tiles.
+  const int total = tiles_m * tiles_n, x = blockIdx.x % 8, q8 = total / 8, r8 = total % 8;
+  const int logical = x * q8 + min(x, r8) + (int)blockIdx.x / 8;
+  const int grp = logical / (8 * tiles_n), first = grp * 8, gm = min(tiles_m - first, 8);
+  const int rem = logical - grp * 8 * tiles_n;
+  const int bm = first + rem % gm, bn = rem / gm;
+  const int m0 = bm * kA16BM, Mrows = min(kA16BM, M - m0);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gw0 = bn * (kA16BN / 16) + w * 4;                  // first of this wave's four column groups
+  const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
+
+  // activation loads: thread -> row tid/4 (clamped into the valid rows), 32-block tid%4
+  const int ar = tid >> 2, ab = tid & 3;
+  const uint16_t* arow = A + (size_t)(m0 + min(ar, Mrows - 1)) * K + ab * kBlock;
+  const uint8_t* wb[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) wb[g] = Wp + (size_t)min(gw0 + g, G - 1) * T * 1024 + lane * 16;
+  const uint8_t* sb = Wsc + (size_t)min(gw0 >> 2, G / 4 - 1) * T * 256 + lane * 4;
+
+  uint32_t xa[16];
+  uint4 wq[2][4];
+  uint32_t ws[2];
+  auto load = [&](int t, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    load_block(arow + (size_t)t * kStepK, xa);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) wq[SL][g] = *reinterpret_cast<const uint4*>(wb[g] + (size_t)t * 1024);
+    ws[SL] = *reinterpret_cast<const uint32_t*>(sb + (size_t)t * 256);
+  };
+  auto sa = [&](int buf, int row, int chunk) { return smem + buf * kA16BM * kA16Row + row * kA16Row + 16 * a16_chunk(row, chunk); };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // step t: weights of step t in slot SL (compile time), activations of step t in xa
+  auto step = [&](int t, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const int buf = t & 1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint4*>(sa(buf, ar, 4 * ab + c)) = make_uint4(xa[4 * c], xa[4 * c + 1], xa[4 * c + 2], xa[4 * c + 3]);
+    load(min(t + 1, T - 1), std::integral_constant<int, SL ^ 1>{});  // past the end: a harmless re-load
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 bop[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        bop[mt] = *reinterpret_cast<const uint4*>(sa(buf, 16 * mt + (lane & 15), 4 * (lane >> 4) + j));
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t s = (ws[SL] >> (8 * g)) & 0xffu;
+        const float sc = __builtin_bit_cast(float, s ? (s << 23) : 0x00400000u);
+        const uint32_t codes = j == 0 ? wq[SL][g].x : j == 1 ? wq[SL][g].y : j == 2 ? wq[SL][g].z : wq[SL][g].w;
+        uint32_t d[4];
+        d[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+        d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+        d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+        d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+        const bf16x8 aop = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[g][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bop[mt]), acc[g][mt],
+                                                               0, 0, 0);
+      }
+    }
+    __syncthreads();  // the buffer written two steps on is free only once every wave has read it
+  };
+
+  load(0, std::integral_constant<int, 0>{});
+  int t = 0;
+  for (; t + 2 <= T; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
+  }
+  if (t < T) step(t, std::integral_constant<int, 0>{});
+
+  // Epilogue: lane l holds C[m = 16 mt + l % 16][n = 16 g + 4 (l / 16) .. + 3] of its wave's
+  // columns; stage the tile as bf16 in LDS, then write whole rows 16 bytes per lane.
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int r = 16 * mt + (lane & 15), cl = 16 * (w * 4 + g) + 4 * (lane >> 4);
+      *reinterpret_cast<uint2*>(smem + r * kA16CRow + cl * 2) =
+          pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
+    }
+  __syncthreads();
+  const int n0 = bn * kA16BN;
+#pragma unroll
+  for (int i = 0; i < kA16BM * (kA16BN / 8) / kA16Threads; ++i) {
+    const int id = tid + i * kA16Threads;
+    const int r = id / (kA16BN / 8), ch = id % (kA16BN / 8);
+    if (r < Mrows) {
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + r * kA16CRow + ch * 16);
+      *reinterpret_cast<uint4*>(C + (size_t)(m0 + r) * N + n0 + 8 * ch) = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_a16w4(const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t tiles = ((M + kA16BM - 1) / kA16BM) * (N / kA16BN);
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gemm_a16w4, dim3((unsigned)tiles), dim3(kA16Threads), 0, st, static_cast<const uint16_t*>(a),
+                     static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -120,6 +120,17 @@ mx_status mx_a4w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int
   return from_hip(mx::launch_gemm(a_bf16, w_prep, c_bf16, M, N, K, workspace, workspace_bytes, stream));
 }
 
+mx_status mx_a16w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int64_t M, int64_t N, int64_t K,
+                        hipStream_t stream) {
+  if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (M == 0) return MX_OK;
+  if (!a_bf16 || !w_prep || !c_bf16) return MX_ERR_NULL;
+  if (!aligned16(a_bf16) || !aligned16(w_prep) || !aligned16(c_bf16)) return MX_ERR_ALIGN;
+  mx_status d = check_device();
+  if (d != MX_OK) return d;
+  return from_hip(mx::launch_a16w4(a_bf16, w_prep, c_bf16, M, N, K, stream));
+}
+
 mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token, const int32_t* expert_offsets,
                                int64_t E, int64_t R_max, const void* w_prep_stacked, void* c_bf16,
                                int64_t T, int64_t N, int64_t K, int64_t rows_hint, hipStream_t stream) {

@@ -231,3 +231,15 @@ def test_gemm2_and_combine_argument_errors_and_plan(monkeypatch):
     assert mx.mx_a4w4_gemm_grouped_mx_plan(3584, 768, 73) == "k_gemm_grouped_tile_mx<1, 8, 8, 4, 1, 2>"
     assert mx.mx_a4w4_gemm_grouped_mx_plan(3584, 768, 5) == "k_gemm_grouped_tile_mx<1, 4, 4, 4, 2, 2>"
     assert mx.mx_a4w4_gemm_grouped_mx_plan(768, 768, 73) == "k_gemm_grouped_tile_mx<1, 4, 4, 4, 2, 2>"
+
+
+def test_a16w4_argument_errors():
+    f = mx.lib().mx_a16w4_gemm
+    assert f(A, B, Cp, 0, 256, 256, None) == mx.MX_OK              # M = 0: no-op
+    assert f(A, B, Cp, -1, 256, 256, None) == mx.MX_ERR_SHAPE
+    assert f(A, B, Cp, 4, 300, 256, None) == mx.MX_ERR_SHAPE
+    assert f(A, B, Cp, 4, 256, 200, None) == mx.MX_ERR_SHAPE
+    assert f(None, B, Cp, 4, 256, 256, None) == mx.MX_ERR_NULL
+    assert f(A, None, Cp, 4, 256, 256, None) == mx.MX_ERR_NULL
+    assert f(A, B, None, 4, 256, 256, None) == mx.MX_ERR_NULL
+    assert f(MIS, B, Cp, 4, 256, 256, None) == mx.MX_ERR_ALIGN
