@@ -732,6 +732,174 @@ void k_gemm_tile(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp,
   tile_core<WM, WN, MT, NG, PF>(rows, min(S::BM, M - m0), Wp, C + (size_t)m0 * N, Pout, N, K, bn, tb, te, smem);
 }
 
+// ====================================================================== short-K sweep GEMM (large M)
+//
+// When K is at most eight 128-wide steps, a CTA's activation rows fit the LDS whole once
+// quantized (BM x K/2 payload bytes and BM x K/32 scale bytes: 68 KiB for 128 rows at
+// K = 1024). A CTA then quantizes its BM rows over the whole K once and sweeps J adjacent
+// column tiles of BN columns. Inside a column tile the waves only read activation
+// operands from LDS and stream their weight operands from global memory; the weight
+// stream runs PF steps ahead without a break at column-tile boundaries, so the K loop
+// holds no barrier. Each tile's bf16 output is staged in one of two LDS buffers and
+// stored while the next tiles' MFMAs run. Vector-memory stores and loads retire in issue
+// order, so a load issued after a tile's stores cannot be waited on before those stores
+// complete: with PF beyond one tile's steps, the first such wait comes PF - T steps into
+// the tile after next.
+//
+// LDS: activation payload [T][16-row tile][1 KiB operand block] (the XOR-swizzled operand
+// layout of tile_core), scales [T][operand lane][16-row tile] bytes, then two output
+// staging buffers [BM][BN + 8] bf16.
+template <int WM, int WN, int MT, int NG, int T, int PF>
+struct SweepShape {
+  static constexpr int MTC = MT * WM, BM = 16 * MTC, BN = 16 * NG * WN, NW = WM * WN, NTH = 64 * NW;
+  static constexpr int IPW = T * MTC / NW;  // (step, 16-row tile) items each wave quantizes
+  static constexpr int AQ = T * MTC * 1024, AS = T * 64 * MTC;
+  static constexpr int CROW = BN * 2 + 16, CS = BM * CROW;
+  static constexpr int SMEM = AQ + AS + 2 * CS;
+  static constexpr int R = PF + 1;  // weight register slots, indexed by the flattened step
+  static_assert((T * MTC) % NW == 0, "every wave quantizes the same number of items");
+  static_assert(MT == 4, "a wave's four row tiles share one activation scale word");
+  static_assert(NG == 2 || NG == 4, "a wave's column groups sit in one weight scale word");
+  static_assert(SMEM <= 160 * 1024, "the quantized rows and the output staging fit the LDS");
+};
+
+template <int WM, int WN, int MT, int NG, int T, int PF, int J>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void k_gemm_sweep(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
+                  int M, int N, int GM) {
+  using S = SweepShape<WM, WN, MT, NG, T, PF>;
+  constexpr int MTC = S::MTC, BM = S::BM, BN = S::BN, NW = S::NW, NTH = S::NTH, R = S::R;
+  constexpr int K = T * kStepK;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint8_t* const aq = smem;
+  uint8_t* const as = smem + S::AQ;
+  uint8_t* const cs0 = smem + S::AQ + S::AS;
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN, chunks = (tiles_n + J - 1) / J;
+  int bm, ch;
+  tile_coords(blockIdx.x, tiles_m * chunks, tiles_m, chunks, GM, bm, ch);
+  const int m0 = bm * BM, Mrows = min(BM, M - m0), bn0 = ch * J;
+  const int bn_last = min(bn0 + J, tiles_n) - 1;  // weight loads past it re-read it
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / WN, wn = w % WN;
+
+  // Weight operands of flattened step u = j T + t (column tile bn0 + j, step t): NG 1 KiB
+  // payload tiles and the scale word of their column-group quad. The wave's groups start
+  // at byte (wn NG) % 4 of that word; the shift that brings them to byte 0 is applied
+  // where the word is used, so no arithmetic waits on a load in flight.
+  const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
+  const int sshift = 8 * ((wn * NG) & 3);
+  uint4 wq[R][NG];
+  uint32_t wsw[R];
+  auto load_w = [&](int u, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    const int bn = min(bn0 + u / T, bn_last), t = u % T;
+    const int gw0 = bn * (BN / 16) + wn * NG;
+    const uint8_t* p = Wp + ((size_t)gw0 * T + t) * 1024 + lane * 16;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) wq[SL][g] = *reinterpret_cast<const uint4*>(p + (size_t)g * T * 1024);
+    wsw[SL] = *reinterpret_cast<const uint32_t*>(Wsc + ((size_t)(gw0 >> 2) * T + t) * 256 + lane * 4);
+  };
+
+  static_for<PF>([&](auto p) { load_w((int)decltype(p)::value, p); });
+
+  // Quantize: item i = (step t, 16-row tile) = (i / MTC, i % MTC); lane 4r + j takes the
+  // 32-block j of row r of that tile at that step. All of a wave's loads are issued before
+  // the first block is quantized. Rows past Mrows re-read the last valid row and are never
+  // stored.
+  auto swz = [](int rr) { return ((rr >> 1) ^ (rr >> 2)) & 3; };  // tile_core's operand swizzle
+  {
+    const uint32_t st_off = (uint32_t)(((lane >> 2) * 4 + ((lane & 3) ^ swz(lane >> 2))) * 16);
+    const uint32_t st_sc = (uint32_t)(((lane >> 2) + 16 * (lane & 3)) * MTC);
+    const uint8_t* abase = reinterpret_cast<const uint8_t*>(A) + (size_t)m0 * K * 2;
+    uint32_t x[S::IPW][16];
+#pragma unroll
+    for (int k = 0; k < S::IPW; ++k) {
+      const int it = w + NW * k, t = it / MTC, tile = it % MTC;
+      const int r = min(16 * tile + (lane >> 2), Mrows - 1);
+      load_block_at(abase, (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(t * kStepK * 2 + (lane & 3) * 64), x[k]);
+    }
+    // keep every load ahead of the first quantization (the scheduler would otherwise
+    // interleave them and serialize their latencies)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < S::IPW; ++k) {
+      const int it = w + NW * k, t = it / MTC, tile = it % MTC;
+      uint32_t q[4];
+      const uint32_t sc = quant_block(x[k], q);
+      *reinterpret_cast<uint4*>(aq + (t * MTC + tile) * 1024 + st_off) = make_uint4(q[0], q[1], q[2], q[3]);
+      as[t * 64 * MTC + st_sc + tile] = (uint8_t)sc;
+    }
+  }
+  __syncthreads();
+
+  const uint32_t ld_off = (uint32_t)(((lane & 15) * 4 + ((lane >> 4) ^ swz(lane & 15))) * 16);
+  // Every CTA runs all J column tiles: one past the last column tile (a partial last
+  // chunk) is computed from re-read weights and not stored. A guard around the whole tile
+  // would make the loads inside it join with their skipped paths and wait there.
+  static_for<J>([&](auto j_c) {
+    constexpr int j = decltype(j_c)::value;
+    const int bn = bn0 + j;
+    {
+      v4f acc[NG][MT];
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+      static_for<T>([&](auto t_c) {
+        constexpr int t = decltype(t_c)::value, u = j * T + t;
+        // a step boundary the scheduler may not cross: it would sink each prefetch down to
+        // its use, PF steps later, and wait on it there
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(u + PF, std::integral_constant<int, (u + PF) % R>{});
+        uint4 b[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          b[mt] = *reinterpret_cast<const uint4*>(aq + (t * MTC + wm * MT + mt) * 1024 + ld_off);
+        const uint32_t sbw = *reinterpret_cast<const uint32_t*>(as + (t * 64 + lane) * MTC + wm * MT);
+        const uint32_t sww = NG == 4 ? wsw[u % R] : wsw[u % R] >> sshift;
+        static_for<NG>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          static_for<MT>([&](auto m_c) {
+            constexpr int mt = decltype(m_c)::value;
+            acc[g][mt] = mfma_fp4_sel<g, mt>(wq[u % R][g], b[mt], acc[g][mt], sww, sbw);
+          });
+        });
+      });
+      // Stage the tile as bf16 in buffer j % 2 (its previous contents, tile j - 2, were read
+      // by every wave before the barrier that followed the staging of tile j - 1), then
+      // store whole rows, 16 bytes per lane; the stores drain under the next tiles.
+      uint8_t* const cs = cs0 + (j & 1) * S::CS;
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int r = 16 * (wm * MT + mt) + (lane & 15);
+          const int cl = 16 * (wn * NG + g) + 4 * (lane >> 4);
+          *reinterpret_cast<uint2*>(cs + r * S::CROW + cl * 2) =
+              pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
+        }
+      __syncthreads();
+      constexpr int CPR = BN / 8, CPT = BM * CPR / NTH;
+      static_assert((BM * CPR) % NTH == 0, "every thread stores the same number of chunks");
+      u32x4 v[CPT];  // all of a thread's LDS reads before its first (row-guarded) store
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int id = threadIdx.x + i * NTH;
+        v[i] = *reinterpret_cast<const u32x4*>(cs + (id / CPR) * S::CROW + (id % CPR) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int id = threadIdx.x + i * NTH;
+        const int r = id / CPR, c16 = id % CPR;
+        if (r < Mrows && bn <= bn_last)
+          __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(C + (size_t)(m0 + r) * N + bn * BN + 8 * c16));
+      }
+    }
+  });
+}
+
 // ====================================================================== grouped MoE GEMM1, tiled
 //
 // For segments of tens of rows or more. Each expert's rows are cut into BM-row tiles and
@@ -1218,6 +1386,8 @@ struct GemmConfig {
   int MT = 1, NG = 1, WK = 4, S = 1;     // streaming kernel (S = K slices)
   int WM = 1, WN = 4, PF = 2, GM = 8;    // tiled kernel (uses MT, NG too)
   int OCC = 1;                           // tiled kernel: minimum waves per SIMD asked of the compiler
+  bool sweep = false;                    // short-K sweep kernel (uses J, GM)
+  int J = 1;                             // sweep kernel: column tiles per CTA
 };
 
 #define MX_STREAM_CONFIGS(X) \
@@ -1226,6 +1396,11 @@ struct GemmConfig {
   X(4, 1, 4) X(4, 1, 8) X(4, 2, 4) X(4, 4, 4) X(8, 1, 4) X(8, 2, 4)
 
 #define MX_WIDE_CONFIGS(X) X(8, 2) X(8, 4) X(4, 4) X(4, 8)
+
+// short-K sweep kernel: (K steps T, weight prefetch depth PF in steps, column tiles per CTA
+// J); the CTA is 8 waves of 64 x 32 (128-row tiles, 128-column tiles)
+#define MX_SWEEP_CONFIGS(X) \
+  X(2, 3, 2) X(2, 3, 4) X(4, 6, 2) X(4, 6, 4) X(6, 9, 2) X(6, 9, 4) X(8, 10, 2) X(8, 10, 4)
 
 #define MX_TILE_CONFIGS(X) \
   X(1, 4, 4, 4, 2, 1) X(2, 4, 4, 4, 2, 1) X(1, 4, 8, 4, 1, 1) X(2, 2, 4, 8, 1, 1) X(1, 4, 4, 2, 2, 1) \
@@ -1319,6 +1494,34 @@ hipError_t run_wide(const void* a, const void* wp, void* c, int M, int N, int K,
   return hipGetLastError();
 }
 
+template <int T, int PF, int J>
+hipError_t run_sweep(const void* a, const void* wp, void* c, int M, int N, int K, int GM, hipStream_t st) {
+  using S = SweepShape<2, 4, 4, 2, T, PF>;
+  if (K != T * kStepK || N % S::BN != 0) return hipErrorInvalidValue;
+  auto kern = k_gemm_sweep<2, 4, 4, 2, T, PF, J>;
+  static std::atomic<uint64_t> configured{0};
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), configured);
+  if (e != hipSuccess) return e;
+  const int64_t grid = (int64_t)((M + S::BM - 1) / S::BM) * ((N / S::BN + J - 1) / J);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(S::NTH), S::SMEM, st, static_cast<const uint16_t*>(a),
+                     static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), M, N, GM);
+  return hipGetLastError();
+}
+
+bool sweep_supported(int T, int J) {
+#define X(t, pf, j) if (T == t && J == j) return true;
+  MX_SWEEP_CONFIGS(X)
+#undef X
+  return false;
+}
+
+int sweep_pf(int T) {
+#define X(t, pf, j) if (T == t) return pf;
+  MX_SWEEP_CONFIGS(X)
+#undef X
+  return 0;
+}
+
 bool wide_supported(int MT, int NG) {
 #define X(mt, ng) if (MT == mt && NG == ng) return true;
   MX_WIDE_CONFIGS(X)
@@ -1343,6 +1546,13 @@ bool tile_supported(const GemmConfig& c) {
 
 hipError_t run_config(const GemmConfig& c, const void* a, const void* wp, void* out, float* P, int M,
                       int N, int K, hipStream_t st) {
+  if (c.sweep) {
+    const int T = steps_of(K);
+#define X(t, pf, j) if (T == t && c.J == j) return run_sweep<t, pf, j>(a, wp, out, M, N, K, c.GM, st);
+    MX_SWEEP_CONFIGS(X)
+#undef X
+    return hipErrorInvalidValue;
+  }
   if (c.wide) {
 #define X(mt, ng) if (c.MT == mt && c.NG == ng) return run_wide<mt, ng>(a, wp, out, M, N, K, c.GM, st);
     MX_WIDE_CONFIGS(X)
@@ -1422,6 +1632,13 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   // tiled kernel: 64 x 256 tiles when there are enough of them (two steps of prefetch only
   // for long K at moderate sizes), else 64 x 128 tiles at one CTA per SIMD set
   c.tile = true;
+  // short K and enough rows: each 128-row tile quantized once and swept over four 128-column
+  // tiles, when that still gives about 200 CTAs or more (N=7168, K=768, M=2048: 224)
+  const int64_t sweeps = (int64_t)((M + 127) / 128) * ((N / 128 + 3) / 4);
+  if (sweep_supported(T, 4) && sweeps >= 200) {
+    c.sweep = true; c.J = 4; c.GM = 8;
+    return c;
+  }
   // 128 x 512 tiles (eight waves of 128 x 64) halve the load instructions per output; they
   // pay when one round of them (at most one per CU) nearly fills the chip
   const int64_t tiles512 = (int64_t)((M + 127) / 128) * (N / 512);
@@ -1455,7 +1672,7 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
 }
 
 // Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming), "t,WM,WN,MT,NG,PF,GM[,OCC[,S]]" (tiled,
-// S = K slices) or "w,MT,NG,GM" (wide-tile)
+// S = K slices), "k,J,GM" (short-K sweep, J column tiles per CTA) or "w,MT,NG,GM" (wide-tile)
 // replaces the default choice. Returns 0 when unset, 1 when applied, -1 when the string
 // does not name a compiled configuration (the call then fails rather than silently
 // running something else).
@@ -1467,6 +1684,8 @@ int override_config(GemmConfig& c) {
   if (e[0] == 's' && std::sscanf(e, "s,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) == 4) {
     o.tile = false; o.MT = v[0]; o.NG = v[1]; o.WK = v[2]; o.S = v[3];
     if (!stream_supported(o.MT, o.NG, o.WK) || o.S < 1) return -1;
+  } else if (e[0] == 'k' && std::sscanf(e, "k,%d,%d", &v[0], &v[1]) == 2) {
+    o.tile = true; o.sweep = true; o.J = v[0]; o.GM = v[1] < 1 ? 1 : v[1];
   } else if (e[0] == 'w' && std::sscanf(e, "w,%d,%d,%d", &v[0], &v[1], &v[2]) == 3) {
     o.tile = true; o.wide = true; o.MT = v[0]; o.NG = v[1]; o.GM = v[2] < 1 ? 1 : v[2];
     if (!wide_supported(o.MT, o.NG)) return -1;
@@ -1501,6 +1720,7 @@ bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
   cfg = select_config(M, N, K, ws_bytes);
   const int ov = override_config(cfg);
   if (ov < 0) return false;
+  if (ov > 0 && cfg.sweep && (!sweep_supported(steps_of(K), cfg.J) || N % 128 != 0)) return false;
   if (ov > 0 && cfg.tile && !cfg.wide && cfg.S > 1) {
     const int T = steps_of(K);
     if (cfg.S > T) cfg.S = T;
@@ -1533,7 +1753,10 @@ bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf
   const int M = (int)M64, N = (int)N64, K = (int)K64;
   GemmConfig c;
   if (!resolve_config(M, N, K, ws_bytes, c)) return false;
-  if (c.wide) {
+  if (c.sweep) {
+    const int T = steps_of(K);
+    std::snprintf(buf, len, "k_gemm_sweep<2, 4, 4, 2, %d, %d, %d> GM=%d", T, sweep_pf(T), c.J, c.GM);
+  } else if (c.wide) {
     std::snprintf(buf, len, "k_gemm_wide<%d, %d> GM=%d", c.MT, c.NG, c.GM);
   } else if (c.tile) {
     const int T = steps_of(K), TS = (T + c.S - 1) / c.S, S = (T + TS - 1) / TS;  // as run_tile slices

@@ -121,7 +121,9 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     monkeypatch.delenv("MX_GEMM_CONFIG", raising=False)
     assert mx.mx_a4w4_gemm_plan(0, 7168, 768) == "none"
     assert mx.mx_a4w4_gemm_plan(1, 7168, 768).startswith("k_gemm_stream<1, ")
-    assert mx.mx_a4w4_gemm_plan(2048, 7168, 768) == "k_gemm_tile<1, 8, 8, 4, 1, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 768) == "k_gemm_sweep<2, 4, 4, 2, 6, 9, 4> GM=8"
+    assert mx.mx_a4w4_gemm_plan(1024, 7168, 768) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_gemm_tile<1, 8, 8, 4, 1, 2> GM=8"
     assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
     # split K only with a workspace; the streaming kernels never need one otherwise
     with_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168)
@@ -132,6 +134,16 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     monkeypatch.setenv("MX_GEMM_CONFIG", "t,9,9,9,9,9,9")
     with pytest.raises(mx.MxError):
         mx.mx_a4w4_gemm_plan(64, 7168, 768)
+    # the short-K sweep kernel exists for 2, 4, 6 and 8 steps of K and one or two column tiles
+    monkeypatch.setenv("MX_GEMM_CONFIG", "k,2,8")
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 768) == "k_gemm_sweep<2, 4, 4, 2, 6, 9, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(300, 768, 256) == "k_gemm_sweep<2, 4, 4, 2, 2, 3, 2> GM=8"
+    for K in (384, 4224):
+        with pytest.raises(mx.MxError):
+            mx.mx_a4w4_gemm_plan(2048, 7168, K)
+    monkeypatch.setenv("MX_GEMM_CONFIG", "k,3,8")
+    with pytest.raises(mx.MxError):
+        mx.mx_a4w4_gemm_plan(2048, 7168, 768)
 
 
 def test_grouped_plan_names_the_selected_kernel(monkeypatch):

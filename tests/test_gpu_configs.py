@@ -24,6 +24,7 @@ TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8,
         (1, 4, 4, 4, 1, 2), (1, 4, 4, 4, 2, 2), (2, 4, 4, 4, 1, 1), (1, 4, 4, 2, 2, 2),
         (1, 8, 8, 4, 1, 2)]
 WIDE = [(8, 2), (8, 4), (4, 4), (4, 8)]
+SWEEP_K = (256, 512, 768, 1024)  # the short-K sweep kernel's compiled step counts 2, 4, 6, 8
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
 K_TESTS = (4224, 768)  # 33 and 6 steps of 128
 LDS_MAX = 160 * 1024
@@ -113,6 +114,42 @@ def test_wide_config(cfg, K):
         c = _run(f"w,{cfg[0]},{cfg[1]},{gm}", a[:M], wp, False)
         torch.cuda.synchronize()
         check_gemm(c, exact[:M], what=f"wide {cfg} GM={gm} M={M} K={K}")
+
+
+@pytest.mark.parametrize("K", SWEEP_K)
+@pytest.mark.parametrize("J", (2, 4))
+def test_sweep_config(J, K):
+    """The short-K sweep kernel (each 128-row tile quantized once, J column tiles of 128 per
+    CTA): a ragged last row tile (300 = 2 x 128 + 44; 37 rows alone), a CTA with only some
+    of its column tiles (N = 768 = 6 x 128 with J = 4), several tile orders, and canary
+    rows past M that must stay untouched."""
+    torch = torch_or_skip()
+    a, wp, exact = _case(K)
+    for M, gm in ((300, 8), (37, 1), (256, 3)):
+        full = torch.full((M + 5, N_TEST), -7.0, dtype=torch.bfloat16, device="cuda")
+        os.environ["MX_GEMM_CONFIG"] = f"k,{J},{gm}"
+        try:
+            mx = lib_or_fail()
+            mx.mx_a4w4_gemm(dev_bf16(a[:M]), wp, N_TEST, out=full[:M], workspace=False)
+        finally:
+            del os.environ["MX_GEMM_CONFIG"]
+        torch.cuda.synchronize()
+        check_gemm(host_bits(full[:M]), exact[:M], what=f"sweep J={J} GM={gm} M={M} K={K}")
+        assert bool((full[M:] == -7.0).all()), f"sweep J={J} M={M} K={K}: rows past M were written"
+
+
+def test_sweep_rejects_long_k():
+    """The sweep kernel holds a row tile's whole K in LDS: an override at K = 4224 (33
+    steps, not compiled) fails instead of running."""
+    torch_or_skip()
+    mx = lib_or_fail()
+    a, wp, _ = _case(4224)
+    os.environ["MX_GEMM_CONFIG"] = "k,2,8"
+    try:
+        with pytest.raises(mx.MxError):
+            mx.mx_a4w4_gemm(dev_bf16(a[:64]), wp, N_TEST, workspace=False)
+    finally:
+        del os.environ["MX_GEMM_CONFIG"]
 
 
 def test_invalid_override_fails_loudly():
