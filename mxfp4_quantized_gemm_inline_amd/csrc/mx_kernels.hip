@@ -911,8 +911,34 @@ void k_gemm_sweep(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp
 // CTAs exit. One expert's units are consecutive and dealt to one XCD (as in tile_coords),
 // so its column tiles share the gathered rows and its row tiles the weight in that L2.
 // The unit (expert, row tile, column tile) of this CTA: the grid is an upper bound on the
-// units; the CTA ranks the experts' unit counts with a block scan (s_scan: NTH ints, s_unit:
+// units; the CTA ranks the experts' unit counts with a wave-shuffle scan (s_scan: an int per wave, s_unit:
 // 4 ints of LDS) and finds its own. False for a surplus CTA. Every value is CTA-uniform.
+// Exclusive prefix sum, in thread order, of v over the CTA's NTH threads; `total` receives
+// the CTA-wide sum. Each wave scans with lane shuffles (no barrier), then the wave totals
+// meet in s_w (one int per wave) behind one barrier. Every thread must call it.
+template <int NTH>
+__device__ __forceinline__ int cta_exclusive_scan(int v, int* s_w, int& total) {
+  constexpr int NW = NTH / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_w[w] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int t = s_w[i];
+    before += i < w ? t : 0;
+    total += t;
+  }
+  return before + x - v;
+}
+
 struct GroupedUnit {
   int e, r0, Mrows, bn;
 };
@@ -932,17 +958,10 @@ __device__ __forceinline__ bool grouped_unit(const int32_t* __restrict__ offs, i
     const int e = tid * ept + i;
     if (e < E) { int lo, hi; seg(e, lo, hi); local += (hi - lo + BM - 1) / BM * tiles_n; }
   }
-  s_scan[tid] = local;
   if (tid == 0) s_unit[0] = -1;
-  __syncthreads();
-  for (int d = 1; d < NTH; d <<= 1) {
-    const int v = (tid >= d) ? s_scan[tid - d] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
+  int all_units;
   {
-    int u = s_scan[tid] - local;  // units before this thread's experts
+    int u = cta_exclusive_scan<NTH>(local, s_scan, all_units);  // units before this thread's experts
     if (L >= u && L < u + local) {
       for (int i = 0; i < ept; ++i) {
         const int e = tid * ept + i;
@@ -1264,17 +1283,10 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_grouped(const uint16_t* __rest
     const int e = tid * ept + i;
     if (e < E) { int lo, hi; seg(e, lo, hi); local += (hi > lo); }
   }
-  s_scan[tid] = local;
   if (tid == 0) s_e = -1;
-  __syncthreads();
-  for (int d = 1; d < NTH; d <<= 1) {
-    const int v = (tid >= d) ? s_scan[tid - d] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
+  int all_active;
   {
-    int rank = s_scan[tid] - local;  // active segments before this thread's range
+    int rank = cta_exclusive_scan<NTH>(local, s_scan, all_active);  // active segments before this thread's range
     if (a >= rank && a < rank + local) {
       for (int i = 0; i < ept; ++i) {
         const int e = tid * ept + i;
