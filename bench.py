@@ -467,7 +467,7 @@ def main():
                                    "tflops": round(Fm / us16 / 1e6, 2), "gbps": round(Bm / us16 / 1e3, 1),
                                    "frac_hbm": round(Bm / HBM_PEAK * 1e6 / us16, 4),
                                    "frac_mfma_bf16": round(Fm / MFMA_BF16_PEAK * 1e6 / us16, 4),
-                                   "kernel": "k_gemm_a16w4 (64 x 256 tiles)"})
+                                   "kernel": mx.mx_a16w4_gemm_plan(m, N, K)})
             log(f"  a16w4 {HEADLINE} M={m}: {us16:.2f} us cold")
         if not args.no_grouped:
             sweep["grouped"] = grouped_sweep(torch, mx, W, timer)

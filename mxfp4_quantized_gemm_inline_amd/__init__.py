@@ -29,6 +29,7 @@ SIGNATURES = {
     "mx_a4w4_gemm_grouped": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _c_i64,
                                       _c_i64, _c_i64, _vp]),
     "mx_a4w4_gemm_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_sz, ctypes.c_char_p, _c_sz]),
+    "mx_a16w4_gemm_plan": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
     "mx_a4w4_gemm_grouped_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_char_p,
                                            _c_sz]),
     "mx_a4w4_gemm_grouped_act_quant": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _c_i64,
@@ -312,6 +313,13 @@ def mx_a4w4_gemm_plan(M: int, N: int, K: int, workspace_bytes=None) -> str:
     return buf.value.decode()
 
 
+def mx_a16w4_gemm_plan(M: int, N: int, K: int) -> str:
+    """Kernel mx_a16w4_gemm launches for this shape."""
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().mx_a16w4_gemm_plan(int(M), int(N), int(K), buf, len(buf)), "mx_a16w4_gemm_plan")
+    return buf.value.decode()
+
+
 def mx_a4w4_gemm_grouped_plan(E: int, R_max: int, T: int, N: int, K: int, rows_hint: int = 1) -> str:
     """Kernel mx_a4w4_gemm_grouped launches for this table size, token count and hint."""
     buf = ctypes.create_string_buffer(256)
@@ -348,7 +356,7 @@ __all__ = [
     "LIB_PATH", "MxError", "lib", "status_string", "mx_prepared_layout_version",
     "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
     "mx_prepare_weight_packed", "mx_unprepare_weight", "mx_quant_act", "mx_a4w4_gemm", "mx_a4w4_gemm_grouped",
-    "mx_a4w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_a4w4_gemm_grouped_act_quant",
+    "mx_a4w4_gemm_plan", "mx_a16w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_a4w4_gemm_grouped_act_quant",
     "mx_a4w4_gemm_grouped_act_quant_plan", "mx_a4w4_gemm_grouped_mx", "mx_a4w4_gemm_grouped_mx_plan",
     "mx_moe_combine", "mx_a16w4_gemm", "MX_ACT_SILU", "MX_ACT_SWIGLU", "mx_calib_read", "mx_calib_mfma",
     "mx_calib_mfma_flops",

@@ -223,6 +223,13 @@ mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t N, int64_t K, int32_t act,
   return MX_OK;
 }
 
+mx_status mx_a16w4_gemm_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
+  if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (!buf || buf_len == 0) return MX_ERR_NULL;
+  mx::a16w4_plan(M, N, K, buf, buf_len);
+  return MX_OK;
+}
+
 mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_bytes, char* buf, size_t buf_len) {
   if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;

@@ -28,6 +28,7 @@ hipError_t launch_gemm_grouped_mx(const void* aq, const void* as, const int32_t*
 bool grouped_mx_plan(int64_t N, int64_t rows_hint, char* buf, size_t len);
 // A16WFP4: bf16 A [M, K] times the prepared weight decoded to bf16, bf16 C [M, N].
 hipError_t launch_a16w4(const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K, hipStream_t st);
+bool a16w4_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t len);
 hipError_t launch_moe_combine(const void* y, int64_t R, const int32_t* rows, const float* w, int64_t T, int64_t topk,
                               int64_t N, void* out, hipStream_t st);
 // Name the kernel(s) the launchers above would run (false: the tuning override is invalid).

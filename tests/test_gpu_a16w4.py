@@ -1,7 +1,8 @@
 """GPU parity of the A16WFP4 variant (bf16 activations x decoded MXFP4 weight on the bf16
 MFMA) against the oracle (oracle/mx_oracle.py: gemm_a16w4_ref), within the GEMM tolerance
 |gpu - exact| <= 2^-7 |exact| + 1e-3 rms(exact): every output for ragged M over several
-64-row tiles and both K forms (K = 768, 4224), sampled rows at the headline shape
+64-row tiles and both K forms (K = 768, 4224), the decode form (M <= 16) over its launch
+shapes, sampled rows at the headline shape
 (N = 7168, K = 768, M = 2048, the launch the bench times); a one-hot activation probe that
 must reproduce the decoded weight bit for bit; canary rows past M left untouched."""
 import numpy as np
@@ -30,6 +31,26 @@ def test_a16w4_matches_oracle(M, K):
     torch.cuda.synchronize()
     assert np.all(O.bf16_to_f64(c[M:]) == 5.0)
     check_gemm(c[:M], O.gemm_a16w4_ref(a, w), what=f"a16w4 M={M} K={K}")
+
+
+@pytest.mark.parametrize("N,K,M", [(768, 768, 1), (768, 768, 16), (768, 4224, 5), (8192, 256, 3),
+                                   (256, 9216, 2), (8192, 768, 16)])
+def test_a16w4_decode_form_matches_oracle(N, K, M):
+    """The decode form (M <= 16): one and two column groups per CTA, four and eight waves,
+    a K share of 1 to 9 steps per wave (9216 = 72 steps: two prefetch chunks of 8), rows
+    past M neither read as real rows nor written."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    assert mx.mx_a16w4_gemm_plan(M, N, K).startswith("k_gemm_a16w4_stream<")
+    a = W.dense_activation(16, K, "plain", seed=74)[:M]
+    w = W.dense_weight(N, K, seed=75)
+    wp = mx.mx_prepare_weight(dev_bf16(w))
+    out = torch.full((M + 3, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    mx.mx_a16w4_gemm(dev_bf16(a), wp, N, out=out[:M])
+    c = host_bits(out)
+    torch.cuda.synchronize()
+    assert np.all(O.bf16_to_f64(c[M:]) == 5.0)
+    check_gemm(c[:M], O.gemm_a16w4_ref(a, w), what=f"a16w4 decode N={N} K={K} M={M}")
 
 
 def test_a16w4_headline_shape_sampled():
