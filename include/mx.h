@@ -255,7 +255,7 @@ mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t T, int64_t
 mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t N, int64_t K, int32_t act, int64_t rows_hint,
                                               char* buf, size_t buf_len);
 
-/* The same for mx_a4w4_gemm_grouped_mx (its kernel depends on N and the hint). Errors as
+/* The same for mx_a4w4_gemm_grouped_mx (its kernel depends on N, K and the hint). Errors as
  * for mx_a4w4_gemm_grouped_act_quant_plan. */
 mx_status mx_a4w4_gemm_grouped_mx_plan(int64_t N, int64_t K, int64_t rows_hint, char* buf,
                                        size_t buf_len);

@@ -190,7 +190,7 @@ mx_status mx_a4w4_gemm_grouped_mx(const void* a_fp4, const void* a_scale, const 
 mx_status mx_a4w4_gemm_grouped_mx_plan(int64_t N, int64_t K, int64_t rows_hint, char* buf, size_t buf_len) {
   if (!gemm_shape_ok(N, K)) return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;
-  if (!mx::grouped_mx_plan(N, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
+  if (!mx::grouped_mx_plan(N, K, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
     buf[0] = '\0';
     return MX_ERR_HIP;
   }

@@ -25,7 +25,7 @@ bool grouped_act_plan(int64_t N, int act, int64_t rows_hint, char* buf, size_t l
 // Second MoE GEMM on MXFP4 rows (aq [R_max, K/2], as [R_max, K/32]) and the top-k combine.
 hipError_t launch_gemm_grouped_mx(const void* aq, const void* as, const int32_t* offsets, int64_t E, int64_t R_max,
                                   const void* wp, void* c, int64_t N, int64_t K, int64_t rows_hint, hipStream_t st);
-bool grouped_mx_plan(int64_t N, int64_t rows_hint, char* buf, size_t len);
+bool grouped_mx_plan(int64_t N, int64_t K, int64_t rows_hint, char* buf, size_t len);
 // A16WFP4: bf16 A [M, K] times the prepared weight decoded to bf16, bf16 C [M, N].
 hipError_t launch_a16w4(const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K, hipStream_t st);
 bool a16w4_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t len);

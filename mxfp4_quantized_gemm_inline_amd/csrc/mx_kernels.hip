@@ -763,23 +763,20 @@ struct SweepShape {
   static_assert(SMEM <= 160 * 1024, "the quantized rows and the output staging fit the LDS");
 };
 
-template <int WM, int WN, int MT, int NG, int T, int PF, int J>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void k_gemm_sweep(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
-                  int M, int N, int GM) {
+// One CTA's work: Mrows (1..BM) activation rows from `rows` (bf16 rows to quantize, or
+// MXFP4 rows to copy), column tiles bn0 .. bn0 + J - 1 of the prepared weight Wp, output
+// rows at Cout + r * N for r < Mrows; column tiles past bn_last are computed from re-read
+// weights and not stored.
+template <int WM, int WN, int MT, int NG, int T, int PF, int J, class Rows>
+__device__ __forceinline__ void sweep_core(const Rows& rows, int Mrows, const uint8_t* __restrict__ Wp,
+                                           uint16_t* __restrict__ Cout, int N, int bn0, int bn_last,
+                                           uint8_t* smem) {
   using S = SweepShape<WM, WN, MT, NG, T, PF>;
-  constexpr int MTC = S::MTC, BM = S::BM, BN = S::BN, NW = S::NW, NTH = S::NTH, R = S::R;
+  constexpr int MTC = S::MTC, BM = S::BM, NW = S::NW, NTH = S::NTH, R = S::R, BN = S::BN;
   constexpr int K = T * kStepK;
-  extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* const aq = smem;
   uint8_t* const as = smem + S::AQ;
   uint8_t* const cs0 = smem + S::AQ + S::AS;
-
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN, chunks = (tiles_n + J - 1) / J;
-  int bm, ch;
-  tile_coords(blockIdx.x, tiles_m * chunks, tiles_m, chunks, GM, bm, ch);
-  const int m0 = bm * BM, Mrows = min(BM, M - m0), bn0 = ch * J;
-  const int bn_last = min(bn0 + J, tiles_n) - 1;  // weight loads past it re-read it
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / WN, wn = w % WN;
@@ -812,13 +809,21 @@ void k_gemm_sweep(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp
   {
     const uint32_t st_off = (uint32_t)(((lane >> 2) * 4 + ((lane & 3) ^ swz(lane >> 2))) * 16);
     const uint32_t st_sc = (uint32_t)(((lane >> 2) + 16 * (lane & 3)) * MTC);
-    const uint8_t* abase = reinterpret_cast<const uint8_t*>(A) + (size_t)m0 * K * 2;
-    uint32_t x[S::IPW][16];
+    // a lane's block per item: 16 bf16 words, or (already quantized) 4 payload words and the
+    // scale byte
+    constexpr int AW = Rows::kMx ? 5 : 16;
+    uint32_t x[S::IPW][AW];
 #pragma unroll
     for (int k = 0; k < S::IPW; ++k) {
       const int it = w + NW * k, t = it / MTC, tile = it % MTC;
       const int r = min(16 * tile + (lane >> 2), Mrows - 1);
-      load_block_at(abase, (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(t * kStepK * 2 + (lane & 3) * 64), x[k]);
+      if constexpr (Rows::kMx) {
+        const uint4 u = *reinterpret_cast<const uint4*>(rows.q + (size_t)r * (K / 2) + t * (kStepK / 2) + (lane & 3) * 16);
+        x[k][0] = u.x; x[k][1] = u.y; x[k][2] = u.z; x[k][3] = u.w;
+        x[k][4] = rows.s[(size_t)r * (K / kBlock) + t * (kStepK / kBlock) + (lane & 3)];
+      } else {
+        load_block_at(rows.base, (uint32_t)r * (uint32_t)(K * 2) + (uint32_t)(t * kStepK * 2 + (lane & 3) * 64), x[k]);
+      }
     }
     // keep every load ahead of the first quantization (the scheduler would otherwise
     // interleave them and serialize their latencies)
@@ -827,7 +832,13 @@ void k_gemm_sweep(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp
     for (int k = 0; k < S::IPW; ++k) {
       const int it = w + NW * k, t = it / MTC, tile = it % MTC;
       uint32_t q[4];
-      const uint32_t sc = quant_block(x[k], q);
+      uint32_t sc;
+      if constexpr (Rows::kMx) {
+        q[0] = x[k][0]; q[1] = x[k][1]; q[2] = x[k][2]; q[3] = x[k][3];
+        sc = x[k][4];
+      } else {
+        sc = quant_block(x[k], q);
+      }
       *reinterpret_cast<uint4*>(aq + (t * MTC + tile) * 1024 + st_off) = make_uint4(q[0], q[1], q[2], q[3]);
       as[t * 64 * MTC + st_sc + tile] = (uint8_t)sc;
     }
@@ -894,10 +905,25 @@ void k_gemm_sweep(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp
         const int id = threadIdx.x + i * NTH;
         const int r = id / CPR, c16 = id % CPR;
         if (r < Mrows && bn <= bn_last)
-          __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(C + (size_t)(m0 + r) * N + bn * BN + 8 * c16));
+          __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(Cout + (size_t)r * N + bn * BN + 8 * c16));
       }
     }
   });
+}
+
+template <int WM, int WN, int MT, int NG, int T, int PF, int J>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void k_gemm_sweep(const uint16_t* __restrict__ A, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
+                  int M, int N, int GM) {
+  using S = SweepShape<WM, WN, MT, NG, T, PF>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tiles_m = (M + S::BM - 1) / S::BM, tiles_n = N / S::BN, chunks = (tiles_n + J - 1) / J;
+  int bm, ch;
+  tile_coords(blockIdx.x, tiles_m * chunks, tiles_m, chunks, GM, bm, ch);
+  const int m0 = bm * S::BM, bn0 = ch * J;
+  const TileRowsDense rows{reinterpret_cast<const uint8_t*>(A) + (size_t)m0 * (T * kStepK) * 2, T * kStepK};
+  sweep_core<WM, WN, MT, NG, T, PF, J>(rows, min(S::BM, M - m0), Wp, C + (size_t)m0 * N, N, bn0,
+                                       min(bn0 + J, tiles_n) - 1, smem);
 }
 
 // ====================================================================== grouped MoE GEMM1, tiled
@@ -1044,6 +1070,29 @@ void k_gemm_grouped_tile_mx(const uint8_t* __restrict__ Aq, const uint8_t* __res
   const TileRowsMx rows{Aq + (size_t)u.r0 * (K / 2), As + (size_t)u.r0 * (K / kBlock), K};
   tile_core<WM, WN, MT, NG, PF>(rows, u.Mrows, Wall + (size_t)u.e * prepared_bytes(N, K), C + (size_t)u.r0 * N,
                                 nullptr, N, K, u.bn, 0, steps_of(K), smem);
+}
+
+// The second MoE GEMM at short K (at most eight 128-wide steps): the units are (expert,
+// 128-row tile, chunk of J 128-column tiles); each CTA copies its MXFP4 rows into LDS once
+// and sweeps its column tiles (sweep_core), so a unit's lookup, pipeline fill and epilogue
+// are paid once per J column tiles and a tile's stores drain under the next tiles.
+template <int T, int PF, int J>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void k_gemm_grouped_sweep_mx(const uint8_t* __restrict__ Aq, const uint8_t* __restrict__ As,
+                             const int32_t* __restrict__ offs, int E, int R_max, const uint8_t* __restrict__ Wall,
+                             uint16_t* __restrict__ C, int N) {
+  using S = SweepShape<2, 4, 4, 2, T, PF>;
+  constexpr int K = T * kStepK;
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_scan[S::NTH];
+  __shared__ int s_unit[4];
+  const int tiles_n = N / S::BN, chunks = (tiles_n + J - 1) / J;
+  GroupedUnit u;
+  if (!grouped_unit<S::NTH, S::BM>(offs, E, R_max, chunks, s_scan, s_unit, u)) return;
+  const int bn0 = u.bn * J;
+  const TileRowsMx rows{Aq + (size_t)u.r0 * (K / 2), As + (size_t)u.r0 * (K / kBlock), K};
+  sweep_core<2, 4, 4, 2, T, PF, J>(rows, u.Mrows, Wall + (size_t)u.e * prepared_bytes(N, K), C + (size_t)u.r0 * N,
+                                   N, bn0, min(bn0 + J, tiles_n) - 1, smem);
 }
 
 // Top-k weighted combine: out[t, n] = sum_k w[t, k] * y[rows[t, k], n] in FP32 in k order,
@@ -1370,15 +1419,19 @@ namespace {
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per CU (and per workgroup) on gfx950
 
-// Raise a kernel's dynamic-LDS limit to the full 160 KiB once per device. `done` is the
-// caller's per-kernel bitmask of devices already configured.
+// Raise a kernel's dynamic-LDS limit to what the 160 KiB leave beside its static LDS, once
+// per device. `done` is the caller's per-kernel bitmask of devices already configured.
 hipError_t ensure_lds_limit(const void* kern, std::atomic<uint64_t>& done) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
   if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  hipFuncAttributes attr{};
+  e = hipFuncGetAttributes(&attr, kern);
+  if (e != hipSuccess) return e;
+  if (attr.sharedSizeBytes > kMaxLds) return hipErrorInvalidValue;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLds - attr.sharedSizeBytes));
   if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
   return e;
 }
@@ -1989,11 +2042,78 @@ hipError_t launch_gemm_grouped_act(const void* a, const int32_t* row_token, cons
   return hipErrorInvalidValue;
 }
 
+namespace {
+
+// Grouped short-K sweep configurations (T, PF, J), 128 x 128 column tiles.
+#define MX_GROUPED_SWEEP_CONFIGS(X) X(2, 3, 4) X(4, 6, 4) X(6, 9, 4) X(6, 9, 7) X(8, 10, 4)
+
+template <int T, int PF, int J>
+hipError_t run_grouped_sweep_mx(const void* aq, const void* as, const int32_t* offs, int E, int R_max, const void* wp,
+                                void* c, int N, int K, hipStream_t st) {
+  using S = SweepShape<2, 4, 4, 2, T, PF>;
+  if (K != T * kStepK || N % S::BN != 0) return hipErrorInvalidValue;
+  auto kern = k_gemm_grouped_sweep_mx<T, PF, J>;
+  static std::atomic<uint64_t> configured{0};
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), configured);
+  if (e != hipSuccess) return e;
+  const int64_t active = E < R_max ? E : R_max;
+  const int64_t grid = (active + R_max / S::BM) * ((N / S::BN + J - 1) / J);
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(S::NTH), S::SMEM, st, static_cast<const uint8_t*>(aq),
+                     static_cast<const uint8_t*>(as), offs, E, R_max, static_cast<const uint8_t*>(wp),
+                     static_cast<uint16_t*>(c), N);
+  return hipGetLastError();
+}
+
+bool grouped_sweep_supported(int T, int J) {
+#define X(t, pf, j) if (T == t && J == j) return true;
+  MX_GROUPED_SWEEP_CONFIGS(X)
+#undef X
+  return false;
+}
+
+int grouped_sweep_pf(int T) {
+#define X(t, pf, j) if (T == t) return pf;
+  MX_GROUPED_SWEEP_CONFIGS(X)
+#undef X
+  return 0;
+}
+
+// The second GEMM's configuration: the sweep kernel (J > 0) when segments exceed 64 rows and
+// K is a compiled step count (seven column tiles per unit where compiled, else four), the
+// tiled kernel otherwise. Tuning only: MX_GROUPED_CONFIG="gk,J" forces the sweep kernel,
+// "gt,..." a tiled configuration; false when the choice cannot run this call.
+bool resolve_grouped_mx(int N, int K, int64_t rows_hint, GroupedConfig& g, int& J) {
+  const int T = steps_of(K);
+  J = 0;
+  const char* s = std::getenv("MX_GROUPED_CONFIG");
+  if (s && *s && s[0] == 'g' && s[1] == 'k') {
+    if (std::sscanf(s, "gk,%d", &J) != 1) return false;
+    return grouped_sweep_supported(T, J) && N % 128 == 0;
+  }
+  if (!(s && *s) && rows_hint > 64 && N % 128 == 0) {
+    if (grouped_sweep_supported(T, 7)) { J = 7; return true; }
+    if (grouped_sweep_supported(T, 4)) { J = 4; return true; }
+  }
+  return resolve_grouped_act(N, rows_hint, g);
+}
+
+}  // namespace
+
 hipError_t launch_gemm_grouped_mx(const void* aq, const void* as, const int32_t* offsets, int64_t E, int64_t R_max,
                                   const void* wp, void* c, int64_t N, int64_t K, int64_t rows_hint, hipStream_t st) {
   const int e = (int)E, r = (int)R_max, n = (int)N, k = (int)K;
   GroupedConfig g;
-  if (!resolve_grouped_act(n, rows_hint, g)) return hipErrorInvalidValue;
+  int J = 0;
+  if (!resolve_grouped_mx(n, k, rows_hint, g, J)) return hipErrorInvalidValue;
+  if (J > 0) {
+    const int T = steps_of(k);
+#define X(t, pf, j) if (T == t && J == j) return run_grouped_sweep_mx<t, pf, j>(aq, as, offsets, e, r, wp, c, n, k, st);
+    MX_GROUPED_SWEEP_CONFIGS(X)
+#undef X
+    return hipErrorInvalidValue;
+  }
 #define X(wm, wn, mt, ng, pf, occ)                                                          \
   if (g.WM == wm && g.WN == wn && g.MT == mt && g.NG == ng && g.PF == pf && g.OCC == occ)  \
     return run_grouped_tile_mx<wm, wn, mt, ng, pf, occ>(aq, as, offsets, e, r, wp, c, n, k, st);
@@ -2002,9 +2122,15 @@ hipError_t launch_gemm_grouped_mx(const void* aq, const void* as, const int32_t*
   return hipErrorInvalidValue;
 }
 
-bool grouped_mx_plan(int64_t N, int64_t rows_hint, char* buf, size_t len) {
+bool grouped_mx_plan(int64_t N, int64_t K, int64_t rows_hint, char* buf, size_t len) {
   GroupedConfig g;
-  if (!resolve_grouped_act((int)N, rows_hint, g)) return false;
+  int J = 0;
+  if (!resolve_grouped_mx((int)N, (int)K, rows_hint, g, J)) return false;
+  if (J > 0) {
+    const int T = steps_of((int)K);
+    std::snprintf(buf, len, "k_gemm_grouped_sweep_mx<%d, %d, %d>", T, grouped_sweep_pf(T), J);
+    return true;
+  }
   std::snprintf(buf, len, "k_gemm_grouped_tile_mx<%d, %d, %d, %d, %d, %d>", g.WM, g.WN, g.MT, g.NG, g.PF, g.OCC);
   return true;
 }
