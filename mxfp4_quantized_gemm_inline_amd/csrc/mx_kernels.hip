@@ -2044,8 +2044,10 @@ hipError_t launch_gemm_grouped_act(const void* a, const int32_t* row_token, cons
 
 namespace {
 
-// Grouped short-K sweep configurations (T, PF, J), 128 x 128 column tiles.
-#define MX_GROUPED_SWEEP_CONFIGS(X) X(2, 3, 4) X(4, 6, 4) X(6, 9, 4) X(6, 9, 7) X(8, 10, 4)
+// Grouped short-K sweep configurations (T, PF, J), 128 x 128 column tiles. More column tiles per
+// unit amortize its lookup, pipeline fill and epilogue further (N=3584, K=768, T=4096: J = 4, 7,
+// 14 took 512, 451, 424 us).
+#define MX_GROUPED_SWEEP_CONFIGS(X) X(2, 3, 4) X(4, 6, 4) X(6, 9, 4) X(6, 9, 7) X(6, 9, 14) X(8, 10, 4)
 
 template <int T, int PF, int J>
 hipError_t run_grouped_sweep_mx(const void* aq, const void* as, const int32_t* offs, int E, int R_max, const void* wp,
@@ -2081,7 +2083,8 @@ int grouped_sweep_pf(int T) {
 }
 
 // The second GEMM's configuration: the sweep kernel (J > 0) when segments exceed 64 rows and
-// K is a compiled step count (seven column tiles per unit where compiled, else four), the
+// K is a compiled step count (the most column tiles per unit compiled for it: 14 at K = 768,
+// which makes N = 3584 two units per expert), the
 // tiled kernel otherwise. Tuning only: MX_GROUPED_CONFIG="gk,J" forces the sweep kernel,
 // "gt,..." a tiled configuration; false when the choice cannot run this call.
 bool resolve_grouped_mx(int N, int K, int64_t rows_hint, GroupedConfig& g, int& J) {
@@ -2093,8 +2096,8 @@ bool resolve_grouped_mx(int N, int K, int64_t rows_hint, GroupedConfig& g, int& 
     return grouped_sweep_supported(T, J) && N % 128 == 0;
   }
   if (!(s && *s) && rows_hint > 64 && N % 128 == 0) {
-    if (grouped_sweep_supported(T, 7)) { J = 7; return true; }
-    if (grouped_sweep_supported(T, 4)) { J = 4; return true; }
+    for (const int j : {14, 7, 4})
+      if (grouped_sweep_supported(T, j)) { J = j; return true; }
   }
   return resolve_grouped_act(N, rows_hint, g);
 }

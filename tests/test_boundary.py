@@ -207,7 +207,7 @@ def test_calibration_argument_errors():
 def test_gemm2_plan_picks_the_sweep_for_long_segments_at_short_k(monkeypatch):
     monkeypatch.delenv("MX_GROUPED_CONFIG", raising=False)
     plan = mx.mx_a4w4_gemm_grouped_mx_plan
-    assert plan(3584, 768, 73) == "k_gemm_grouped_sweep_mx<6, 9, 7>"
+    assert plan(3584, 768, 73) == "k_gemm_grouped_sweep_mx<6, 9, 14>"
     assert plan(1024, 512, 73) == "k_gemm_grouped_sweep_mx<4, 6, 4>"
     assert plan(3584, 768, 5).startswith("k_gemm_grouped_tile_mx<")
     assert plan(3584, 4224, 73).startswith("k_gemm_grouped_tile_mx<")  # 33 steps: not compiled
@@ -264,9 +264,9 @@ def test_gemm2_and_combine_argument_errors_and_plan(monkeypatch):
     assert c(None, 8, B, Cp, 4, 2, 64, A, None) == mx.MX_ERR_NULL
     assert c(A, 8, B, Cp, 4, 2, 64, MIS, None) == mx.MX_ERR_ALIGN
     assert c(A, 8, B + 2, Cp, 4, 2, 64, A, None) == mx.MX_ERR_ALIGN
-    assert mx.mx_a4w4_gemm_grouped_mx_plan(3584, 768, 73) == "k_gemm_grouped_sweep_mx<6, 9, 7>"
+    assert mx.mx_a4w4_gemm_grouped_mx_plan(3584, 768, 73) == "k_gemm_grouped_sweep_mx<6, 9, 14>"
     assert mx.mx_a4w4_gemm_grouped_mx_plan(3584, 768, 5) == "k_gemm_grouped_tile_mx<1, 4, 4, 4, 2, 2>"
-    assert mx.mx_a4w4_gemm_grouped_mx_plan(768, 768, 73) == "k_gemm_grouped_sweep_mx<6, 9, 7>"
+    assert mx.mx_a4w4_gemm_grouped_mx_plan(768, 768, 73) == "k_gemm_grouped_sweep_mx<6, 9, 14>"
 
 
 def test_a16w4_argument_errors():

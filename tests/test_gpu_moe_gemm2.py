@@ -4,7 +4,7 @@ the oracle (oracle/mx_oracle.py: grouped_gemm_mx_ref, combine_ref).
 - GEMM2 at the layer's shape (E = 896, N = model_dim 3584, K = inter_dim 768) for the routed
   rows of T = 1, 16, 256, 4096 tokens, on sampled rows, in the configuration the library
   picks (the one the bench times); arbitrary MXFP4 rows (every E2M1 code, scales 2^-9..2^2).
-- Every configuration (tiled, and the short-K sweep with 4 and 7 column tiles per unit,
+- Every configuration (tiled, and the short-K sweep with 4, 7 and 14 column tiles per unit,
   N = 1024 leaving a partial chunk) on a ragged segment table (0, 1, 63, 64, 130, 200 rows),
   all rows.
 - The combine, with out-of-range row indices, against the exact weighted sum of the same
@@ -65,7 +65,7 @@ def test_gemm2_matches_oracle(T):
     check_gemm(c[rows], exact, what=f"gemm2 T={T} ({mx.mx_a4w4_gemm_grouped_mx_plan(W.MOE_N2, W.MOE_K2, hint)})")
 
 
-@pytest.mark.parametrize("cfg", ["gt,1,4,4,4,2,2", "gt,1,8,8,4,1,2", "gk,4", "gk,7"])
+@pytest.mark.parametrize("cfg", ["gt,1,4,4,4,2,2", "gt,1,8,8,4,1,2", "gk,4", "gk,7", "gk,14"])
 def test_gemm2_every_config_on_ragged_segments(cfg, monkeypatch):
     torch = torch_or_skip()
     mx = lib_or_fail()
