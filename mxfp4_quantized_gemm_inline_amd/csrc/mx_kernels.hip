@@ -1469,7 +1469,8 @@ struct GemmConfig {
 
 #define MX_TILE_CONFIGS(X) \
   X(1, 4, 4, 4, 2, 1) X(2, 4, 4, 4, 2, 1) X(1, 4, 8, 4, 1, 1) X(2, 2, 4, 8, 1, 1) X(1, 4, 4, 2, 2, 1) \
-  X(1, 4, 4, 4, 1, 2) X(1, 4, 4, 4, 2, 2) X(2, 4, 4, 4, 1, 1) X(1, 4, 4, 2, 2, 2) X(1, 8, 8, 4, 1, 2)
+  X(1, 4, 4, 4, 1, 2) X(1, 4, 4, 4, 2, 2) X(2, 4, 4, 4, 1, 1) X(1, 4, 4, 2, 2, 2) X(1, 8, 8, 4, 1, 2) \
+  X(1, 4, 4, 1, 2, 1) X(1, 4, 4, 1, 2, 2)
 
 // Weight prefetch depth: enough registers for a wave's whole K share when it fits (4, 8 or
 // 16 steps of NG operands, at most kSkinnyPD operands), so no registers go to duplicate
@@ -1717,6 +1718,17 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   if (tiles256 >= 150) {
     c.NG = 4; c.GM = 8; c.OCC = 2;
     c.PF = K <= 1024 || G >= 512 || (M >= 1024 && G >= 256) ? 1 : 2;
+    return c;
+  }
+  // few 256-wide tiles but about 200 or more 64 x 64 ones (N=7168 at M=65..128): narrow
+  // tiles at two CTAs per CU fill the chip without K slices or their reduce, as long as the
+  // bf16 activation rows that every 64-column tile re-reads through L2 stay modest (at most
+  // 160 MB in all: 22 MB at 7168 x 768 and 121 MB at 7168 x 4224 for M = 128 gained 13% and
+  // 6%; 242 MB at 8448 x 7168 took 41 us against 22.6 us for K slices)
+  const int64_t tiles64 = (int64_t)((M + 63) / 64) * (N / 64);
+  const int64_t reread = (int64_t)(N / 64) * ((M + 63) / 64 * 64) * K * 2;
+  if (tiles64 >= 200 && reread <= (int64_t)160 << 20) {
+    c.NG = 1; c.PF = 2; c.GM = 8; c.OCC = 2;
     return c;
   }
   if (split_ok) {

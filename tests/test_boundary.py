@@ -125,6 +125,10 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     assert mx.mx_a4w4_gemm_plan(1024, 7168, 768) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
     assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_gemm_tile<1, 8, 8, 4, 1, 2> GM=8"
     assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
+    # mid M: 64 x 64 tiles while the activation re-reads stay modest, K slices beyond
+    assert mx.mx_a4w4_gemm_plan(128, 7168, 768) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(100, 7168, 4224) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
+    assert "k_splitk_reduce" in mx.mx_a4w4_gemm_plan(128, 8448, 7168)
     # split K only with a workspace; the streaming kernels never need one otherwise
     with_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168)
     no_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168, workspace_bytes=0)

@@ -22,7 +22,7 @@ STREAM = [(1, 1, 2), (1, 1, 4), (1, 1, 8), (1, 2, 4), (1, 2, 8), (1, 4, 4), (1, 
           (4, 1, 4), (4, 1, 8), (4, 2, 4), (4, 4, 4), (8, 1, 4), (8, 2, 4)]
 TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8, 1, 1), (1, 4, 4, 2, 2, 1),
         (1, 4, 4, 4, 1, 2), (1, 4, 4, 4, 2, 2), (2, 4, 4, 4, 1, 1), (1, 4, 4, 2, 2, 2),
-        (1, 8, 8, 4, 1, 2)]
+        (1, 8, 8, 4, 1, 2), (1, 4, 4, 1, 2, 1), (1, 4, 4, 1, 2, 2)]
 WIDE = [(8, 2), (8, 4), (4, 4), (4, 8)]
 SWEEP_K = (256, 512, 768, 1024)  # the short-K sweep kernel's compiled step counts 2, 4, 6, 8
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
