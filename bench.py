@@ -574,7 +574,7 @@ def grouped_sweep(torch, mx, W, timer):
                      "tflops": round(F / us_f / 1e6, 2), "gbps": round(Bf / us_f / 1e3, 1),
                      "frac_hbm": round(Bf / HBM_PEAK * 1e6 / us_f, 4),
                      "frac_mfma": round(F / MFMA_FP4_PEAK * 1e6 / us_f, 4),
-                     "kernel": mx.mx_a4w4_gemm_grouped_act_quant_plan(N, K, mx.MX_ACT_SWIGLU, hint)})
+                     "kernel": mx.mx_a4w4_gemm_grouped_act_quant_plan(E, R, N, K, mx.MX_ACT_SWIGLU, hint)})
         log(f"  grouped T={T} + fused SwiGLU/MXFP4 epilogue: {us_f:.2f} us")
         # the layer's second GEMM on MXFP4 rows (inter_dim 768 -> model_dim 3584), then the combine
         N2, K2 = W.MOE_N2, W.MOE_K2

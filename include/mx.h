@@ -248,12 +248,14 @@ mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t T, int64_t
                                     int64_t rows_hint, char* buf, size_t buf_len);
 
 /*
- * The same for mx_a4w4_gemm_grouped_act_quant (its kernel depends on N, act and the hint;
- * tuning override MX_GROUPED_CONFIG="gt,..."). Errors: MX_ERR_SHAPE (shape or act),
- * MX_ERR_NULL (buf), MX_ERR_HIP (the override names no fused configuration for N).
+ * The same for mx_a4w4_gemm_grouped_act_quant (its kernel depends on E, R_max, N, act and
+ * the hint, as for the call; tuning override MX_GROUPED_CONFIG="gt,..."). Errors:
+ * MX_ERR_SHAPE (E, R_max, shape or act as for the call), MX_ERR_NULL (buf), MX_ERR_HIP (the
+ * override names no fused configuration for N).
  */
-mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t N, int64_t K, int32_t act, int64_t rows_hint,
-                                              char* buf, size_t buf_len);
+mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t E, int64_t R_max, int64_t N, int64_t K,
+                                              int32_t act, int64_t rows_hint, char* buf,
+                                              size_t buf_len);
 
 /* The same for mx_a4w4_gemm_grouped_mx (its kernel depends on N, K and the hint). Errors as
  * for mx_a4w4_gemm_grouped_act_quant_plan. */

@@ -34,7 +34,7 @@ SIGNATURES = {
                                            _c_sz]),
     "mx_a4w4_gemm_grouped_act_quant": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _c_i64,
                                                 ctypes.c_int32, _c_i64, _vp, _vp, _vp]),
-    "mx_a4w4_gemm_grouped_act_quant_plan": (_c_int, [_c_i64, _c_i64, ctypes.c_int32, _c_i64, ctypes.c_char_p,
+    "mx_a4w4_gemm_grouped_act_quant_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_i64, ctypes.c_int32, _c_i64, ctypes.c_char_p,
                                                      _c_sz]),
     "mx_a4w4_gemm_grouped_mx": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]),
     "mx_a4w4_gemm_grouped_mx_plan": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
@@ -241,9 +241,12 @@ def mx_a4w4_gemm_grouped_act_quant(a_bf16, row_token, expert_offsets, E: int, R_
     return h_fp4, h_scale
 
 
-def mx_a4w4_gemm_grouped_act_quant_plan(N: int, K: int, act: int = MX_ACT_SWIGLU, rows_hint: int = 1) -> str:
+def mx_a4w4_gemm_grouped_act_quant_plan(E: int, R_max: int, N: int, K: int, act: int = MX_ACT_SWIGLU,
+                                        rows_hint: int = 1) -> str:
+    """Kernel mx_a4w4_gemm_grouped_act_quant launches for this table size, shape and hint."""
     buf = ctypes.create_string_buffer(256)
-    _check(lib().mx_a4w4_gemm_grouped_act_quant_plan(int(N), int(K), int(act), int(rows_hint), buf, len(buf)),
+    _check(lib().mx_a4w4_gemm_grouped_act_quant_plan(int(E), int(R_max), int(N), int(K), int(act), int(rows_hint),
+                                                     buf, len(buf)),
            "mx_a4w4_gemm_grouped_act_quant_plan")
     return buf.value.decode()
 

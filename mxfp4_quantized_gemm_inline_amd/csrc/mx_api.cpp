@@ -212,11 +212,13 @@ mx_status mx_moe_combine(const void* y_bf16, int64_t R, const int32_t* token_row
   return from_hip(mx::launch_moe_combine(y_bf16, R, token_rows, token_weights, T, topk, N, out_bf16, stream));
 }
 
-mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t N, int64_t K, int32_t act, int64_t rows_hint, char* buf,
-                                              size_t buf_len) {
-  if (!gemm_shape_ok(N, K) || (act != MX_ACT_SILU && act != MX_ACT_SWIGLU)) return MX_ERR_SHAPE;
+mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int32_t act,
+                                              int64_t rows_hint, char* buf, size_t buf_len) {
+  if (E < 1 || R_max < 0 || E > (1 << 20) || R_max > (1ll << 31) - 1 || !gemm_shape_ok(N, K) ||
+      (act != MX_ACT_SILU && act != MX_ACT_SWIGLU))
+    return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;
-  if (!mx::grouped_act_plan(N, act, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
+  if (!mx::grouped_act_plan(E, R_max, N, act, rows_hint < 1 ? 1 : rows_hint, buf, buf_len)) {
     buf[0] = '\0';
     return MX_ERR_HIP;
   }

@@ -21,7 +21,7 @@ hipError_t launch_gemm_grouped(const void* a, const int32_t* row_token, const in
 hipError_t launch_gemm_grouped_act(const void* a, const int32_t* row_token, const int32_t* offsets, int64_t E,
                                    int64_t R_max, const void* wp, void* hq, void* hs, int64_t T, int64_t N,
                                    int64_t K, int act, int64_t rows_hint, hipStream_t st);
-bool grouped_act_plan(int64_t N, int act, int64_t rows_hint, char* buf, size_t len);
+bool grouped_act_plan(int64_t E, int64_t R_max, int64_t N, int act, int64_t rows_hint, char* buf, size_t len);
 // Second MoE GEMM on MXFP4 rows (aq [R_max, K/2], as [R_max, K/32]) and the top-k combine.
 hipError_t launch_gemm_grouped_mx(const void* aq, const void* as, const int32_t* offsets, int64_t E, int64_t R_max,
                                   const void* wp, void* c, int64_t N, int64_t K, int64_t rows_hint, hipStream_t st);

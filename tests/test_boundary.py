@@ -236,14 +236,18 @@ def test_fused_act_quant_argument_errors_and_plan(monkeypatch):
     assert f(A, B, Cp, 4, 16, A, 1, 1536, 3584, 1, 1, A, MIS, None) == mx.MX_ERR_ALIGN
     assert f(A, B, Cp, 4, 0, A, 1, 1536, 3584, 1, 1, None, None, None) == mx.MX_OK       # no rows: no-op
     plan = mx.mx_a4w4_gemm_grouped_act_quant_plan
-    assert plan(1536, 3584, mx.MX_ACT_SWIGLU, 73) == "k_gemm_grouped_tile<1, 8, 8, 4, 1, 2, swiglu>"
-    assert plan(1536, 3584, mx.MX_ACT_SWIGLU, 5) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2, swiglu>"
-    assert plan(768, 3584, mx.MX_ACT_SILU, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2, silu>"   # 768 % 512
-    with pytest.raises(mx.MxError):
-        plan(1536, 3584, 2, 1)
+    assert plan(896, 65536, 1536, 3584, mx.MX_ACT_SWIGLU, 73) == "k_gemm_grouped_tile<1, 8, 8, 4, 1, 2, swiglu>"
+    assert plan(896, 4096, 1536, 3584, mx.MX_ACT_SWIGLU, 5) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2, swiglu>"
+    assert plan(896, 65536, 768, 3584, mx.MX_ACT_SILU, 73) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2, silu>"   # 768 % 512
+    # a handful of rows (T = 1: 16 rows, 96 CTAs of 64 x 256): 64 x 128 tiles
+    assert plan(896, 16, 1536, 3584, mx.MX_ACT_SWIGLU, 1) == "k_gemm_grouped_tile<1, 4, 4, 2, 2, 2, swiglu>"
+    assert plan(896, 256, 1536, 3584, mx.MX_ACT_SWIGLU, 1) == "k_gemm_grouped_tile<1, 4, 4, 4, 2, 2, swiglu>"
+    for bad in ((896, 16, 1536, 3584, 2, 1), (0, 16, 1536, 3584, 1, 1), (896, -1, 1536, 3584, 1, 1)):
+        with pytest.raises(mx.MxError):
+            plan(*bad)
     monkeypatch.setenv("MX_GROUPED_CONFIG", "gt,1,4,4,4,1,2")   # compiled, but not with the fused epilogue
     with pytest.raises(mx.MxError):
-        plan(1536, 3584, mx.MX_ACT_SWIGLU, 1)
+        plan(896, 16, 1536, 3584, mx.MX_ACT_SWIGLU, 1)
 
 
 def test_gemm2_and_combine_argument_errors_and_plan(monkeypatch):

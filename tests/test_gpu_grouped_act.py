@@ -55,7 +55,7 @@ def test_swiglu_quant_matches_oracle(T):
     assert np.all(q[R:] == 0xAB) and np.all(s[R:] == 0xCD)       # rows >= R untouched
     rows = sample_rows(R, n=24, seed=100 + T)
     _check(q, s, a, row_token, offs, W.moe_expert_weight, AO.ACT_SWIGLU, rows,
-           f"swiglu T={T} ({mx.mx_a4w4_gemm_grouped_act_quant_plan(W.MOE_N, W.MOE_K, 1, rows_hint(T))})")
+           f"swiglu T={T} ({mx.mx_a4w4_gemm_grouped_act_quant_plan(W.MOE_E, R, W.MOE_N, W.MOE_K, 1, rows_hint(T))})")
 
 
 def test_silu_quant_matches_oracle():
@@ -75,7 +75,7 @@ def test_silu_quant_matches_oracle():
     _check(host_u8(hq), host_u8(hs), a, row_token, offs, W.moe_expert_weight, AO.ACT_SILU, rows, "silu T=256")
 
 
-ACT_CONFIGS = ["gt,1,4,4,4,2,2", "gt,1,8,8,4,1,2"]
+ACT_CONFIGS = ["gt,1,4,4,4,2,2", "gt,1,8,8,4,1,2", "gt,1,4,4,2,2,2"]
 
 
 @pytest.mark.parametrize("act", [0, 1])

@@ -65,7 +65,7 @@ def test_gemm2_matches_oracle(T):
     check_gemm(c[rows], exact, what=f"gemm2 T={T} ({mx.mx_a4w4_gemm_grouped_mx_plan(W.MOE_N2, W.MOE_K2, hint)})")
 
 
-@pytest.mark.parametrize("cfg", ["gt,1,4,4,4,2,2", "gt,1,8,8,4,1,2", "gk,4", "gk,7", "gk,14"])
+@pytest.mark.parametrize("cfg", ["gt,1,4,4,4,2,2", "gt,1,8,8,4,1,2", "gt,1,4,4,2,2,2", "gk,4", "gk,7", "gk,14"])
 def test_gemm2_every_config_on_ragged_segments(cfg, monkeypatch):
     torch = torch_or_skip()
     mx = lib_or_fail()
