@@ -232,7 +232,7 @@ mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_by
 
 /*
  * Introspection (host only, no GPU needed): the kernel instantiation mx_a16w4_gemm would
- * launch for (M, N, K): "k_gemm_a16w4_stream<NG, WK, PD>" (decode M, at most 16 rows) or
+ * launch for (M, N, K): "k_gemm_a16w4_stream<MT, NG, WK, PD>" (decode M, at most 32 rows) or
  * "k_gemm_a16w4 (64 x 256 tiles)", written NUL-terminated (truncated to buf_len) into the
  * caller's host buffer; "none" for M == 0. Errors: MX_ERR_SHAPE (as mx_a16w4_gemm),
  * MX_ERR_NULL (buf NULL or buf_len 0).

@@ -3,7 +3,7 @@
 // bf16 output ("[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", CI Guide, names the
 // variant as outside that change; the weight is the same prepared blob).
 //
-// Two forms: a weight-streaming kernel for decode M (at most 16 rows, below) and a tiled
+// Two forms: a weight-streaming kernel for decode M (at most 32 rows, below) and a tiled
 // kernel for larger M. Tile: BM = 64 rows x BN = 256 columns, four waves side by side along N, each 64 x 64
 // (four 16-row tiles x four 16-column groups). Per 128-wide K step the CTA's bf16
 // activation tile (64 x 128, 16 KiB) goes to LDS, double buffered, its 16-byte chunks
@@ -147,35 +147,41 @@ __global__ __launch_bounds__(kA16Threads, 2) void k_gemm_a16w4(const uint16_t* _
   }
 }
 
-// Decode-M form (M <= 16): one 16-row MFMA tile. A CTA owns 16 NG columns over all of K;
+// Decode-M form (M <= 32): MT 16-row MFMA tiles. A CTA owns 16 NG columns over all of K;
 // its WK waves split the K steps. Each wave issues the weight loads of up to PD steps at
 // once (1 KiB per column group and step, the A4W4 layout, plus one scale byte per lane and
 // group), then the matching activation loads, which go from global memory straight into
-// MFMA operands: lane l reads the 64 bytes of row l % 16 (clamped to the last row, never
-// stored) and 32-block l / 16, which are its operands of the four 16x16x32 MFMAs of the
-// step under the k order above. No LDS staging, no barrier in the K loop; the wave partial
-// sums meet in LDS in a fixed wave order.
-template <int NG, int WK, int PD>
+// MFMA operands: lane l reads, for row tile mt, the 64 bytes of row 16 mt + l % 16
+// (clamped to the last row, never stored) and 32-block l / 16, which are its operands of
+// the four 16x16x32 MFMAs of the step under the k order above; each decoded weight operand
+// serves all MT row tiles. No LDS staging, no barrier in the K loop; the wave partial sums
+// meet in LDS in a fixed wave order.
+template <int MT, int NG, int WK, int PD>
 __global__ __launch_bounds__(64 * WK) void k_gemm_a16w4_stream(const uint16_t* __restrict__ A,
                                                                const uint8_t* __restrict__ Wp,
                                                                uint16_t* __restrict__ C, int M, int N, int K) {
-  __shared__ __align__(16) v4f red[WK > 1 ? WK * NG * 64 : 1];
+  __shared__ __align__(16) v4f red[WK > 1 ? WK * NG * MT * 64 : 1];
   const int T = K / kStepK;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g0 = blockIdx.x * NG;
   const int per = (T + WK - 1) / WK, t0 = min(T, w * per), t1 = min(T, t0 + per);
   const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
-  const uint8_t* __restrict__ arow =
-      reinterpret_cast<const uint8_t*>(A + (size_t)min(lane & 15, M - 1) * K) + (lane >> 4) * (kBlock * 2);
-
-  v4f acc[NG];
+  const uint8_t* arow[MT];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+    arow[mt] = reinterpret_cast<const uint8_t*>(A + (size_t)min(16 * mt + (lane & 15), M - 1) * K) +
+               (lane >> 4) * (kBlock * 2);
+
+  v4f acc[NG][MT];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int tb = t0; tb < t1; tb += PD) {
     uint4 wq[PD][NG];
     uint32_t wsb[PD][NG];
-    uint32_t xa[PD][16];
+    uint32_t xa[PD][MT][16];
     // branch-free: steps past the wave's range re-load its last step and are never used
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
@@ -187,7 +193,10 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_a16w4_stream(const uint16_t* _
       }
     }
 #pragma unroll
-    for (int i = 0; i < PD; ++i) load_block_at(arow, (uint32_t)(min(tb + i, t1 - 1) * kStepK * 2), xa[i]);
+    for (int i = 0; i < PD; ++i)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        load_block_at(arow[mt], (uint32_t)(min(tb + i, t1 - 1) * kStepK * 2), xa[i][mt]);
     __builtin_amdgcn_sched_barrier(0);  // every load of the chunk ahead of its first use
     const int nh = min(PD, t1 - tb);
 #pragma unroll
@@ -206,62 +215,81 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_a16w4_stream(const uint16_t* _
             d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
             d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
             const bf16x8 aop = __builtin_bit_cast(bf16x8, make_uint4(d[0], d[1], d[2], d[3]));
-            const bf16x8 bop = __builtin_bit_cast(
-                bf16x8, make_uint4(xa[i][4 * j], xa[i][4 * j + 1], xa[i][4 * j + 2], xa[i][4 * j + 3]));
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc[g], 0, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const bf16x8 bop = __builtin_bit_cast(
+                  bf16x8, make_uint4(xa[i][mt][4 * j], xa[i][mt][4 * j + 1], xa[i][mt][4 * j + 2], xa[i][mt][4 * j + 3]));
+              acc[g][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc[g][mt], 0, 0, 0);
+            }
           }
         }
       }
     }
   }
-  // lane l holds C[m = l % 16][n = 16 (g0 + g) + 4 (l / 16) .. + 3]
-  auto store = [&](int g, const v4f& v) {
-    const int m = lane & 15;
+  // lane l holds C[m = 16 mt + l % 16][n = 16 (g0 + g) + 4 (l / 16) .. + 3]
+  auto store = [&](int g, int mt, const v4f& v) {
+    const int m = 16 * mt + (lane & 15);
     if (m < M)
       *reinterpret_cast<uint2*>(C + (size_t)m * N + 16 * (g0 + g) + 4 * (lane >> 4)) = pack4_bf16(v[0], v[1], v[2], v[3]);
   };
   if constexpr (WK == 1) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) store(g, acc[g]);
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) store(g, mt, acc[g][mt]);
   } else {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) red[(w * NG + g) * 64 + lane] = acc[g];
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[((w * NG + g) * MT + mt) * 64 + lane] = acc[g][mt];
     __syncthreads();
-    for (int g = w; g < NG; g += WK) {
-      v4f sum = red[g * 64 + lane];
-      for (int ww = 1; ww < WK; ++ww) sum += red[(ww * NG + g) * 64 + lane];
-      store(g, sum);
+    for (int p = w; p < NG * MT; p += WK) {
+      v4f sum = red[p * 64 + lane];
+      for (int ww = 1; ww < WK; ++ww) sum += red[(ww * NG * MT + p) * 64 + lane];
+      store(p / MT, p % MT, sum);
     }
   }
 }
 
-// Decode-M choice: one column group per CTA when there are at least 512 of them, else two;
-// eight waves per CTA for long K (16 steps or more), else four; a wave's whole K share in
-// registers in chunks of PD = 2, 4 or 8 steps.
+// Decode-M choice: one 16-row tile up to 16 rows, two up to 32; one column group per CTA
+// when there are at least 512 of them, else two; eight waves per CTA for long K (16 steps
+// or more), else four; a wave's whole K share in registers in chunks of PD = 2, 4 or 8 steps
+// (at most 4 with two row tiles).
 struct A16StreamCfg {
-  int NG, WK, PD;
+  int MT, NG, WK, PD;
 };
-A16StreamCfg a16_stream_cfg(int64_t N, int64_t K) {
+A16StreamCfg a16_stream_cfg(int64_t M, int64_t N, int64_t K) {
   const int G = (int)(N / 16), T = (int)(K / kStepK);
-  A16StreamCfg c{G >= 512 ? 1 : 2, T >= 16 ? 8 : 4, 2};
-  const int per = (T + c.WK - 1) / c.WK;
-  while (c.PD < per && c.PD < 8) c.PD *= 2;
+  A16StreamCfg c{M > 16 ? 2 : 1, G >= 512 ? 1 : 2, T >= 16 ? 8 : 4, 2};
+  const int per = (T + c.WK - 1) / c.WK, cap = c.MT == 2 ? 4 : 8;
+  while (c.PD < per && c.PD < cap) c.PD *= 2;
   return c;
 }
 
-template <int NG, int WK>
+template <int MT, int NG, int WK>
 hipError_t run_a16_stream(int PD, const void* a, const void* wp, void* c, int M, int N, int K, hipStream_t st) {
   const dim3 grid((unsigned)(N / (16 * NG))), block(64 * WK);
   const auto* A = static_cast<const uint16_t*>(a);
   const auto* W = static_cast<const uint8_t*>(wp);
   auto* C = static_cast<uint16_t*>(c);
-  if (PD == 2) hipLaunchKernelGGL((k_gemm_a16w4_stream<NG, WK, 2>), grid, block, 0, st, A, W, C, M, N, K);
-  else if (PD == 4) hipLaunchKernelGGL((k_gemm_a16w4_stream<NG, WK, 4>), grid, block, 0, st, A, W, C, M, N, K);
-  else hipLaunchKernelGGL((k_gemm_a16w4_stream<NG, WK, 8>), grid, block, 0, st, A, W, C, M, N, K);
+  if (PD == 2) hipLaunchKernelGGL((k_gemm_a16w4_stream<MT, NG, WK, 2>), grid, block, 0, st, A, W, C, M, N, K);
+  else if (PD == 4) hipLaunchKernelGGL((k_gemm_a16w4_stream<MT, NG, WK, 4>), grid, block, 0, st, A, W, C, M, N, K);
+  else if constexpr (MT == 1) hipLaunchKernelGGL((k_gemm_a16w4_stream<MT, NG, WK, 8>), grid, block, 0, st, A, W, C, M, N, K);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-constexpr int64_t kA16StreamMaxM = 16;
+template <int MT>
+hipError_t run_a16_stream_mt(const A16StreamCfg& cfg, const void* a, const void* wp, void* c, int M, int N, int K,
+                             hipStream_t st) {
+  if (cfg.NG == 1)
+    return cfg.WK == 8 ? run_a16_stream<MT, 1, 8>(cfg.PD, a, wp, c, M, N, K, st)
+                       : run_a16_stream<MT, 1, 4>(cfg.PD, a, wp, c, M, N, K, st);
+  return cfg.WK == 8 ? run_a16_stream<MT, 2, 8>(cfg.PD, a, wp, c, M, N, K, st)
+                     : run_a16_stream<MT, 2, 4>(cfg.PD, a, wp, c, M, N, K, st);
+}
+
+constexpr int64_t kA16StreamMaxM = 32;
 
 }  // namespace
 
@@ -269,8 +297,8 @@ bool a16w4_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t len) {
   if (M <= 0) {
     std::snprintf(buf, len, "none");
   } else if (M <= kA16StreamMaxM) {
-    const A16StreamCfg c = a16_stream_cfg(N, K);
-    std::snprintf(buf, len, "k_gemm_a16w4_stream<%d, %d, %d>", c.NG, c.WK, c.PD);
+    const A16StreamCfg c = a16_stream_cfg(M, N, K);
+    std::snprintf(buf, len, "k_gemm_a16w4_stream<%d, %d, %d, %d>", c.MT, c.NG, c.WK, c.PD);
   } else {
     std::snprintf(buf, len, "k_gemm_a16w4 (64 x 256 tiles)");
   }
@@ -280,13 +308,9 @@ bool a16w4_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t len) {
 hipError_t launch_a16w4(const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (M <= kA16StreamMaxM) {
-    const A16StreamCfg cfg = a16_stream_cfg(N, K);
-    if (cfg.NG == 1) {
-      return cfg.WK == 8 ? run_a16_stream<1, 8>(cfg.PD, a, wp, c, (int)M, (int)N, (int)K, st)
-                         : run_a16_stream<1, 4>(cfg.PD, a, wp, c, (int)M, (int)N, (int)K, st);
-    }
-    return cfg.WK == 8 ? run_a16_stream<2, 8>(cfg.PD, a, wp, c, (int)M, (int)N, (int)K, st)
-                       : run_a16_stream<2, 4>(cfg.PD, a, wp, c, (int)M, (int)N, (int)K, st);
+    const A16StreamCfg cfg = a16_stream_cfg(M, N, K);
+    return cfg.MT == 2 ? run_a16_stream_mt<2>(cfg, a, wp, c, (int)M, (int)N, (int)K, st)
+                       : run_a16_stream_mt<1>(cfg, a, wp, c, (int)M, (int)N, (int)K, st);
   }
   const int64_t tiles = ((M + kA16BM - 1) / kA16BM) * (N / kA16BN);
   if (tiles <= 0) return hipSuccess;

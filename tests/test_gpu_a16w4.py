@@ -1,7 +1,7 @@
 """GPU parity of the A16WFP4 variant (bf16 activations x decoded MXFP4 weight on the bf16
 MFMA) against the oracle (oracle/mx_oracle.py: gemm_a16w4_ref), within the GEMM tolerance
 |gpu - exact| <= 2^-7 |exact| + 1e-3 rms(exact): every output for ragged M over several
-64-row tiles and both K forms (K = 768, 4224), the decode form (M <= 16) over its launch
+64-row tiles and both K forms (K = 768, 4224), the decode form (M <= 32) over its launch
 shapes, sampled rows at the headline shape
 (N = 7168, K = 768, M = 2048, the launch the bench times); a one-hot activation probe that
 must reproduce the decoded weight bit for bit; canary rows past M left untouched."""
@@ -34,15 +34,17 @@ def test_a16w4_matches_oracle(M, K):
 
 
 @pytest.mark.parametrize("N,K,M", [(768, 768, 1), (768, 768, 16), (768, 4224, 5), (8192, 256, 3),
-                                   (256, 9216, 2), (8192, 768, 16)])
+                                   (256, 9216, 2), (8192, 768, 16), (768, 768, 17), (768, 4224, 32),
+                                   (8192, 768, 32), (256, 9216, 20)])
 def test_a16w4_decode_form_matches_oracle(N, K, M):
-    """The decode form (M <= 16): one and two column groups per CTA, four and eight waves,
-    a K share of 1 to 9 steps per wave (9216 = 72 steps: two prefetch chunks of 8), rows
-    past M neither read as real rows nor written."""
+    """The decode form (M <= 32, one or two 16-row tiles): one and two column groups per
+    CTA, four and eight waves, a K share of 1 to 9 steps per wave (9216 = 72 steps: two
+    prefetch chunks of 8, or three of 4 with two row tiles), rows past M neither read as
+    real rows nor written."""
     torch = torch_or_skip()
     mx = lib_or_fail()
     assert mx.mx_a16w4_gemm_plan(M, N, K).startswith("k_gemm_a16w4_stream<")
-    a = W.dense_activation(16, K, "plain", seed=74)[:M]
+    a = W.dense_activation(32, K, "plain", seed=74)[:M]
     w = W.dense_weight(N, K, seed=75)
     wp = mx.mx_prepare_weight(dev_bf16(w))
     out = torch.full((M + 3, N), 5.0, dtype=torch.bfloat16, device="cuda")
