@@ -109,19 +109,25 @@ mx_status mx_quant_act(const void* a_bf16, int64_t M, int64_t K, void* a_fp4, vo
                        hipStream_t stream);
 
 /*
- * Workspace the dense GEMM can use for a split-K reduction at this shape. It is
- * always optional: with a NULL or smaller workspace the library picks a
- * configuration that needs none.
+ * Workspace the dense GEMM can use at this shape: FP32 partial sums of a split-K
+ * reduction (few rows), or, at large M, the activations quantized once into the
+ * prepared layout (M rounded up to 64, times K * 17 / 32 bytes). It is always optional:
+ * with a NULL or smaller workspace the library picks a configuration that needs none,
+ * with the same results. 0 for an invalid shape.
  */
 size_t mx_a4w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * The dense A4W4 GEMM ("flydsl_gemm_a4w4" of "[gfx950][FlyDSL] Add direct dense A4W4
  * MXFP4 GEMM", Summary and Implementation): C = Q(A) * Q(W)^T with Q the MXFP4
- * quantization above; A is quantized inside the kernel, never written to memory.
+ * quantization above; A is quantized inside the kernel, never written to memory, except
+ * that at large M with a big enough workspace its MXFP4 codes are written once into the
+ * workspace and read back by the product kernel (bit-identical results).
  * a_bf16: [M, K] bf16. w_prep: prepared weight of shape [N, K]. c_bf16: [M, N] bf16,
- * rows < M written with the FP32 sum rounded to nearest even. Requires M >= 0,
- * N % 256 == 0, K % 128 == 0. M == 0 is a no-op. workspace may be NULL.
+ * rows < M written with the FP32 sum rounded to nearest even. Requires 0 <= M <= 2^30,
+ * N % 256 == 0, K % 128 == 0, N <= 2^30, K <= 2^24. M == 0 is a no-op. workspace may be
+ * NULL (then workspace_bytes is ignored); a non-NULL workspace must be 16-byte aligned.
+ * The call is asynchronous on stream; workspace must stay alive until it completes.
  */
 mx_status mx_a4w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int64_t M,
                        int64_t N, int64_t K, void* workspace, size_t workspace_bytes,

@@ -29,7 +29,7 @@ extern "C" {
  * that is stored to the 4-byte device word `sink` only when it equals a fixed improbable
  * constant (the store keeps the loads from being optimized away; `sink` is normally left
  * untouched). bytes must be a positive multiple of 16; buf 16-byte aligned; ctas in
- * [1, 2^20]. Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_HIP.
+ * [1, 2^20]. Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE (not gfx950), MX_ERR_HIP.
  */
 mx_status mx_calib_read(const void* buf, size_t bytes, int64_t ctas, void* sink, hipStream_t stream);
 
@@ -37,7 +37,7 @@ mx_status mx_calib_read(const void* buf, size_t bytes, int64_t ctas, void* sink,
  * One launch of `ctas` workgroups of 256 threads (four waves), each wave issuing `iters`
  * rounds of eight independent 16x16x128 block-scaled FP4 MFMAs on register operands (no
  * memory traffic but one conditional 4-byte store to `sink`, as above). ctas in [1, 2^20],
- * iters in [1, 2^24]. Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_HIP.
+ * iters in [1, 2^24]. Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE (not gfx950), MX_ERR_HIP.
  */
 mx_status mx_calib_mfma(int64_t ctas, int64_t iters, void* sink, hipStream_t stream);
 

@@ -95,17 +95,40 @@ def _stream_ptr(stream=None) -> int:
     return int(s.cuda_stream)
 
 
-def _dev(t, dtype, name):
+def _need(t, name, dtype=None, shape=None, min_bytes=None, min_numel=None):
+    """Validate a tensor argument from its metadata alone (type, dtype, shape, size), before
+    any device pointer is taken: a short or mis-shaped buffer would otherwise be read or
+    written out of bounds by the kernels, which receive only pointers and sizes."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(d) for d in shape)}, got {tuple(t.shape)}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs at least {min_bytes}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _dev(t, dtype, name):
+    """Device pointer of a validated tensor (raises if it is not on the current device)."""
+    torch = _torch()
+    _need(t, name, dtype)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device cuda:{torch.cuda.current_device()}")
     return t.data_ptr()
+
+
+def _dims2(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return int(t.shape[0]), int(t.shape[1])
 
 
 def mx_prepared_layout_version() -> int:
@@ -123,10 +146,12 @@ def mx_a4w4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 def mx_prepare_weight(w_bf16, out=None, stream=None):
     """W [N, K] bf16 -> opaque prepared MXFP4 blob (uint8, mx_prepared_weight_bytes(N, K))."""
     torch = _torch()
-    N, K = w_bf16.shape
+    _need(w_bf16, "w_bf16", torch.bfloat16)
+    N, K = _dims2(w_bf16, "w_bf16")
     nbytes = mx_prepared_weight_bytes(N, K)
     if out is None:
         out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w_bf16.device)
+    _need(out, "out", torch.uint8, min_bytes=nbytes)
     _check(lib().mx_prepare_weight(_dev(w_bf16, torch.bfloat16, "w_bf16"), N, K,
                                    _dev(out, torch.uint8, "w_prep"), _stream_ptr(stream)),
            "mx_prepare_weight")
@@ -137,16 +162,14 @@ def mx_prepare_weight_packed(w_fp4, w_scale, out=None, stream=None):
     """Caller-quantized weight -> prepared blob: w_fp4 uint8 [N, K/2] (low nibble = even k),
     w_scale uint8 [N, K/32] (E8M0)."""
     torch = _torch()
-    if w_fp4.dim() != 2 or w_scale.dim() != 2:
-        raise ValueError("w_fp4 and w_scale must be 2-D")
-    N, K = w_fp4.shape[0], 2 * w_fp4.shape[1]
-    if tuple(w_scale.shape) != (N, K // 32):
-        raise ValueError(f"w_scale must be [{N}, {K // 32}], got {tuple(w_scale.shape)}")
+    _need(w_fp4, "w_fp4", torch.uint8)
+    N, K2 = _dims2(w_fp4, "w_fp4")
+    K = 2 * K2
+    _need(w_scale, "w_scale", torch.uint8, shape=(N, K // 32))
     nbytes = mx_prepared_weight_bytes(N, K)
     if out is None:
         out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w_fp4.device)
-    elif out.numel() * out.element_size() < nbytes:
-        raise ValueError("out is too small")
+    _need(out, "out", torch.uint8, min_bytes=nbytes)
     _check(lib().mx_prepare_weight_packed(_dev(w_fp4, torch.uint8, "w_fp4"), _dev(w_scale, torch.uint8, "w_scale"),
                                           N, K, _dev(out, torch.uint8, "w_prep"), _stream_ptr(stream)),
            "mx_prepare_weight_packed")
@@ -156,6 +179,7 @@ def mx_prepare_weight_packed(w_fp4, w_scale, out=None, stream=None):
 def mx_unprepare_weight(w_prep, N: int, K: int, stream=None):
     """Prepared blob -> canonical (payload uint8 [N, K/2], scales uint8 [N, K/32])."""
     torch = _torch()
+    _need(w_prep, "w_prep", torch.uint8, min_bytes=mx_prepared_weight_bytes(N, K))
     q = torch.empty((N, K // 2), dtype=torch.uint8, device=w_prep.device)
     s = torch.empty((N, K // 32), dtype=torch.uint8, device=w_prep.device)
     _check(lib().mx_unprepare_weight(_dev(w_prep, torch.uint8, "w_prep"), N, K,
@@ -167,9 +191,12 @@ def mx_unprepare_weight(w_prep, N: int, K: int, stream=None):
 def mx_quant_act(a_bf16, q_out=None, s_out=None, stream=None):
     """A [M, K] bf16 -> (payload uint8 [M, K/2], scales uint8 [M, K/32]), canonical layout."""
     torch = _torch()
-    M, K = a_bf16.shape
+    _need(a_bf16, "a_bf16", torch.bfloat16)
+    M, K = _dims2(a_bf16, "a_bf16")
     q = q_out if q_out is not None else torch.empty((M, K // 2), dtype=torch.uint8, device=a_bf16.device)
     s = s_out if s_out is not None else torch.empty((M, K // 32), dtype=torch.uint8, device=a_bf16.device)
+    _need(q, "a_fp4", torch.uint8, min_bytes=M * (K // 2))
+    _need(s, "a_scale", torch.uint8, min_bytes=M * (K // 32))
     if M == 0:
         return q, s
     _check(lib().mx_quant_act(_dev(a_bf16, torch.bfloat16, "a_bf16"), M, K, _dev(q, torch.uint8, "a_fp4"),
@@ -185,8 +212,11 @@ def mx_a4w4_gemm(a_bf16, w_prep, N: int, out=None, workspace=None, stream=None):
     (the library then picks a configuration that needs no workspace).
     """
     torch = _torch()
-    M, K = a_bf16.shape
+    _need(a_bf16, "a_bf16", torch.bfloat16)
+    M, K = _dims2(a_bf16, "a_bf16")
+    _need(w_prep, "w_prep", torch.uint8, min_bytes=max(1, mx_prepared_weight_bytes(N, K)))
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_bf16.device)
+    _need(c, "out", torch.bfloat16, shape=(M, N))
     if M == 0:
         return c
     if workspace is None:
@@ -201,12 +231,27 @@ def mx_a4w4_gemm(a_bf16, w_prep, N: int, out=None, workspace=None, stream=None):
     return c
 
 
+def _grouped_tables(row_token, expert_offsets, w_prep_stacked, E, R_max, N, K):
+    """The segment table, the row-to-token map and the stacked weights of a grouped call:
+    expert_offsets [E+1] int32, row_token at least R_max int32 (when rows exist), E prepared
+    weights of shape [N, K]."""
+    torch = _torch()
+    _need(expert_offsets, "expert_offsets", torch.int32, min_numel=int(E) + 1)
+    if row_token is not None and R_max > 0:
+        _need(row_token, "row_token", torch.int32, min_numel=int(R_max))
+    _need(w_prep_stacked, "w_prep_stacked", torch.uint8,
+          min_bytes=max(1, int(E) * mx_prepared_weight_bytes(N, K)))
+
+
 def mx_a4w4_gemm_grouped(a_bf16, row_token, expert_offsets, E: int, R_max: int, w_prep_stacked,
                          N: int, rows_hint: int = 1, out=None, stream=None):
     """Grouped GEMM1: C [R_max, N] bf16, rows in expert-sorted order (rows >= R untouched)."""
     torch = _torch()
-    T, K = a_bf16.shape
+    _need(a_bf16, "a_bf16", torch.bfloat16)
+    T, K = _dims2(a_bf16, "a_bf16")
+    _grouped_tables(row_token, expert_offsets, w_prep_stacked, E, R_max, N, K)
     c = out if out is not None else torch.empty((R_max, N), dtype=torch.bfloat16, device=a_bf16.device)
+    _need(c, "out", torch.bfloat16, shape=(R_max, N))
     _check(lib().mx_a4w4_gemm_grouped(
         _dev(a_bf16, torch.bfloat16, "a_bf16") if T > 0 else None,
         _dev(row_token, torch.int32, "row_token") if R_max > 0 else None,
@@ -222,14 +267,16 @@ def mx_a4w4_gemm_grouped_act_quant(a_bf16, row_token, expert_offsets, E: int, R_
     """Grouped GEMM1 with fused SiLU / SwiGLU + MXFP4 quantization: returns (h_fp4 uint8
     [R_max, Nh/2], h_scale uint8 [R_max, Nh/32]) with Nh = N/2 (SwiGLU) or N (SiLU)."""
     torch = _torch()
-    T, K = a_bf16.shape
+    _need(a_bf16, "a_bf16", torch.bfloat16)
+    T, K = _dims2(a_bf16, "a_bf16")
+    _grouped_tables(row_token, expert_offsets, w_prep_stacked, E, R_max, N, K)
     Nh = N // 2 if act == MX_ACT_SWIGLU else N
     if h_fp4 is None:
         h_fp4 = torch.empty((R_max, Nh // 2), dtype=torch.uint8, device=a_bf16.device)
     if h_scale is None:
         h_scale = torch.empty((R_max, Nh // 32), dtype=torch.uint8, device=a_bf16.device)
-    if h_fp4.numel() < R_max * (Nh // 2) or h_scale.numel() < R_max * (Nh // 32):
-        raise ValueError("h_fp4 / h_scale are too small")
+    _need(h_fp4, "h_fp4", torch.uint8, min_bytes=R_max * (Nh // 2))
+    _need(h_scale, "h_scale", torch.uint8, min_bytes=R_max * (Nh // 32))
     _check(lib().mx_a4w4_gemm_grouped_act_quant(
         _dev(a_bf16, torch.bfloat16, "a_bf16") if T > 0 else None,
         _dev(row_token, torch.int32, "row_token") if R_max > 0 else None,
@@ -256,10 +303,15 @@ def mx_a4w4_gemm_grouped_mx(a_fp4, a_scale, expert_offsets, E: int, R_max: int, 
     """Second MoE GEMM on MXFP4 rows: a_fp4 uint8 [R_max, K/2], a_scale uint8 [R_max, K/32]
     -> C [R_max, N] bf16 (rows >= R untouched)."""
     torch = _torch()
-    K = 2 * a_fp4.shape[1]
-    if tuple(a_scale.shape) != (a_fp4.shape[0], K // 32) or a_fp4.shape[0] < R_max:
-        raise ValueError("a_fp4 / a_scale must be [>= R_max, K/2] and [same rows, K/32]")
+    _need(a_fp4, "a_fp4", torch.uint8)
+    rows, K2 = _dims2(a_fp4, "a_fp4")
+    K = 2 * K2
+    _need(a_scale, "a_scale", torch.uint8, shape=(rows, K // 32))
+    if rows < R_max:
+        raise ValueError(f"a_fp4 / a_scale hold {rows} rows, need at least R_max = {R_max}")
+    _grouped_tables(None, expert_offsets, w_prep_stacked, E, R_max, N, K)
     c = out if out is not None else torch.empty((R_max, N), dtype=torch.bfloat16, device=a_fp4.device)
+    _need(c, "out", torch.bfloat16, shape=(R_max, N))
     _check(lib().mx_a4w4_gemm_grouped_mx(
         _dev(a_fp4, torch.uint8, "a_fp4") if R_max > 0 else None,
         _dev(a_scale, torch.uint8, "a_scale") if R_max > 0 else None,
@@ -279,11 +331,13 @@ def mx_a4w4_gemm_grouped_mx_plan(N: int, K: int, rows_hint: int = 1) -> str:
 def mx_moe_combine(y_bf16, token_rows, token_weights, out=None, stream=None):
     """out [T, N] bf16 = sum_k token_weights[t, k] * y[token_rows[t, k]] (FP32, k order)."""
     torch = _torch()
-    R, N = y_bf16.shape
-    T, topk = token_rows.shape
-    if tuple(token_weights.shape) != (T, topk):
-        raise ValueError("token_weights must match token_rows")
+    _need(y_bf16, "y_bf16", torch.bfloat16)
+    R, N = _dims2(y_bf16, "y_bf16")
+    _need(token_rows, "token_rows", torch.int32)
+    T, topk = _dims2(token_rows, "token_rows")
+    _need(token_weights, "token_weights", torch.float32, shape=(T, topk))
     o = out if out is not None else torch.empty((T, N), dtype=torch.bfloat16, device=token_rows.device)
+    _need(o, "out", torch.bfloat16, shape=(T, N))
     _check(lib().mx_moe_combine(
         _dev(y_bf16, torch.bfloat16, "y_bf16") if R > 0 else None, R,
         _dev(token_rows, torch.int32, "token_rows") if T > 0 else None,
@@ -295,8 +349,11 @@ def mx_moe_combine(y_bf16, token_rows, token_weights, out=None, stream=None):
 def mx_a16w4_gemm(a_bf16, w_prep, N: int, out=None, stream=None):
     """A16WFP4: A [M, K] bf16 (not quantized) x decoded prepared weight -> C [M, N] bf16."""
     torch = _torch()
-    M, K = a_bf16.shape
+    _need(a_bf16, "a_bf16", torch.bfloat16)
+    M, K = _dims2(a_bf16, "a_bf16")
+    _need(w_prep, "w_prep", torch.uint8, min_bytes=max(1, mx_prepared_weight_bytes(N, K)))
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_bf16.device)
+    _need(c, "out", torch.bfloat16, shape=(M, N))
     if M == 0:
         return c
     _check(lib().mx_a16w4_gemm(_dev(a_bf16, torch.bfloat16, "a_bf16"), _dev(w_prep, torch.uint8, "w_prep"),

@@ -18,11 +18,19 @@ std::atomic<int> g_arch_ok[kMaxDevices];
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Rows of one GEMM call: at most 2^30, so row and tile counts (M + 255, M padded to 64) stay
+// within 32-bit integers in the kernels and launchers.
+constexpr int64_t kMaxRows = 1ll << 30;
+
 // K <= 2^24 keeps a tile row's byte offset (at most 127 rows of 2K bytes) in 32 bits.
 bool gemm_shape_ok(int64_t N, int64_t K) {
   return N > 0 && K > 0 && N % 256 == 0 && K % 128 == 0 && N <= (1ll << 30) && K <= (1ll << 24);
 }
 
+}  // namespace
+
+namespace mx {
+// The gfx950 check every entry point makes (also used by the measurement entry points).
 mx_status check_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MX_ERR_HIP;
@@ -36,6 +44,10 @@ mx_status check_device() {
   }
   return st == 1 ? MX_OK : MX_ERR_DEVICE;
 }
+}  // namespace mx
+
+namespace {
+using mx::check_device;
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
@@ -104,13 +116,13 @@ mx_status mx_quant_act(const void* a_bf16, int64_t M, int64_t K, void* a_fp4, vo
 }
 
 size_t mx_a4w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M <= 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return 0;
+  if (M <= 0 || !gemm_shape_ok(N, K) || M > kMaxRows) return 0;
   return mx::gemm_workspace_bytes(M, N, K);
 }
 
 mx_status mx_a4w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int64_t M, int64_t N,
                        int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (M < 0 || !gemm_shape_ok(N, K) || M > kMaxRows) return MX_ERR_SHAPE;
   if (M == 0) return MX_OK;
   if (!a_bf16 || !w_prep || !c_bf16) return MX_ERR_NULL;
   if (!aligned16(a_bf16) || !aligned16(w_prep) || !aligned16(c_bf16)) return MX_ERR_ALIGN;
@@ -122,7 +134,7 @@ mx_status mx_a4w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int
 
 mx_status mx_a16w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int64_t M, int64_t N, int64_t K,
                         hipStream_t stream) {
-  if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (M < 0 || !gemm_shape_ok(N, K) || M > kMaxRows) return MX_ERR_SHAPE;
   if (M == 0) return MX_OK;
   if (!a_bf16 || !w_prep || !c_bf16) return MX_ERR_NULL;
   if (!aligned16(a_bf16) || !aligned16(w_prep) || !aligned16(c_bf16)) return MX_ERR_ALIGN;
@@ -134,8 +146,8 @@ mx_status mx_a16w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, in
 mx_status mx_a4w4_gemm_grouped(const void* a_bf16, const int32_t* row_token, const int32_t* expert_offsets,
                                int64_t E, int64_t R_max, const void* w_prep_stacked, void* c_bf16,
                                int64_t T, int64_t N, int64_t K, int64_t rows_hint, hipStream_t stream) {
-  if (E < 1 || T < 0 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1 ||
-      T > (1ll << 31) - 1)
+  if (E < 1 || T < 0 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > kMaxRows ||
+      T > kMaxRows)
     return MX_ERR_SHAPE;
   if (!expert_offsets || !w_prep_stacked) return MX_ERR_NULL;
   if (R_max > 0 && (!row_token || !c_bf16)) return MX_ERR_NULL;
@@ -154,8 +166,8 @@ mx_status mx_a4w4_gemm_grouped_act_quant(const void* a_bf16, const int32_t* row_
                                          const int32_t* expert_offsets, int64_t E, int64_t R_max,
                                          const void* w_prep_stacked, int64_t T, int64_t N, int64_t K, int32_t act,
                                          int64_t rows_hint, void* h_fp4, void* h_scale, hipStream_t stream) {
-  if (E < 1 || T < 0 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1 ||
-      T > (1ll << 31) - 1 || (act != MX_ACT_SILU && act != MX_ACT_SWIGLU))
+  if (E < 1 || T < 0 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > kMaxRows ||
+      T > kMaxRows || (act != MX_ACT_SILU && act != MX_ACT_SWIGLU))
     return MX_ERR_SHAPE;
   if (!expert_offsets || !w_prep_stacked) return MX_ERR_NULL;
   if (R_max > 0 && (!row_token || !h_fp4 || !h_scale)) return MX_ERR_NULL;
@@ -174,7 +186,7 @@ mx_status mx_a4w4_gemm_grouped_act_quant(const void* a_bf16, const int32_t* row_
 mx_status mx_a4w4_gemm_grouped_mx(const void* a_fp4, const void* a_scale, const int32_t* expert_offsets, int64_t E,
                                   int64_t R_max, const void* w_prep_stacked, void* c_bf16, int64_t N, int64_t K,
                                   int64_t rows_hint, hipStream_t stream) {
-  if (E < 1 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (E < 1 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > kMaxRows) return MX_ERR_SHAPE;
   if (!expert_offsets || !w_prep_stacked) return MX_ERR_NULL;
   if (R_max > 0 && (!a_fp4 || !a_scale || !c_bf16)) return MX_ERR_NULL;
   if ((a_fp4 && !aligned16(a_fp4)) || (a_scale && !aligned16(a_scale)) || !aligned16(w_prep_stacked) ||
@@ -199,8 +211,8 @@ mx_status mx_a4w4_gemm_grouped_mx_plan(int64_t N, int64_t K, int64_t rows_hint, 
 
 mx_status mx_moe_combine(const void* y_bf16, int64_t R, const int32_t* token_rows, const float* token_weights,
                          int64_t T, int64_t topk, int64_t N, void* out_bf16, hipStream_t stream) {
-  if (R < 0 || T < 0 || topk < 1 || topk > 1024 || N <= 0 || N % 8 != 0 || R > (1ll << 31) - 1 ||
-      T > (1ll << 31) - 1 || N > (1ll << 30) || T * (N / 8) > (1ll << 39))
+  if (R < 0 || T < 0 || topk < 1 || topk > 1024 || N <= 0 || N % 8 != 0 || R > kMaxRows ||
+      T > kMaxRows || N > (1ll << 30) || T * (N / 8) > (1ll << 39))
     return MX_ERR_SHAPE;
   if (T == 0) return MX_OK;
   if (!token_rows || !token_weights || !out_bf16 || (R > 0 && !y_bf16)) return MX_ERR_NULL;
@@ -214,7 +226,7 @@ mx_status mx_moe_combine(const void* y_bf16, int64_t R, const int32_t* token_row
 
 mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int32_t act,
                                               int64_t rows_hint, char* buf, size_t buf_len) {
-  if (E < 1 || R_max < 0 || E > (1 << 20) || R_max > (1ll << 31) - 1 || !gemm_shape_ok(N, K) ||
+  if (E < 1 || R_max < 0 || E > (1 << 20) || R_max > kMaxRows || !gemm_shape_ok(N, K) ||
       (act != MX_ACT_SILU && act != MX_ACT_SWIGLU))
     return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;
@@ -226,14 +238,14 @@ mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t E, int64_t R_max, int64_t 
 }
 
 mx_status mx_a16w4_gemm_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
-  if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (M < 0 || !gemm_shape_ok(N, K) || M > kMaxRows) return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;
   mx::a16w4_plan(M, N, K, buf, buf_len);
   return MX_OK;
 }
 
 mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_bytes, char* buf, size_t buf_len) {
-  if (M < 0 || !gemm_shape_ok(N, K) || M > (1ll << 31) - 1) return MX_ERR_SHAPE;
+  if (M < 0 || !gemm_shape_ok(N, K) || M > kMaxRows) return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;
   if (M == 0) {
     std::snprintf(buf, buf_len, "none");
@@ -248,8 +260,8 @@ mx_status mx_a4w4_gemm_plan(int64_t M, int64_t N, int64_t K, size_t workspace_by
 
 mx_status mx_a4w4_gemm_grouped_plan(int64_t E, int64_t R_max, int64_t T, int64_t N, int64_t K,
                                     int64_t rows_hint, char* buf, size_t buf_len) {
-  if (E < 1 || T < 0 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > (1ll << 31) - 1 ||
-      T > (1ll << 31) - 1)
+  if (E < 1 || T < 0 || R_max < 0 || !gemm_shape_ok(N, K) || E > (1 << 20) || R_max > kMaxRows ||
+      T > kMaxRows)
     return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;
   if (R_max == 0) {

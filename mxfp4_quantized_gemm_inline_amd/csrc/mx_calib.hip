@@ -5,6 +5,7 @@
 
 #include "mx_calib.h"
 #include "mx_device.h"
+#include "mx_internal.h"
 
 namespace {
 
@@ -59,6 +60,8 @@ extern "C" mx_status mx_calib_read(const void* buf, size_t bytes, int64_t ctas, 
   if (!buf || !sink) return MX_ERR_NULL;
   if (bytes == 0 || bytes % 16 != 0 || ctas < 1 || ctas > kMaxCtas) return MX_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0) return MX_ERR_ALIGN;
+  const mx_status d = mx::check_device();
+  if (d != MX_OK) return d;
   hipLaunchKernelGGL(k_calib_read, dim3((unsigned)ctas), dim3(kThreads), 0, stream,
                      static_cast<const u32x4*>(buf), bytes / 16, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_HIP;
@@ -68,6 +71,8 @@ extern "C" mx_status mx_calib_mfma(int64_t ctas, int64_t iters, void* sink, hipS
   if (!sink) return MX_ERR_NULL;
   if (ctas < 1 || ctas > kMaxCtas || iters < 1 || iters > kMaxIters) return MX_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return MX_ERR_ALIGN;
+  const mx_status d = mx::check_device();
+  if (d != MX_OK) return d;
   hipLaunchKernelGGL(k_calib_mfma, dim3((unsigned)ctas), dim3(kThreads), 0, stream, (int)iters,
                      static_cast<float*>(sink));
   return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_HIP;

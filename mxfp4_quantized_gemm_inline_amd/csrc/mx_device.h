@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -137,6 +139,31 @@ __device__ __forceinline__ void zero_block(uint32_t (&x)[16]) {
   for (int i = 0; i < 16; ++i) x[i] = 0u;
 }
 
+// ------------------------------------------------------------------ launch helpers
+
+// Tile order: CTAs are dealt round-robin to the 8 XCDs (blockIdx % 8), each with its own
+// L2, so CTA i is given logical tile (its XCD's contiguous share) and logical tiles walk
+// GM tile-rows at a time; the CTAs resident on one XCD then share activation rows and
+// weight columns in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int i, int total, int tiles_m, int tiles_n, int GM, int& bm,
+                                            int& bn) {
+  const int q = total / 8, r = total % 8;
+  const int x = i % 8, j = i / 8;
+  const int logical = x * q + min(x, r) + j;
+  const int gsize = GM * tiles_n;
+  const int grp = logical / gsize, first = grp * GM;
+  const int gm = min(tiles_m - first, GM);
+  const int rem = logical - grp * gsize;
+  bm = first + rem % gm;
+  bn = rem / gm;
+}
+
+template <int N_, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) { (f(std::integral_constant<int, I>{}), ...); }(
+      std::make_integer_sequence<int, N_>{});
+}
+
 // ------------------------------------------------------------------ MFMA
 
 // acc += (a * 2^(sa-127)) (16 x 128 FP4, rows) times (b * 2^(sb-127)) (128 x 16 FP4, cols).
@@ -151,6 +178,14 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f acc,
 // Same, with the scales taken from byte SA of sa and byte SB of sb (the op_sel fields).
 template <int SA, int SB>
 __device__ __forceinline__ v4f mfma_fp4_sel(const uint4& a, const uint4& b, v4f acc, uint32_t sa, uint32_t sb) {
+  v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, SA, (int)sa, SB, (int)sb);
+}
+
+// Same on native 4 x 32-bit vectors (what LDS and global loads of 16 bytes return).
+template <int SA, int SB>
+__device__ __forceinline__ v4f mfma_fp4_sel(const u32x4& a, const u32x4& b, v4f acc, uint32_t sa, uint32_t sb) {
   v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, SA, (int)sa, SB, (int)sb);

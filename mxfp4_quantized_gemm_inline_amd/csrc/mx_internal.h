@@ -5,10 +5,19 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "mx.h"
+
 namespace mx {
+
+// MX_OK when the current device is gfx950, else MX_ERR_DEVICE (MX_ERR_HIP if it cannot be
+// queried); cached per device.
+mx_status check_device();
 
 hipError_t launch_quant_act(const void* a, int64_t M, int64_t K, void* q, void* s, hipStream_t st);
 hipError_t launch_prepare(const void* w, int64_t N, int64_t K, void* wp, hipStream_t st);
+// The prepared layout for N rows (N % 64 == 0) of which the first `valid` are read from w; the
+// rest encode as zero blocks.
+hipError_t launch_prepare_rows(const void* w, int64_t valid, int64_t N, int64_t K, void* wp, hipStream_t st);
 hipError_t launch_prepare_packed(const void* q, const void* s, int64_t N, int64_t K, void* wp, hipStream_t st);
 hipError_t launch_unprepare(const void* wp, int64_t N, int64_t K, void* q, void* s, hipStream_t st);
 hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K,
@@ -31,6 +40,17 @@ hipError_t launch_a16w4(const void* a, const void* wp, void* c, int64_t M, int64
 bool a16w4_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t len);
 hipError_t launch_moe_combine(const void* y, int64_t R, const int32_t* rows, const float* w, int64_t T, int64_t topk,
                               int64_t N, void* out, hipStream_t st);
+// Quantize-once GEMM (mx_gemm_qo.hip): the activations are laid out in the prepared layout in
+// ws (qo_act_bytes(M, K) bytes) by k_prepare, then k_gemm_qo<WM, WN, MT, NG, NBUF, OCC>
+// multiplies the two prepared operands.
+size_t qo_act_bytes(int64_t M, int64_t K);
+bool qo_supported(int WM, int WN, int MT, int NG, int NBUF, int OCC);
+hipError_t launch_gemm_qo(int WM, int WN, int MT, int NG, int NBUF, int OCC, const void* a, const void* wp, void* c,
+                          int64_t M, int64_t N, int64_t K, int GM, void* ws, hipStream_t st);
+// The same with k_gemm_qw<NGT, NBUF>: 128 x 16 NGT tiles, N a multiple of 16 NGT.
+bool qw_supported(int NGT, int NBUF);
+hipError_t launch_gemm_qw(int NGT, int NBUF, const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K,
+                          int GM, void* ws, hipStream_t st);
 // Name the kernel(s) the launchers above would run (false: the tuning override is invalid).
 bool gemm_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes, char* buf, size_t len);
 bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t T, int64_t rows_hint, char* buf,

@@ -42,8 +42,11 @@ __global__ __launch_bounds__(256) void k_quant_act(const uint16_t* __restrict__ 
 
 // One thread per (column-group quad q, step t, lane): quantizes the four 32-blocks that lane
 // owns in column groups 4q..4q+3 at step t and writes them and their scale word in place.
+// Rows n >= valid (padding up to a whole quad of groups) are not read and encode as zero
+// blocks with scale byte 0. The same kernel lays out activation rows in this layout for the
+// quantize-once GEMM (rows = M padded to a multiple of 64, valid = M).
 __global__ __launch_bounds__(256) void k_prepare(const uint16_t* __restrict__ W,
-                                                  uint8_t* __restrict__ Wp, int N, int K) {
+                                                  uint8_t* __restrict__ Wp, int N, int K, int valid) {
   const int T = steps_of(K), Q = N / 64;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)Q * T * 64) return;
@@ -57,7 +60,8 @@ __global__ __launch_bounds__(256) void k_prepare(const uint16_t* __restrict__ W,
     const int g = 4 * q + j;
     const int n = 16 * g + (lane & 15);
     uint32_t x[16];
-    load_block(W + (size_t)n * K + (size_t)kb * kBlock, x);
+    if (n < valid) load_block(W + (size_t)n * K + (size_t)kb * kBlock, x);
+    else zero_block(x);
     uint32_t qq[4];
     const uint32_t sc = quant_block(x, qq);
     *reinterpret_cast<uint4*>(Wp + wp_payload_off(g, t, lane, T)) = make_uint4(qq[0], qq[1], qq[2], qq[3]);
@@ -318,31 +322,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // straight from global memory (a contiguous 1 KiB each) and its activation operands from
 // LDS. Global loads run PF steps ahead of the MFMAs (activations in PF register slots,
 // weights in PF + 1). A tile whose columns run past N (BN not dividing N) masks whole
-// column groups.
-//
-// Tile order: CTAs are dealt round-robin to the 8 XCDs (blockIdx % 8), each with its own
-// L2, so CTA i is given logical tile (its XCD's contiguous share) and logical tiles walk
-// GM tile-rows at a time; the CTAs resident on one XCD then share activation rows and
-// weight columns in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int i, int total, int tiles_m, int tiles_n, int GM, int& bm,
-                                            int& bn) {
-  const int q = total / 8, r = total % 8;
-  const int x = i % 8, j = i / 8;
-  const int logical = x * q + min(x, r) + j;
-  const int gsize = GM * tiles_n;
-  const int grp = logical / gsize, first = grp * GM;
-  const int gm = min(tiles_m - first, GM);
-  const int rem = logical - grp * gsize;
-  bm = first + rem % gm;
-  bn = rem / gm;
-}
-
-template <int N_, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  [&]<int... I>(std::integer_sequence<int, I...>) { (f(std::integral_constant<int, I>{}), ...); }(
-      std::make_integer_sequence<int, N_>{});
-}
-
+// column groups. Tiles are dealt to CTAs in the XCD-aware order of tile_coords.
 template <int WM, int WN, int MT, int NG>
 struct TileShape {
   static constexpr int MTC = MT * WM;  // 16-row tiles per CTA
@@ -1123,178 +1103,6 @@ __global__ __launch_bounds__(256) void k_moe_combine(const uint16_t* __restrict_
   *reinterpret_cast<uint4*>(out + (size_t)t * N + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-// ====================================================================== wide-tile GEMM (large M)
-//
-// One wave per SIMD, four waves side by side along N: a CTA owns a BM x BN tile with
-// BM = 16 * MT rows and BN = 64 * NG columns, each wave MT x NG MFMA tiles (accumulators
-// live in the unified register file, 4 * MT * NG per lane). Wide N per CTA cuts both the
-// activation re-reads (each bf16 A row is read N / BN times) and the redundant inline
-// quantization (about 208 / BN of the MFMA time). With MT = 8 and NG = ceil(G / 64) the
-// tile grid is 16 x 16 for M = 2048, one tile per CU.
-//
-// Software pipeline, per K step t: the MFMAs of step t are issued in the same stretch of
-// code as the quantization of step t+1 (whose bf16 loads were issued a step earlier), so a
-// single wave keeps the matrix core and the vector ALU busy together; then the step-(t+1)
-// operands go to LDS, loads for step t+2 are issued, one barrier, and the step-(t+1)
-// activation operands are read back. Weight operands for step t+1 load straight into
-// registers one step ahead. Column groups past N (a tail tile) re-load the last group and
-// are never stored; rows past M re-read row M-1 and are never stored.
-//
-// The activation store to LDS is bank-conflict free: thread (wave v, lane l) quantizes row
-// 16 * (tile) + (l % 16), block l / 16, so a wave writes 64 consecutive 16-byte slots.
-template <int MT, int NG>
-__global__ __launch_bounds__(256) void k_gemm_wide(const uint16_t* __restrict__ A,
-                                                   const uint8_t* __restrict__ Wp,
-                                                   uint16_t* __restrict__ C, int M, int N, int K,
-                                                   int GM) {
-  constexpr int BM = 16 * MT, BNG = 4 * NG;   // rows, column groups per CTA
-  constexpr int NBLK = 4 * BM;                // 32-blocks of A per K step
-  static_assert(NBLK % 256 == 0, "every thread quantizes the same number of blocks");
-  constexpr int BPT = NBLK / 256;             // blocks per thread per step (= MT / 4)
-  __shared__ __align__(16) uint8_t sq[2][MT * 64 * 16];
-  __shared__ __align__(16) uint8_t ss[2][MT * 64];
-
-  const int T = steps_of(K), G = N / 16;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (G + BNG - 1) / BNG;
-  int bm, bn;
-  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, GM, bm, bn);
-  const int m0 = bm * BM;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw0 = bn * BNG + w * NG;
-  const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
-
-  // thread -> (16-row tile, row, block): consecutive lanes write consecutive LDS slots
-  const uint8_t* __restrict__ A8 = reinterpret_cast<const uint8_t*>(A);
-  uint32_t aoff[BPT];
-  int aslot[BPT];
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    const int tile = w + 4 * i;                 // 16-row tile index within the CTA
-    const int r = 16 * tile + (lane & 15);
-    aslot[i] = tile * 64 + lane;                // = tile*64 + (r%16) + 16*block
-    aoff[i] = (uint32_t)((size_t)min(m0 + r, M - 1) * K * 2 + (lane >> 4) * kBlock * 2);
-  }
-  // Column-group bases are wave-uniform (scalar registers); only the lane offset is per lane.
-  constexpr int NQ = (NG + 3) / 4;
-  const uint8_t* wbase[NG];
-  const uint8_t* sbase[NQ];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) wbase[g] = Wp + (size_t)min(gw0 + g, G - 1) * T * 1024;
-#pragma unroll
-  for (int qi = 0; qi < NQ; ++qi) sbase[qi] = Wsc + (size_t)min((gw0 >> 2) + qi, G / 4 - 1) * T * 256;
-  const uint32_t wlane = lane * 16, slane = lane * 4;
-  const int sbyte = gw0 & 3;
-
-  uint32_t areg[BPT][16];
-  uint4 wq[2][NG];
-  uint32_t wsw[2][NQ];
-  uint4 af[MT];
-  uint32_t asc[MT];
-
-  auto load_a = [&](int t) {
-    const uint8_t* base = A8 + (size_t)t * kStepK * 2;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) load_block_at(base, aoff[i], areg[i]);
-  };
-  auto load_w = [&](int t, auto slot_c) {
-    constexpr int SL = decltype(slot_c)::value;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) wq[SL][g] = *reinterpret_cast<const uint4*>(wbase[g] + (size_t)t * 1024 + wlane);
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi) wsw[SL][qi] = *reinterpret_cast<const uint32_t*>(sbase[qi] + (size_t)t * 256 + slane);
-  };
-  auto quant_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      uint32_t q[4];
-      const uint32_t sc = quant_block(areg[i], q);
-      *reinterpret_cast<uint4*>(&sq[buf][aslot[i] * 16]) = make_uint4(q[0], q[1], q[2], q[3]);
-      ss[buf][aslot[i]] = (uint8_t)sc;
-    }
-  };
-  auto read_frags = [&](int buf) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      af[mt] = *reinterpret_cast<const uint4*>(&sq[buf][(mt * 64 + lane) * 16]);
-      asc[mt] = ss[buf][mt * 64 + lane];
-    }
-  };
-
-  v4f acc[NG][MT];
-#pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // prologue: step 0 quantized and its operands read; step 1 loads in flight
-  load_a(0);
-  load_w(0, std::integral_constant<int, 0>{});
-  quant_store(0);
-  load_a(min(1, T - 1));
-  load_w(min(1, T - 1), std::integral_constant<int, 1>{});
-  __syncthreads();
-  read_frags(0);
-
-  auto mfmas = [&](auto sw_c) {
-    constexpr int SW = decltype(sw_c)::value;
-    static_for<NG>([&](auto g_c) {
-      constexpr int g = decltype(g_c)::value;
-      if constexpr (NG % 4 == 0) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[g][mt] = mfma_fp4_sel<g & 3, 0>(wq[SW][g], af[mt], acc[g][mt], wsw[SW][g >> 2], asc[mt]);
-      } else {
-        const uint32_t sw = wsw[SW][0] >> (8 * (sbyte + g));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[g][mt] = mfma_fp4(wq[SW][g], af[mt], acc[g][mt], sw, asc[mt]);
-      }
-    });
-  };
-  // One step t that has a successor: its MFMAs and step t+1's quantization in one basic
-  // block (so they can be interleaved), then the step-(t+2) loads, one barrier, and the
-  // step-(t+1) activation operands.
-  // Scheduling fences keep the phases in order, so the compiler cannot hoist the next
-  // step's loads above this step's MFMAs (which would double the live operand registers).
-  auto step = [&](int t, auto sw_c) {
-    mfmas(sw_c);
-    quant_store((t + 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    const int tn = min(t + 2, T - 1);  // past the end: a harmless re-load of the last step
-    load_a(tn);
-    load_w(tn, sw_c);                  // the slot step t just consumed
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    read_frags((t + 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  int t = 0;
-  for (; t + 2 < T; t += 2) {  // straight-line body: both steps have a successor
-    step(t, std::integral_constant<int, 0>{});
-    step(t + 1, std::integral_constant<int, 1>{});
-  }
-  if (t + 1 < T) {  // two steps left
-    step(t, std::integral_constant<int, 0>{});
-    mfmas(std::integral_constant<int, 1>{});
-  } else {          // one step left
-    mfmas(std::integral_constant<int, 0>{});
-  }
-
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    if (gw0 + g < G) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = m0 + 16 * mt + (lane & 15);
-        const int n = 16 * (gw0 + g) + 4 * (lane >> 4);
-        if (m < M)
-          *reinterpret_cast<uint2*>(C + (size_t)m * N + n) =
-              pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
-      }
-    }
-  }
-}
-
 // ====================================================================== grouped MoE GEMM1
 //
 // Expert-segmented A4W4 GEMM: output row r (expert-sorted) = Q(A[row_token[r]]) Q(W_e)^T.
@@ -1401,9 +1209,14 @@ hipError_t launch_quant_act(const void* a, int64_t M, int64_t K, void* q, void* 
 }
 
 hipError_t launch_prepare(const void* w, int64_t N, int64_t K, void* wp, hipStream_t st) {
+  return launch_prepare_rows(w, N, N, K, wp, st);
+}
+
+hipError_t launch_prepare_rows(const void* w, int64_t valid, int64_t N, int64_t K, void* wp, hipStream_t st) {
   const int64_t n = (N / 64) * steps_of((int)K) * 64;
+  if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_prepare, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(w), static_cast<uint8_t*>(wp), (int)N, (int)K);
+                     static_cast<const uint16_t*>(w), static_cast<uint8_t*>(wp), (int)N, (int)K, (int)valid);
   return hipGetLastError();
 }
 
@@ -1447,20 +1260,20 @@ size_t stream_lds_bytes(int M, int TS, int MT, int NG, int WK) {
 // ---------------------------------------------------------------- configurations
 struct GemmConfig {
   bool tile = false;
-  bool wide = false;                     // wide-tile kernel (uses MT, NG, GM)
   int MT = 1, NG = 1, WK = 4, S = 1;     // streaming kernel (S = K slices)
   int WM = 1, WN = 4, PF = 2, GM = 8;    // tiled kernel (uses MT, NG too)
   int OCC = 1;                           // tiled kernel: minimum waves per SIMD asked of the compiler
   bool sweep = false;                    // short-K sweep kernel (uses J, GM)
   int J = 1;                             // sweep kernel: column tiles per CTA
+  bool qo = false;                       // quantize-once path (uses WM, WN, MT, NG, NBUF, OCC, GM)
+  int NBUF = 4;                          // quantize-once kernel: LDS stage buffers
+  int NGT = 0;                           // > 0: the wide-tile quantize-once kernel (uses NBUF, GM)
 };
 
 #define MX_STREAM_CONFIGS(X) \
   X(1, 1, 2) X(1, 1, 4) X(1, 1, 8) X(1, 2, 4) X(1, 2, 8) X(1, 4, 4) X(1, 4, 8) \
   X(2, 1, 2) X(2, 1, 4) X(2, 1, 8) X(2, 2, 4) X(2, 2, 8) X(2, 4, 4) X(2, 4, 8) \
   X(4, 1, 4) X(4, 1, 8) X(4, 2, 4) X(4, 4, 4) X(8, 1, 4) X(8, 2, 4)
-
-#define MX_WIDE_CONFIGS(X) X(8, 2) X(8, 4) X(4, 4) X(4, 8)
 
 // short-K sweep kernel: (K steps T, weight prefetch depth PF in steps, column tiles per CTA
 // J); the CTA is 8 waves of 64 x 32 (128-row tiles, 128-column tiles)
@@ -1533,7 +1346,7 @@ template <int WM, int WN, int MT, int NG, int PF, int OCC>
 hipError_t run_tile(const void* a, const void* wp, void* c, float* P, int M, int N, int K, int GM, int S,
                     hipStream_t st) {
   constexpr int BM = 16 * MT * WM, BN = 16 * NG * WN;
-  const int64_t grid = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t grid = ((int64_t)M + BM - 1) / BM * ((N + BN - 1) / BN);
   const int T = steps_of(K);
   if (!P) S = 1;
   const int TS = (T + S - 1) / S;
@@ -1549,17 +1362,6 @@ hipError_t run_tile(const void* a, const void* wp, void* c, float* P, int M, int
   return hipGetLastError();
 }
 
-template <int MT, int NG>
-hipError_t run_wide(const void* a, const void* wp, void* c, int M, int N, int K, int GM, hipStream_t st) {
-  constexpr int BM = 16 * MT, BNG = 4 * NG;
-  const int G = N / 16;
-  const int64_t grid = (int64_t)((M + BM - 1) / BM) * ((G + BNG - 1) / BNG);
-  hipLaunchKernelGGL((k_gemm_wide<MT, NG>), dim3((unsigned)grid), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(a), static_cast<const uint8_t*>(wp),
-                     static_cast<uint16_t*>(c), M, N, K, GM);
-  return hipGetLastError();
-}
-
 template <int T, int PF, int J>
 hipError_t run_sweep(const void* a, const void* wp, void* c, int M, int N, int K, int GM, hipStream_t st) {
   using S = SweepShape<2, 4, 4, 2, T, PF>;
@@ -1568,7 +1370,7 @@ hipError_t run_sweep(const void* a, const void* wp, void* c, int M, int N, int K
   static std::atomic<uint64_t> configured{0};
   hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(kern), configured);
   if (e != hipSuccess) return e;
-  const int64_t grid = (int64_t)((M + S::BM - 1) / S::BM) * ((N / S::BN + J - 1) / J);
+  const int64_t grid = ((int64_t)M + S::BM - 1) / S::BM * ((N / S::BN + J - 1) / J);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(S::NTH), S::SMEM, st, static_cast<const uint16_t*>(a),
                      static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), M, N, GM);
   return hipGetLastError();
@@ -1588,13 +1390,6 @@ int sweep_pf(int T) {
   return 0;
 }
 
-bool wide_supported(int MT, int NG) {
-#define X(mt, ng) if (MT == mt && NG == ng) return true;
-  MX_WIDE_CONFIGS(X)
-#undef X
-  return false;
-}
-
 bool stream_supported(int MT, int NG, int WK) {
 #define X(mt, ng, wk) if (MT == mt && NG == ng && WK == wk) return true;
   MX_STREAM_CONFIGS(X)
@@ -1612,16 +1407,12 @@ bool tile_supported(const GemmConfig& c) {
 
 hipError_t run_config(const GemmConfig& c, const void* a, const void* wp, void* out, float* P, int M,
                       int N, int K, hipStream_t st) {
+  if (c.qo && c.NGT > 0) return launch_gemm_qw(c.NGT, c.NBUF, a, wp, out, M, N, K, c.GM, P, st);
+  if (c.qo) return launch_gemm_qo(c.WM, c.WN, c.MT, c.NG, c.NBUF, c.OCC, a, wp, out, M, N, K, c.GM, P, st);
   if (c.sweep) {
     const int T = steps_of(K);
 #define X(t, pf, j) if (T == t && c.J == j) return run_sweep<t, pf, j>(a, wp, out, M, N, K, c.GM, st);
     MX_SWEEP_CONFIGS(X)
-#undef X
-    return hipErrorInvalidValue;
-  }
-  if (c.wide) {
-#define X(mt, ng) if (c.MT == mt && c.NG == ng) return run_wide<mt, ng>(a, wp, out, M, N, K, c.GM, st);
-    MX_WIDE_CONFIGS(X)
 #undef X
     return hipErrorInvalidValue;
   }
@@ -1698,23 +1489,38 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   // tiled kernel: 64 x 256 tiles when there are enough of them (two steps of prefetch only
   // for long K at moderate sizes), else 64 x 128 tiles at one CTA per SIMD set
   c.tile = true;
+  // Many rows and long K: quantize the activations once into the workspace and multiply the
+  // two prepared operands (k_gemm_qo), when the caller offers that workspace and the 128 x 128
+  // tiles number at least 150. 256 x 256 tiles when one round of them nearly fills the chip
+  // (N=7168, K=4224, M=2048: 224 tiles), 128 x 128 otherwise. Measured against the inline
+  // kernels (cold buffers): 8448 x 7168 M=2048 141 -> 95 us, M=512 55 -> 35 us; 7168 x 4224
+  // M=2048 61 -> 44 us, M=512 26 -> 22 us; 1536 x 7168 M=2048 39 -> 32 us. At M=512 with
+  // N=1536 (48 tiles) the inline kernel with K slices stays ahead (21 against 28 us).
+  const int64_t t256 = ((int64_t)M + 255) / 256 * ((N + 255) / 256);
+  const int64_t t128 = ((int64_t)M + 127) / 128 * ((N + 127) / 128);
+  if (M >= 512 && T >= 16 && t128 >= 150 && qo_act_bytes(M, K) <= ws_bytes) {
+    c.qo = true; c.GM = 8; c.OCC = 2;
+    if (t256 >= 200 && t256 <= 256) { c.WM = 2; c.WN = 4; c.MT = 8; c.NG = 4; c.NBUF = 4; }
+    else { c.WM = 2; c.WN = 2; c.MT = 4; c.NG = 4; c.NBUF = 4; }
+    return c;
+  }
   // short K and enough rows: each 128-row tile quantized once and swept over four 128-column
   // tiles, when that still gives about 200 CTAs or more (N=7168, K=768, M=2048: 224)
-  const int64_t sweeps = (int64_t)((M + 127) / 128) * ((N / 128 + 3) / 4);
+  const int64_t sweeps = ((int64_t)M + 127) / 128 * ((N / 128 + 3) / 4);
   if (sweep_supported(T, 4) && sweeps >= 200) {
     c.sweep = true; c.J = 4; c.GM = 8;
     return c;
   }
   // 128 x 512 tiles (eight waves of 128 x 64) halve the load instructions per output; they
   // pay when one round of them (at most one per CU) nearly fills the chip
-  const int64_t tiles512 = (int64_t)((M + 127) / 128) * (N / 512);
+  const int64_t tiles512 = ((int64_t)M + 127) / 128 * (N / 512);
   if (N % 512 == 0 && tiles512 >= 160 && tiles512 <= 256) {
     c.WM = 1; c.WN = 8; c.MT = 8; c.NG = 4; c.PF = 1; c.GM = 8; c.OCC = 2;
     return c;
   }
   c.WM = 1; c.WN = 4; c.MT = 4;
-  const int64_t tiles256 = (int64_t)((M + 63) / 64) * ((N + 255) / 256);
-  const int64_t tiles128 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
+  const int64_t tiles256 = ((int64_t)M + 63) / 64 * ((N + 255) / 256);
+  const int64_t tiles128 = ((int64_t)M + 63) / 64 * ((N + 127) / 128);
   if (tiles256 >= 150) {
     c.NG = 4; c.GM = 8; c.OCC = 2;
     c.PF = K <= 1024 || G >= 512 || (M >= 1024 && G >= 256) ? 1 : 2;
@@ -1725,8 +1531,8 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   // bf16 activation rows that every 64-column tile re-reads through L2 stay modest (at most
   // 160 MB in all: 22 MB at 7168 x 768 and 121 MB at 7168 x 4224 for M = 128 gained 13% and
   // 6%; 242 MB at 8448 x 7168 took 41 us against 22.6 us for K slices)
-  const int64_t tiles64 = (int64_t)((M + 63) / 64) * (N / 64);
-  const int64_t reread = (int64_t)(N / 64) * ((M + 63) / 64 * 64) * K * 2;
+  const int64_t tiles64 = ((int64_t)M + 63) / 64 * (N / 64);
+  const int64_t reread = (int64_t)(N / 64) * (((int64_t)M + 63) / 64 * 64) * K * 2;
   if (tiles64 >= 200 && reread <= (int64_t)160 << 20) {
     c.NG = 1; c.PF = 2; c.GM = 8; c.OCC = 2;
     return c;
@@ -1749,7 +1555,9 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
 }
 
 // Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming), "t,WM,WN,MT,NG,PF,GM[,OCC[,S]]" (tiled,
-// S = K slices), "k,J,GM" (short-K sweep, J column tiles per CTA) or "w,MT,NG,GM" (wide-tile)
+// S = K slices), "k,J,GM" (short-K sweep, J column tiles per CTA), "q,WM,WN,MT,NG,NBUF,OCC,GM"
+// (quantize-once: k_prepare of the activations into the workspace, then k_gemm_qo), "w,NGT,NBUF,GM"
+// (the same with k_gemm_qw, 128 x 16 NGT tiles)
 // replaces the default choice. Returns 0 when unset, 1 when applied, -1 when the string
 // does not name a compiled configuration (the call then fails rather than silently
 // running something else).
@@ -1761,11 +1569,16 @@ int override_config(GemmConfig& c) {
   if (e[0] == 's' && std::sscanf(e, "s,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3]) == 4) {
     o.tile = false; o.MT = v[0]; o.NG = v[1]; o.WK = v[2]; o.S = v[3];
     if (!stream_supported(o.MT, o.NG, o.WK) || o.S < 1) return -1;
+  } else if (e[0] == 'q' && std::sscanf(e, "q,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5],
+                                         &v[6]) == 7) {
+    o.tile = true; o.qo = true; o.WM = v[0]; o.WN = v[1]; o.MT = v[2]; o.NG = v[3]; o.NBUF = v[4]; o.OCC = v[5];
+    o.GM = v[6] < 1 ? 1 : v[6];
+    if (!qo_supported(o.WM, o.WN, o.MT, o.NG, o.NBUF, o.OCC)) return -1;
+  } else if (e[0] == 'w' && std::sscanf(e, "w,%d,%d,%d", &v[0], &v[1], &v[2]) == 3) {
+    o.tile = true; o.qo = true; o.NGT = v[0]; o.NBUF = v[1]; o.GM = v[2] < 1 ? 1 : v[2];
+    if (!qw_supported(o.NGT, o.NBUF)) return -1;
   } else if (e[0] == 'k' && std::sscanf(e, "k,%d,%d", &v[0], &v[1]) == 2) {
     o.tile = true; o.sweep = true; o.J = v[0]; o.GM = v[1] < 1 ? 1 : v[1];
-  } else if (e[0] == 'w' && std::sscanf(e, "w,%d,%d,%d", &v[0], &v[1], &v[2]) == 3) {
-    o.tile = true; o.wide = true; o.MT = v[0]; o.NG = v[1]; o.GM = v[2] < 1 ? 1 : v[2];
-    if (!wide_supported(o.MT, o.NG)) return -1;
   } else if (e[0] == 't' && std::sscanf(e, "t,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5],
                                          &v[6], &v[7]) >= 6) {
     o.tile = true; o.WM = v[0]; o.WN = v[1]; o.MT = v[2]; o.NG = v[3]; o.PF = v[4]; o.GM = v[5] < 1 ? 1 : v[5];
@@ -1781,10 +1594,16 @@ int override_config(GemmConfig& c) {
 
 }  // namespace
 
+// Workspace a configuration needs: split-K partials, or the quantized activations of the
+// quantize-once kernel.
+size_t config_workspace(const GemmConfig& c, int64_t M, int64_t N, int64_t K) {
+  if (c.qo) return qo_act_bytes(M, K);
+  return c.S > 1 ? (size_t)c.S * (size_t)M * (size_t)N * 4 : 0;
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0) return 0;
-  const GemmConfig c = select_config((int)M, (int)N, (int)K, (size_t)-1);
-  return c.S > 1 ? (size_t)c.S * (size_t)M * (size_t)N * 4 : 0;
+  return config_workspace(select_config((int)M, (int)N, (int)K, (size_t)-1), M, N, K);
 }
 
 namespace {
@@ -1798,7 +1617,9 @@ bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
   const int ov = override_config(cfg);
   if (ov < 0) return false;
   if (ov > 0 && cfg.sweep && (!sweep_supported(steps_of(K), cfg.J) || N % 128 != 0)) return false;
-  if (ov > 0 && cfg.tile && !cfg.wide && cfg.S > 1) {
+  if (ov > 0 && cfg.qo && qo_act_bytes(M, K) > ws_bytes) return false;
+  if (ov > 0 && cfg.qo && cfg.NGT > 0 && N % (16 * cfg.NGT) != 0) return false;
+  if (ov > 0 && cfg.tile && cfg.S > 1) {
     const int T = steps_of(K);
     if (cfg.S > T) cfg.S = T;
     if ((size_t)cfg.S * M * N * 4 > ws_bytes) return false;
@@ -1823,18 +1644,21 @@ hipError_t launch_gemm(const void* a, const void* wp, void* c, int64_t M64, int6
   if (!ws) ws_bytes = 0;
   GemmConfig cfg;
   if (!resolve_config(M, N, K, ws_bytes, cfg)) return hipErrorInvalidValue;
-  return run_config(cfg, a, wp, c, cfg.S > 1 ? static_cast<float*>(ws) : nullptr, M, N, K, st);
+  return run_config(cfg, a, wp, c, (cfg.S > 1 || cfg.qo) ? static_cast<float*>(ws) : nullptr, M, N, K, st);
 }
 
 bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf, size_t len) {
   const int M = (int)M64, N = (int)N64, K = (int)K64;
   GemmConfig c;
   if (!resolve_config(M, N, K, ws_bytes, c)) return false;
-  if (c.sweep) {
+  if (c.qo && c.NGT > 0) {
+    std::snprintf(buf, len, "k_prepare + k_gemm_qw<%d, %d> GM=%d", c.NGT, c.NBUF, c.GM);
+  } else if (c.qo) {
+    std::snprintf(buf, len, "k_prepare + k_gemm_qo<%d, %d, %d, %d, %d, %d> GM=%d", c.WM, c.WN, c.MT, c.NG, c.NBUF,
+                  c.OCC, c.GM);
+  } else if (c.sweep) {
     const int T = steps_of(K);
     std::snprintf(buf, len, "k_gemm_sweep<2, 4, 4, 2, %d, %d, %d> GM=%d", T, sweep_pf(T), c.J, c.GM);
-  } else if (c.wide) {
-    std::snprintf(buf, len, "k_gemm_wide<%d, %d> GM=%d", c.MT, c.NG, c.GM);
   } else if (c.tile) {
     const int T = steps_of(K), TS = (T + c.S - 1) / c.S, S = (T + TS - 1) / TS;  // as run_tile slices
     char split[40] = "";

@@ -75,10 +75,20 @@ def dense_activation_cached(name: str, M: int):
     return W.dense_activation(M, K, structure, m_max=max(max(ms), M))
 
 
-def sample_rows(M: int, n: int = 48, seed: int = 0) -> np.ndarray:
-    """All rows when M is small, else the first, the last and a spread of the rest."""
+def sample_rows(M: int, n: int = 48, seed: int = 0, tile: int | None = 64) -> np.ndarray:
+    """All rows when M is small, else the first, the last, one seeded row inside every
+    `tile`-row tile (so no row tile of any dense kernel goes unchecked: the tiled kernels use
+    16-, 64-, 128- and 256-row tiles, all multiples or divisors of 64 that align with it) and
+    a seeded spread of the rest, at least n rows in all. tile=None skips the per-tile rows
+    (grouped outputs, whose tiles follow the expert segments and are covered by one row of
+    every segment instead)."""
     if M <= n:
         return np.arange(M)
     rng = np.random.default_rng(seed)
-    mid = rng.choice(np.arange(1, M - 1), size=n - 2, replace=False)
-    return np.unique(np.concatenate([[0, M - 1], mid]))
+    per_tile = [] if tile is None else [t0 + int(rng.integers(0, min(tile, M - t0))) for t0 in range(0, M, tile)]
+    picked = set([0, M - 1] + per_tile)
+    rest = np.setdiff1d(np.arange(1, M - 1), np.fromiter(picked, dtype=np.int64))
+    extra = max(0, n - len(picked))
+    if extra and rest.size:
+        picked.update(int(r) for r in rng.choice(rest, size=min(extra, rest.size), replace=False))
+    return np.array(sorted(picked))

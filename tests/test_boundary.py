@@ -123,8 +123,21 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     assert mx.mx_a4w4_gemm_plan(1, 7168, 768).startswith("k_gemm_stream<1, ")
     assert mx.mx_a4w4_gemm_plan(2048, 7168, 768) == "k_gemm_sweep<2, 4, 4, 2, 6, 9, 4> GM=8"
     assert mx.mx_a4w4_gemm_plan(1024, 7168, 768) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
-    assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_gemm_tile<1, 8, 8, 4, 1, 2> GM=8"
-    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
+    # many rows at long K: the activations are quantized once into the workspace (k_prepare),
+    # then both prepared operands are multiplied (k_gemm_qo); without that workspace the
+    # inline kernels run
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_prepare + k_gemm_qo<2, 4, 8, 4, 4, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(512, 8448, 7168) == "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224, workspace_bytes=0) == "k_gemm_tile<1, 8, 8, 4, 1, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=0) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
+    # the quantize-once workspace: the activations of M rows padded to 64, in the prepared layout
+    assert mx.mx_a4w4_gemm_workspace_bytes(2048, 8448, 7168) == 2048 * 7168 * 17 // 32
+    assert mx.mx_a4w4_gemm_workspace_bytes(520, 8448, 7168) == 576 * 7168 * 17 // 32
+    ws = mx.mx_a4w4_gemm_workspace_bytes(2048, 8448, 7168)
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=ws - 1).startswith("k_gemm_tile<")
+    # N = 1536 at M = 512 gives 48 tiles of 128 x 128: too few, K slices keep it inline
+    assert "k_gemm_qo" not in mx.mx_a4w4_gemm_plan(512, 1536, 7168)
     # mid M: 64 x 64 tiles while the activation re-reads stay modest, K slices beyond
     assert mx.mx_a4w4_gemm_plan(128, 7168, 768) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
     assert mx.mx_a4w4_gemm_plan(100, 7168, 4224) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
@@ -148,6 +161,15 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     monkeypatch.setenv("MX_GEMM_CONFIG", "k,3,8")
     with pytest.raises(mx.MxError):
         mx.mx_a4w4_gemm_plan(2048, 7168, 768)
+    # the quantize-once kernel can be forced (it needs its workspace) at any shape
+    monkeypatch.setenv("MX_GEMM_CONFIG", "q,2,2,4,4,5,2,3")
+    ws = 64 * 768 * 17 // 32
+    assert mx.mx_a4w4_gemm_plan(37, 768, 768, ws) == "k_prepare + k_gemm_qo<2, 2, 4, 4, 5, 2> GM=3"
+    with pytest.raises(mx.MxError):
+        mx.mx_a4w4_gemm_plan(37, 768, 768, ws - 1)
+    monkeypatch.setenv("MX_GEMM_CONFIG", "q,2,2,4,4,9,2,3")  # not compiled
+    with pytest.raises(mx.MxError):
+        mx.mx_a4w4_gemm_plan(37, 768, 768, ws)
 
 
 def test_a16w4_plan_names_the_selected_kernel():
@@ -289,3 +311,78 @@ def test_a16w4_argument_errors():
     assert f(A, None, Cp, 4, 256, 256, None) == mx.MX_ERR_NULL
     assert f(A, B, None, 4, 256, 256, None) == mx.MX_ERR_NULL
     assert f(MIS, B, Cp, 4, 256, 256, None) == mx.MX_ERR_ALIGN
+
+
+def _meta(shape, dtype):
+    import torch
+    return torch.empty(shape, dtype=dtype, device="meta")
+
+
+def test_binding_checks_sizes_before_any_pointer_is_taken():
+    """Every wrapper validates shapes and sizes from tensor metadata before it takes a device
+    pointer: a short weight blob, output or table would be read or written out of bounds by
+    kernels that receive only pointers and sizes. Shape-only ("meta") tensors reach these
+    checks without any device; a well-sized one then fails only for not being on a device."""
+    torch = pytest.importorskip("torch")
+    bf, u8, i32, f32 = torch.bfloat16, torch.uint8, torch.int32, torch.float32
+    N, K, M = 512, 768, 40
+    wbytes = mx.mx_prepared_weight_bytes(N, K)
+    a, c = _meta((M, K), bf), _meta((M, N), bf)
+    size_err = "needs at least|must have shape|must be 2-D|need at least"
+    # dense GEMM and A16WFP4: the weight blob and the output
+    for fn in (mx.mx_a4w4_gemm, mx.mx_a16w4_gemm):
+        with pytest.raises(ValueError, match=size_err):
+            fn(a, _meta((wbytes - 16,), u8), N, out=c)
+        with pytest.raises(ValueError, match=size_err):
+            fn(a, _meta((wbytes,), u8), N, out=_meta((M, N - 8), bf))
+        with pytest.raises(ValueError, match=size_err):
+            fn(_meta((M * K,), bf), _meta((wbytes,), u8), N, out=c)
+        with pytest.raises(TypeError):
+            fn(a, _meta((wbytes,), torch.int8), N, out=c)
+        with pytest.raises(ValueError, match="device tensor"):   # sizes fine: only the device is missing
+            fn(a, _meta((wbytes,), u8), N, out=c)
+    # prepare / unprepare / standalone quantizer
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_prepare_weight(_meta((N, K), bf), out=_meta((wbytes - 1,), u8))
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_prepare_weight_packed(_meta((N, K // 2), u8), _meta((N, K // 32 - 1), u8))
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_prepare_weight_packed(_meta((N, K // 2), u8), _meta((N, K // 32), u8), out=_meta((wbytes - 1,), u8))
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_unprepare_weight(_meta((wbytes - 1,), u8), N, K)
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_quant_act(a, q_out=_meta((M, K // 2 - 1), u8), s_out=_meta((M, K // 32), u8))
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_quant_act(a, q_out=_meta((M, K // 2), u8), s_out=_meta((M - 1, K // 32), u8))
+    # grouped calls: segment table, row map, stacked weights, outputs
+    E, R, T, Nh = 6, 100, 20, N // 2
+    at, rt, of = _meta((T, K), bf), _meta((R,), i32), _meta((E + 1,), i32)
+    wst = _meta((E * wbytes,), u8)
+    for bad in (dict(row_token=_meta((R - 1,), i32)), dict(expert_offsets=_meta((E,), i32)),
+                dict(w_prep_stacked=_meta((E * wbytes - 1,), u8)), dict(out=_meta((R, N - 8), bf))):
+        args = dict(row_token=rt, expert_offsets=of, w_prep_stacked=wst, out=_meta((R, N), bf))
+        args.update(bad)
+        with pytest.raises(ValueError, match=size_err):
+            mx.mx_a4w4_gemm_grouped(at, args["row_token"], args["expert_offsets"], E, R, args["w_prep_stacked"], N,
+                                    out=args["out"])
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_a4w4_gemm_grouped_act_quant(at, rt, of, E, R, wst, N, h_fp4=_meta((R, Nh // 2 - 1), u8),
+                                          h_scale=_meta((R, Nh // 32), u8))
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_a4w4_gemm_grouped_act_quant(at, rt, _meta((E,), i32), E, R, wst, N)
+    K2, N2 = 256, 512
+    w2 = _meta((E * mx.mx_prepared_weight_bytes(N2, K2),), u8)
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_a4w4_gemm_grouped_mx(_meta((R - 1, K2 // 2), u8), _meta((R - 1, K2 // 32), u8), of, E, R, w2, N2)
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_a4w4_gemm_grouped_mx(_meta((R, K2 // 2), u8), _meta((R, K2 // 32), u8), of, E, R, w2[:-1], N2)
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_a4w4_gemm_grouped_mx(_meta((R, K2 // 2), u8), _meta((R, K2 // 32), u8), of, E, R, w2, N2,
+                                   out=_meta((R - 1, N2), bf))
+    # combine
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_moe_combine(_meta((R, N2), bf), _meta((T, 16), i32), _meta((T, 15), f32))
+    with pytest.raises(ValueError, match=size_err):
+        mx.mx_moe_combine(_meta((R, N2), bf), _meta((T, 16), i32), _meta((T, 16), f32), out=_meta((T, N2 - 8), bf))
+    with pytest.raises(TypeError):
+        mx.mx_moe_combine(_meta((R, N2), bf), _meta((T, 16), torch.int64), _meta((T, 16), f32))

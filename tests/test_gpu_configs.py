@@ -1,5 +1,6 @@
 """Every compiled GEMM configuration (streaming kernel with and without K slices, tiled
-kernel with and without masked tail tiles, several tile orders) against the oracle.
+kernel with and without masked tail tiles, several tile orders, the short-K sweep kernel and
+the quantize-once kernel) against the oracle.
 
 The library's tuning override (environment variable MX_GEMM_CONFIG) forces each
 configuration; an override that does not name a compiled, feasible configuration fails
@@ -23,7 +24,8 @@ STREAM = [(1, 1, 2), (1, 1, 4), (1, 1, 8), (1, 2, 4), (1, 2, 8), (1, 4, 4), (1, 
 TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8, 1, 1), (1, 4, 4, 2, 2, 1),
         (1, 4, 4, 4, 1, 2), (1, 4, 4, 4, 2, 2), (2, 4, 4, 4, 1, 1), (1, 4, 4, 2, 2, 2),
         (1, 8, 8, 4, 1, 2), (1, 4, 4, 1, 2, 1), (1, 4, 4, 1, 2, 2)]
-WIDE = [(8, 2), (8, 4), (4, 4), (4, 8)]
+# mirrors MX_QO_CONFIGS in mx_gemm_qo.hip: (WM, WN, MT, NG, NBUF, OCC)
+QO = [(2, 4, 8, 4, 4, 2), (2, 2, 4, 4, 4, 2), (2, 2, 4, 4, 5, 2), (1, 4, 8, 4, 3, 2)]
 SWEEP_K = (256, 512, 768, 1024)  # the short-K sweep kernel's compiled step counts 2, 4, 6, 8
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
 K_TESTS = (4224, 768)  # 33 and 6 steps of 128
@@ -105,15 +107,49 @@ def test_tile_split_needs_workspace():
         del os.environ["MX_GEMM_CONFIG"]
 
 
-@pytest.mark.parametrize("K", K_TESTS)
-@pytest.mark.parametrize("cfg", WIDE, ids=[f"w{c}" for c in WIDE])
-def test_wide_config(cfg, K):
+@pytest.mark.parametrize("K", K_TESTS + (7168,))
+@pytest.mark.parametrize("cfg", QO, ids=[f"q{c}" for c in QO])
+def test_quantize_once_config(cfg, K):
+    """The quantize-once kernel (activations quantized once into the workspace, then two
+    prepared operands multiplied) on a ragged last row tile (300 rows: 256 + 44, or 2 x 128 +
+    44), a tile of fewer rows than one 64-row quad (37), several tile orders, tail column tiles
+    (N = 768 = 3 x 256) and canary rows past M. Its per-element sum runs over K steps in order,
+    as in the tiled inline kernel, so the two are also compared bit for bit."""
     torch = torch_or_skip()
+    mx = lib_or_fail()
     a, wp, exact = _case(K)
-    for M, gm in ((300, 8), (37, 1), (129, 3)):
-        c = _run(f"w,{cfg[0]},{cfg[1]},{gm}", a[:M], wp, False)
+    for M, gm in ((300, 8), (37, 1), (256, 3)):
+        full = torch.full((M + 5, N_TEST), -7.0, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty((M + 63) // 64 * 64 * K * 17 // 32, dtype=torch.uint8, device="cuda")
+        os.environ["MX_GEMM_CONFIG"] = "q," + ",".join(map(str, cfg)) + f",{gm}"
+        try:
+            mx.mx_a4w4_gemm(dev_bf16(a[:M]), wp, N_TEST, out=full[:M], workspace=ws)
+        finally:
+            del os.environ["MX_GEMM_CONFIG"]
         torch.cuda.synchronize()
-        check_gemm(c, exact[:M], what=f"wide {cfg} GM={gm} M={M} K={K}")
+        got = host_bits(full[:M])
+        check_gemm(got, exact[:M], what=f"quantize-once {cfg} GM={gm} M={M} K={K}")
+        assert bool((full[M:] == -7.0).all()), f"quantize-once {cfg} M={M} K={K}: rows past M were written"
+        inline = _run("t,1,4,4,4,1,8,2", a[:M], wp, False)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, inline), f"quantize-once {cfg} M={M} K={K}: differs from the inline kernel"
+
+
+def test_quantize_once_needs_workspace():
+    """A forced quantize-once configuration without room for the quantized activations fails
+    instead of running."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    a, wp, _ = _case(4224)
+    os.environ["MX_GEMM_CONFIG"] = "q,2,2,4,4,4,2,8"
+    try:
+        with pytest.raises(mx.MxError):
+            mx.mx_a4w4_gemm(dev_bf16(a[:64]), wp, N_TEST, workspace=False)
+        small = torch.empty(64 * 4224 * 17 // 32 - 16, dtype=torch.uint8, device="cuda")
+        with pytest.raises(mx.MxError):
+            mx.mx_a4w4_gemm(dev_bf16(a[:64]), wp, N_TEST, workspace=small)
+    finally:
+        del os.environ["MX_GEMM_CONFIG"]
 
 
 @pytest.mark.parametrize("K", SWEEP_K)

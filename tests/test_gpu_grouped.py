@@ -10,23 +10,63 @@ from gpu_util import check_gemm, dev_bf16, host_bits, lib_or_fail, sample_rows, 
 
 pytestmark = pytest.mark.gpu
 
-_stack = {"experts": set(), "buf": None}
+_stack = {"experts": set(), "buf": None, "rows": {}}
+CHECK_COLS = 32  # output columns of the one-row-per-expert checks: one MXFP4 block of h
 
 
 def stacked_weights(experts):
     """Stacked prepared weights of all E experts; only the listed ones are filled
-    (the others are never read by a launch whose table leaves them empty)."""
+    (the others are never read by a launch whose table leaves them empty). While each
+    expert's weight is at hand, the rows the one-row-per-expert checks need are kept:
+    W rows 0..31 (output columns 0..31) and 768..799 (the up columns paired with gate
+    columns 0..31)."""
     torch = torch_or_skip()
     mx = lib_or_fail()
     per = mx.mx_prepared_weight_bytes(W.MOE_N, W.MOE_K)
     if _stack["buf"] is None:
         _stack["buf"] = torch.zeros(W.MOE_E * per, dtype=torch.uint8, device="cuda")
     need = sorted(set(int(e) for e in experts) - _stack["experts"])
+    half = W.MOE_N // 2
     for e, w in W.moe_expert_weights(need):
         mx.mx_prepare_weight(dev_bf16(w), out=_stack["buf"][e * per:(e + 1) * per])
+        _stack["rows"][e] = (w[:CHECK_COLS].copy(), w[half:half + CHECK_COLS].copy())
         _stack["experts"].add(e)
     torch.cuda.synchronize()
     return _stack["buf"]
+
+
+def expert_first_rows(e):
+    """W_e rows 0..31: the weight of output columns 0..31 (kept by stacked_weights)."""
+    return _stack["rows"][int(e)][0]
+
+
+def expert_gate_up_rows(e):
+    """W_e rows 0..31 (gate) stacked on rows 768..799 (their up partners): a 64-row weight
+    whose SwiGLU output is h columns 0..31."""
+    lo, up = _stack["rows"][int(e)]
+    return np.concatenate([lo, up])
+
+
+def per_expert_exact(a, row_token, offs, rows):
+    """Exact GEMM1 output columns 0..31 of the given rows (at most one per expert): the same
+    steps as the oracle's grouped reference (quantize the token's row and the expert's weight
+    rows, exact product), with each expert's quantized weight rows kept across calls."""
+    qcache = _stack.setdefault("q", {})
+    expert_of = np.searchsorted(np.asarray(offs, dtype=np.int64), rows, side="right") - 1
+    out = np.empty((len(rows), CHECK_COLS))
+    for i, (r, e) in enumerate(zip(rows, expert_of)):
+        if int(e) not in qcache:
+            qcache[int(e)] = O.quantize_mx(expert_first_rows(e))
+        qa, sa = O.quantize_mx(a[int(row_token[r])][None, :])
+        out[i] = O.gemm_from_mx(qa, sa, *qcache[int(e)])[0]
+    return out
+
+
+def one_row_per_expert(offs, seed):
+    """A seeded row inside every non-empty segment."""
+    rng = np.random.default_rng(seed)
+    return np.array([int(offs[e]) + int(rng.integers(0, offs[e + 1] - offs[e]))
+                     for e in np.flatnonzero(np.diff(offs) > 0)], dtype=np.int64)
 
 
 def rows_hint(T):
@@ -49,9 +89,14 @@ def test_grouped_matches_oracle(T):
     c = host_bits(out)
     torch.cuda.synchronize()
     assert np.all(c[R:] == host_bits(torch.full((1,), 5.0, dtype=torch.bfloat16))[0])
-    rows = sample_rows(R, n=64, seed=T)
+    rows = sample_rows(R, n=24, seed=T, tile=None)
     exact = O.grouped_gemm_ref(a, row_token, offs, W.moe_expert_weight, rows=rows)
     check_gemm(c[rows], exact, what=f"grouped T={T}")
+    # one row of every active expert (its first 32 output columns): a wrong expert or unit
+    # lookup for any segment would show
+    rows = one_row_per_expert(offs, seed=10 + T)
+    exact = per_expert_exact(a, row_token, offs, rows)
+    check_gemm(c[rows, :CHECK_COLS], exact, what=f"grouped T={T}, one row per active expert ({rows.size})")
 
 
 @pytest.mark.parametrize("hint", [1, 20, 64, 100])
@@ -68,7 +113,7 @@ def test_grouped_tiling_hint_only_changes_tiling(hint):
                                           torch.from_numpy(offs).cuda(), W.MOE_E, R, wst, W.MOE_N,
                                           rows_hint=hint))
     torch.cuda.synchronize()
-    rows = sample_rows(R, n=32, seed=hint)
+    rows = sample_rows(R, n=16, seed=hint, tile=None)
     exact = O.grouped_gemm_ref(a, row_token, offs, W.moe_expert_weight, rows=rows)
     check_gemm(c[rows], exact, what=f"grouped hint={hint}")
 

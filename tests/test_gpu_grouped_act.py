@@ -14,7 +14,8 @@ from oracle import mx_act_oracle as AO
 from oracle import mx_oracle as O
 
 from gpu_util import dev_bf16, host_u8, lib_or_fail, sample_rows, torch_or_skip
-from test_gpu_grouped import _ragged_case, rows_hint, stacked_weights
+from test_gpu_grouped import (CHECK_COLS, _ragged_case, expert_first_rows, expert_gate_up_rows, one_row_per_expert,
+                               rows_hint, stacked_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,9 +54,14 @@ def test_swiglu_quant_matches_oracle(T):
     torch.cuda.synchronize()
     q, s = host_u8(hq), host_u8(hs)
     assert np.all(q[R:] == 0xAB) and np.all(s[R:] == 0xCD)       # rows >= R untouched
-    rows = sample_rows(R, n=24, seed=100 + T)
+    rows = sample_rows(R, n=16, seed=100 + T, tile=None)
     _check(q, s, a, row_token, offs, W.moe_expert_weight, AO.ACT_SWIGLU, rows,
            f"swiglu T={T} ({mx.mx_a4w4_gemm_grouped_act_quant_plan(W.MOE_E, R, W.MOE_N, W.MOE_K, 1, rows_hint(T))})")
+    # one row of every active expert: its first 32-column block of h (gate columns 0..31 with
+    # their up partners 768..799)
+    rows = one_row_per_expert(offs, seed=110 + T)
+    _check(q[:, :CHECK_COLS // 2], s[:, :CHECK_COLS // 32], a, row_token, offs, expert_gate_up_rows, AO.ACT_SWIGLU,
+           rows, f"swiglu T={T}, one row per active expert ({rows.size})")
 
 
 def test_silu_quant_matches_oracle():
@@ -71,8 +77,11 @@ def test_silu_quant_matches_oracle():
                                                act=mx.MX_ACT_SILU, rows_hint=rows_hint(T))
     torch.cuda.synchronize()
     assert hq.shape == (R, W.MOE_N // 2) and hs.shape == (R, W.MOE_N // 32)
-    rows = sample_rows(R, n=16, seed=7)
+    rows = sample_rows(R, n=16, seed=7, tile=None)
     _check(host_u8(hq), host_u8(hs), a, row_token, offs, W.moe_expert_weight, AO.ACT_SILU, rows, "silu T=256")
+    rows = one_row_per_expert(offs, seed=8)  # SiLU: h columns 0..31 from output columns 0..31
+    _check(host_u8(hq)[:, :CHECK_COLS // 2], host_u8(hs)[:, :CHECK_COLS // 32], a, row_token, offs,
+           expert_first_rows, AO.ACT_SILU, rows, f"silu T=256, one row per active expert ({rows.size})")
 
 
 ACT_CONFIGS = ["gt,1,4,4,4,2,2", "gt,1,8,8,4,1,2", "gt,1,4,4,2,2,2"]

@@ -22,10 +22,13 @@ from test_gpu_grouped import _ragged_case
 
 pytestmark = pytest.mark.gpu
 
-_w2 = {"buf": None, "done": set()}
+_w2 = {"buf": None, "done": set(), "rows": {}}
+CHECK_COLS = 32
 
 
 def stacked_w2(experts):
+    """Stacked prepared second-GEMM weights; only the listed experts are filled. Rows 0..31
+    of each (the weight of output columns 0..31) are kept for the one-row-per-expert check."""
     torch = torch_or_skip()
     mx = lib_or_fail()
     per = mx.mx_prepared_weight_bytes(W.MOE_N2, W.MOE_K2)
@@ -35,6 +38,7 @@ def stacked_w2(experts):
     for e in need:
         w = W.moe_expert_weight2(e)
         mx.mx_prepare_weight(dev_bf16(w), out=_w2["buf"][e * per:(e + 1) * per])
+        _w2["rows"][e] = w[:CHECK_COLS].copy()
         _w2["done"].add(e)
     torch.cuda.synchronize()
     return _w2["buf"]
@@ -60,9 +64,15 @@ def test_gemm2_matches_oracle(T):
     c = host_bits(out)
     torch.cuda.synchronize()
     assert np.all(O.bf16_to_f64(c[R:]) == 7.0)
-    rows = sample_rows(R, n=24, seed=300 + T)
+    rows = sample_rows(R, n=16, seed=300 + T, tile=None)
     exact = O.grouped_gemm_mx_ref(aq, as_, offs, W.moe_expert_weight2, rows=rows)
     check_gemm(c[rows], exact, what=f"gemm2 T={T} ({mx.mx_a4w4_gemm_grouped_mx_plan(W.MOE_N2, W.MOE_K2, hint)})")
+    # one row of every active expert, output columns 0..31
+    rng = np.random.default_rng(310 + T)
+    rows = np.array([int(offs[e]) + int(rng.integers(0, offs[e + 1] - offs[e]))
+                     for e in np.flatnonzero(np.diff(offs) > 0)], dtype=np.int64)
+    exact = O.grouped_gemm_mx_ref(aq, as_, offs, lambda e: _w2["rows"][int(e)], rows=rows)
+    check_gemm(c[rows, :CHECK_COLS], exact, what=f"gemm2 T={T}, one row per active expert ({rows.size})")
 
 
 @pytest.mark.parametrize("cfg", ["gt,1,4,4,4,2,2", "gt,1,8,8,4,1,2", "gt,1,4,4,2,2,2", "gk,4", "gk,7", "gk,14"])

@@ -371,3 +371,42 @@ def test_prepared_size_matches_page_figure():
     assert O.prepared_weight_bytes(8448, 7168) == 32_169_984
     # and 2.786 GiB over 93 layers
     assert abs(93 * 32_169_984 / 2 ** 30 - 2.786) < 5e-4
+
+
+def _bf16_fraction(bits: int) -> Fraction:
+    """A bf16 bit pattern decoded from its fields (sign, 8-bit exponent, 7-bit fraction)."""
+    sign = -1 if bits & 0x8000 else 1
+    e, f = (bits >> 7) & 0xFF, bits & 0x7F
+    if e == 0:
+        return sign * Fraction(f, 128) * Fraction(2) ** -126
+    return sign * (1 + Fraction(f, 128)) * Fraction(2) ** (e - 127)
+
+
+def test_bf16_exact_product_against_fraction_sums():
+    """gemm_bf16_exact (the unquantized reference of the relative-L2 context metric) equals
+    the exact rational sum of products of the bf16 inputs decoded from their bit fields, on
+    inputs whose float64 sums are exact (exponents within a narrow range, K = 32) and on a
+    hand-worked case."""
+    rng = np.random.default_rng(11)
+    a = (rng.integers(0x3E00, 0x4080, size=(3, 32)) | (rng.integers(0, 2, size=(3, 32)) << 15)).astype(np.uint16)
+    w = (rng.integers(0x3E00, 0x4080, size=(4, 32)) | (rng.integers(0, 2, size=(4, 32)) << 15)).astype(np.uint16)
+    got = O.gemm_bf16_exact(a, w)
+    for m in range(3):
+        for n in range(4):
+            want = sum((_bf16_fraction(int(x)) * _bf16_fraction(int(y)) for x, y in zip(a[m], w[n])), Fraction(0))
+            assert Fraction(got[m, n]) == want
+    # [1.5, -2] . [0.25, 3] = 0.375 - 6 = -5.625 (0x3FC0 = 1.5, 0xC000 = -2, 0x3E80 = 0.25, 0x4040 = 3)
+    hand = O.gemm_bf16_exact(np.array([[0x3FC0, 0xC000]], dtype=np.uint16), np.array([[0x3E80, 0x4040]], dtype=np.uint16))
+    assert hand.tolist() == [[-5.625]]
+    # a transposed operand would not even have the right shape
+    assert O.gemm_bf16_exact(a, w).shape == (3, 4)
+
+
+def test_relative_l2_hand_values():
+    """rel_l2(x, ref) = ||x - ref||_2 / ||ref||_2: hand-worked values, the argument order, and the
+    zero-reference convention."""
+    assert O.rel_l2(np.array([3.6, 4.8]), np.array([3.0, 4.0])) == pytest.approx(0.2, abs=1e-15)
+    assert O.rel_l2(np.zeros(4), np.array([1.0, 0.0, 0.0, 0.0])) == 1.0
+    assert O.rel_l2(np.array([2.0, 0.0]), np.array([1.0, 0.0])) == 1.0
+    assert O.rel_l2(np.array([1.0, 0.0]), np.array([2.0, 0.0])) == 0.5   # not symmetric
+    assert O.rel_l2(np.ones(3), np.zeros(3)) == 0.0                      # zero reference: defined as 0

@@ -54,3 +54,14 @@ def test_moe_routing():
         assert np.all(np.diff(toks) > 0)
         for t in toks:
             assert e in ids[t]
+
+
+def test_expert_weight_rows_are_a_prefix():
+    """The per-expert row prefix used by the layer-shape parity tests equals the first rows
+    of the full expert weight, for GEMM1 and GEMM2 seeds."""
+    for e in (0, 7, 895):
+        full = W.moe_expert_weight(e)
+        assert np.array_equal(W.moe_expert_weight_rows(e, 64), full[:64])
+        full2 = W.moe_expert_weight2(e)
+        assert np.array_equal(W.moe_expert_weight_rows(e, 32, K=W.MOE_K2, seed_base=W.SEED_EXPERT2_BASE),
+                              full2[:32])

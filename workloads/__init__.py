@@ -168,6 +168,13 @@ def moe_expert_weight(e: int, N: int = MOE_N, K: int = MOE_K) -> np.ndarray:
     return normal_bf16((N, K), SEED_EXPERT_BASE + e, W_STD)
 
 
+def moe_expert_weight_rows(e: int, rows: int, K: int = MOE_K, seed_base: int = SEED_EXPERT_BASE) -> np.ndarray:
+    """The first ``rows`` rows of an expert weight (GEMM1 by default; seed_base =
+    SEED_EXPERT2_BASE with K = MOE_K2 for GEMM2), drawn without the rest: the draws are
+    sequential in row-major order, so this is exactly a prefix of the full matrix."""
+    return normal_bf16((rows, K), seed_base + e, W_STD)
+
+
 # GEMM2 (down projection) of the same layer: h [rows, inter_dim] x W2_e [model_dim, inter_dim]
 MOE_N2 = 3584     # model_dim
 MOE_K2 = 768      # inter_dim
