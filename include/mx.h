@@ -134,6 +134,24 @@ mx_status mx_a4w4_gemm(const void* a_bf16, const void* w_prep, void* c_bf16, int
                        hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under stream capture, tight serving
+ * loops, harnesses that forbid allocation): mx_a4w4_gemm with the plan it runs when handed
+ * mx_a4w4_gemm_workspace_bytes(M, N, K) of workspace, that workspace being the library's own
+ * device array of mx_noalloc_scratch_bytes() bytes (32 MiB), one per GPU, held until the
+ * process ends; the call allocates and frees nothing. Same arguments, shape rules and results
+ * as mx_a4w4_gemm without the workspace pair. MX_ERR_WORKSPACE when the plan needs more than
+ * the array holds (e.g. the quantize-once plan at M * K * 17 / 32 > 32 MiB); nothing is
+ * launched then. Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, threads) race and must be serialized by the caller. Nothing in the
+ * array needs clearing between calls (each plan writes what it reads).
+ */
+mx_status mx_a4w4_gemm_noalloc(const void* a_bf16, const void* w_prep, void* c_bf16, int64_t M,
+                               int64_t N, int64_t K, hipStream_t stream);
+
+/* Size in bytes of the scratch array mx_a4w4_gemm_noalloc uses. Host only. */
+size_t mx_noalloc_scratch_bytes(void);
+
+/*
  * A16WFP4 variant (named in "[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", CI Guide, as
  * outside that change): C[M, N] = A[M, K] x W^T with the bf16 activations NOT quantized and
  * W the prepared MXFP4 weight decoded to real values (E2M1 value x 2^(scale - 127), exact

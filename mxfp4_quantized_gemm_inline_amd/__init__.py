@@ -40,6 +40,8 @@ SIGNATURES = {
     "mx_a4w4_gemm_grouped_mx_plan": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
     "mx_moe_combine": (_c_int, [_vp, _c_i64, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp]),
     "mx_a16w4_gemm": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]),
+    "mx_a4w4_gemm_noalloc": (_c_int, [_vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp]),
+    "mx_noalloc_scratch_bytes": (_c_sz, []),
     "mx_calib_read": (_c_int, [_vp, _c_sz, _c_i64, _vp, _vp]),
     "mx_calib_mfma": (_c_int, [_c_i64, _c_i64, _vp, _vp]),
     "mx_calib_mfma_flops": (ctypes.c_double, [_c_i64, _c_i64]),
@@ -229,6 +231,28 @@ def mx_a4w4_gemm(a_bf16, w_prep, N: int, out=None, workspace=None, stream=None):
                               _dev(c, torch.bfloat16, "c_bf16"), M, int(N), K, ws_ptr, ws_bytes,
                               _stream_ptr(stream)), "mx_a4w4_gemm")
     return c
+
+
+def mx_noalloc_scratch_bytes() -> int:
+    """Size of the device scratch array mx_a4w4_gemm_noalloc uses in place of a workspace."""
+    return int(lib().mx_noalloc_scratch_bytes())
+
+
+def mx_a4w4_gemm_noalloc(a_bf16, w_prep, N: int, out, stream=None):
+    """mx_a4w4_gemm without a caller workspace and without any allocation: the library's own
+    device scratch array serves as the workspace (calls that overlap on one device share it).
+    `out` [M, N] bf16 is required (allocating it here would defeat the purpose)."""
+    torch = _torch()
+    _need(a_bf16, "a_bf16", torch.bfloat16)
+    M, K = _dims2(a_bf16, "a_bf16")
+    _need(w_prep, "w_prep", torch.uint8, min_bytes=max(1, mx_prepared_weight_bytes(N, K)))
+    _need(out, "out", torch.bfloat16, shape=(M, N))
+    if M == 0:
+        return out
+    _check(lib().mx_a4w4_gemm_noalloc(_dev(a_bf16, torch.bfloat16, "a_bf16"), _dev(w_prep, torch.uint8, "w_prep"),
+                                      _dev(out, torch.bfloat16, "c_bf16"), M, int(N), K, _stream_ptr(stream)),
+           "mx_a4w4_gemm_noalloc")
+    return out
 
 
 def _grouped_tables(row_token, expert_offsets, w_prep_stacked, E, R_max, N, K):

@@ -24,7 +24,7 @@ HIP_FLAGS = ["-O3", "-std=c++20", f"--offload-arch={ARCH}", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-fno-gpu-rdc", "-Wall", "-Wno-unused-function"]
 SOURCES = ["mx_kernels.hip", "mx_api.cpp", "mx_calib.hip", "mx_prepare_packed.hip", "mx_a16w4.hip",
-           "mx_gemm_qo.hip"]
+           "mx_gemm_qo.hip", "mx_noalloc.hip"]
 
 
 def hipcc() -> str:
