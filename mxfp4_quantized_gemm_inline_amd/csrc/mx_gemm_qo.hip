@@ -90,25 +90,6 @@ __device__ __forceinline__ void copy4(const uint8_t* g, const uint8_t* l) {
       : "v"(g), "s"(lds_addr(l))
       : "memory");
 }
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset (the
-// saddr form): a kernel with many copy slots then keeps one offset register instead of a
-// 64-bit address per slot.
-__device__ __forceinline__ void copy16s(const uint8_t* base, uint32_t off, const uint8_t* l) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(off), "s"(base), "s"(lds_addr(l))
-      : "memory");
-}
-__device__ __forceinline__ void copy4s(const uint8_t* base, uint32_t off, const uint8_t* l) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "v"(off), "s"(base), "s"(lds_addr(l))
-      : "memory");
-}
 // s_waitcnt immediate for vmcnt(vm) expcnt(7) lgkmcnt(lgkm) (vmcnt split over bits 3:0 and
 // 15:14, expcnt bits 6:4, lgkmcnt bits 11:8).
 constexpr int waitcnt_imm(int vm, int lgkm) {
@@ -274,247 +255,6 @@ void k_gemm_qo(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
   store_tile<S::BM, S::BN, MT, NG, WN>(acc, smem, C, M, N, bm, bn);
 }
 
-// k_gemm_qw: the same product with one 128-row tile of 16 NGT columns per CTA, NGT = N / 256,
-// so that N splits into exactly 16 column tiles and M = 2048 into 16 row tiles: 256 CTAs, one
-// per compute unit, all in one round. (At N = 8448 = 256 x 33 the power-of-two tiles leave
-// 1056 tiles of 128 x 128, which two CTAs per compute unit run in three rounds, the last one
-// nearly empty.) Eight waves as 2 x 4: wave (wm, wn) computes rows 64 wm .. 64 wm + 63 of the
-// tile against the NGW = NGT / 4 column groups from wn NGW; the X = NGT % 4 groups left over
-// are shared out by rows: wave w computes the 16-row block 4 wm + wn (one it already holds)
-// of each of them. Every wave thus issues 4 NGW + X MFMAs per step (33 at NGT = 33). A wave's
-// first group can sit at any byte r of a scale word (a word holds the scales of 4 groups), so
-// the wave reads the NQW words its groups span and realigns them with v_alignbyte (a funnel
-// shift by r bytes), after which group j's scale is byte j % 4 of word j / 4, as in k_gemm_qo.
-// Weight operands go through a ring of RB registers (group g of a step in slot (g + P NGW) %
-// RB, refilled with group g + RB right after group g's MFMAs), so only RB of them are live.
-// Pipeline, copies and waits as in k_gemm_qo.
-template <int NGT, int NBUF>
-struct QWShape {
-  static constexpr int NW = 8, NTH = 512, MT = 4;
-  static constexpr int BM = 128, BN = 16 * NGT;
-  static constexpr int NGW = NGT / 4, X = NGT % 4;          // whole groups per wave, groups shared by rows
-  static constexpr int NQW = (NGW + 6) / 4;                  // scale words a wave's groups span, at most
-  static constexpr int RB = 2;                               // weight operand ring slots
-  static constexpr int GA = BM / 16, GW = NGT;                // 1 KiB operand blocks per stage
-  static constexpr int QA = BM / 64, QW = (NGT + 2) / 4 + 1;  // scale chunks: A; the most quads NGT groups span
-  static constexpr int NB = GA + GW, NS = QA + QW;
-  static constexpr int SC_OFF = NB * 1024;
-  // one more (never copied) chunk: a wave may read a word past the tile's last quad, whose
-  // bytes it never uses
-  static constexpr int STAGE = NB * 1024 + (NS + 1) * 256;
-  static constexpr int BPW = (NB + NW - 1) / NW, SPW = (NS + NW - 1) / NW;  // copy slots per wave
-  static constexpr int CSTAGE = BM * (BN * 2 + 16);
-  static constexpr int SMEM = NBUF * STAGE > CSTAGE ? NBUF * STAGE : CSTAGE;
-  static_assert(NGW >= 2 && NGW >= RB - 1, "ring refills stay within two steps");
-  static_assert((2 * NGW) % RB == 0, "ring slots repeat every two steps");
-  static_assert(NBUF >= 3, "stage t + 1 is read while stage t + NBUF - 1 is being copied");
-  static_assert(SMEM <= 160 * 1024, "the stages and the output staging fit the LDS");
-};
-
-// Ap, Wp, C as for k_gemm_qo; N is a multiple of 16 NGT.
-template <int NGT, int NBUF>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_gemm_qw(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C, int M,
-               int N, int K, int GM) {
-  using S = QWShape<NGT, NBUF>;
-  constexpr int NW = S::NW, GA = S::GA, QA = S::QA, BPW = S::BPW, SPW = S::SPW, STAGE = S::STAGE;
-  constexpr int MT = S::MT, NGW = S::NGW, X = S::X, NQW = S::NQW, RB = S::RB;
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int T = steps_of(K);
-  const int Mp = (M + 63) / 64 * 64;
-  const int GAall = Mp / 16, GWall = N / 16;
-  const int tiles_m = (M + S::BM - 1) / S::BM, tiles_n = N / S::BN;
-  int bm, bn;
-  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, GM, bm, bn);
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w / 4, wn = w % 4;
-  const int g_lo = wn * NGW;                       // the wave's first group in the tile
-  const int gbase = bn * NGT, qbase = gbase >> 2;  // the tile's first group and quad
-  const int r_sh = (gbase + g_lo) & 3;             // byte of the wave's first group's scale
-  const uint32_t l16 = lane * 16, l4 = lane * 4;
-  // LDS offsets (within a stage) of this wave's first weight block and first scale word
-  const uint32_t b_off = (GA + g_lo) * 1024 + l16;
-  const uint32_t s_off = S::SC_OFF + (QA + ((gbase + g_lo) >> 2) - qbase) * 256 + l4;
-
-  // Copy slot i of this wave is block w + NW i (the last slot only where that block exists:
-  // `full` waves issue BPW block copies per step, the others BPW - 1) and scale chunk
-  // min(w + NW i, NS - 1) (an idle chunk slot repeats the last chunk). Sources are wave-uniform
-  // bases (SGPRs); the lane offsets l16 / l4 are the only vector registers the copies use.
-  const bool full = w + NW * (BPW - 1) < S::NB;
-  const uint8_t* src[BPW];
-  int dstb[BPW];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int b = min(w + NW * i, S::NB - 1);
-    dstb[i] = b * 1024;
-    src[i] = b < GA ? Ap + (size_t)min(bm * GA + b, GAall - 1) * T * 1024
-                    : Wp + (size_t)min(gbase + (b - GA), GWall - 1) * T * 1024;
-  }
-  const uint8_t* ssrc[SPW];
-  int dsts[SPW];
-#pragma unroll
-  for (int i = 0; i < SPW; ++i) {
-    const int c = min(w + NW * i, S::NS - 1);
-    dsts[i] = S::SC_OFF + c * 256;
-    ssrc[i] = c < QA ? Ap + payload_bytes(Mp, K) + (size_t)min(bm * QA + c, GAall / 4 - 1) * T * 256
-                     : Wp + payload_bytes(N, K) + (size_t)min(qbase + (c - QA), GWall / 4 - 1) * T * 256;
-  }
-  auto copy_stage = [&](int t, int buf) {
-    uint8_t* L = smem + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < BPW - 1; ++i) copy16s(src[i] + (size_t)t * 1024, l16, L + dstb[i]);
-    if (full) copy16s(src[BPW - 1] + (size_t)t * 1024, l16, L + dstb[BPW - 1]);
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) copy4s(ssrc[i] + (size_t)t * 256, l4, L + dsts[i]);
-  };
-  // the copies of the NBUF - 3 stages after stage t + 2 may stay outstanding (this wave's own
-  // count per stage); lgkmcnt(0): this wave's LDS reads are done
-  auto wait_copies = [&]() {
-    if (full)
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 3) * (BPW + SPW), 0));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm((NBUF - 3) * (BPW - 1 + SPW), 0));
-  };
-
-  v4f acc[NGW][MT], accx[X > 0 ? X : 1];
-#pragma unroll
-  for (int j = 0; j < NGW; ++j)
-#pragma unroll
-    for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int x = 0; x < (X > 0 ? X : 1); ++x) accx[x] = v4f{0.f, 0.f, 0.f, 0.f};
-  // a[P]: step t's activation operands in set P = t % 2 (the next step's are read into the
-  // other set at the start of the step); b: the weight operand ring; scale words
-  // double-buffered by parity.
-  u32x4 a[2][MT], b[RB];
-  uint32_t sa[2], sw[2][NQW];
-  auto rd_a = [&](int buf, int i) {
-    return *reinterpret_cast<const u32x4*>(smem + buf * STAGE + (wm * MT + i) * 1024 + l16);
-  };
-  auto rd_b = [&](int buf, int j) { return *reinterpret_cast<const u32x4*>(smem + buf * STAGE + b_off + j * 1024); };
-  auto rd_scales = [&](int buf, auto r_c) {
-    constexpr int R = decltype(r_c)::value;
-    const uint8_t* L = smem + buf * STAGE;
-    sa[R] = *reinterpret_cast<const uint32_t*>(L + S::SC_OFF + wm * 256 + l4);
-#pragma unroll
-    for (int q = 0; q < NQW; ++q) sw[R][q] = *reinterpret_cast<const uint32_t*>(L + s_off + q * 256);
-  };
-  // group j's scale in byte j % 4: the realigned word j / 4
-  auto wscale = [&](int R, int q) {
-    return __builtin_amdgcn_alignbyte(sw[R][q + 1 < NQW ? q + 1 : q], sw[R][q], (uint32_t)r_sh);
-  };
-  // the shared groups: this wave's 16-row block (4 wm + wn, byte wn of the A scale word) and,
-  // per group, its weight block, scale chunk and byte
-  const int xi = wn;
-  uint32_t xb_off[X > 0 ? X : 1], xs_off[X > 0 ? X : 1], xs_sh[X > 0 ? X : 1];
-#pragma unroll
-  for (int x = 0; x < X; ++x) {
-    const int ge = gbase + 4 * NGW + x;
-    xb_off[x] = (GA + 4 * NGW + x) * 1024 + l16;
-    xs_off[x] = S::SC_OFF + (QA + (ge >> 2) - qbase) * 256 + l4;
-    xs_sh[x] = 8 * (ge & 3);
-  }
-
-  for (int s = 0; s < NBUF - 1; ++s) copy_stage(min(s, T - 1), s);
-  wait_copies();
-  __builtin_amdgcn_s_barrier();
-#pragma unroll
-  for (int i = 0; i < MT; ++i) a[0][i] = rd_a(0, i);
-#pragma unroll
-  for (int g = 0; g < RB; ++g) b[g] = rd_b(0, g);
-  rd_scales(0, std::integral_constant<int, 0>{});
-
-  // Step t (its buffer b0; stage t + 1 in b1, complete since the last barrier): read step
-  // t + 1's activation operands and scale words and this step's shared-group operands, copy
-  // stage t + NBUF - 1 into the buffer of step t - 1, run the MFMAs group by group, then the
-  // shared groups', then wait and meet at the barrier as in k_gemm_qo.
-  auto step = [&](int t, int b0, int b1, int bc, auto par_c) {
-    constexpr int P = decltype(par_c)::value;  // t % 2
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 xb[X > 0 ? X : 1], xa;
-    uint32_t xs[X > 0 ? X : 1];
-    if constexpr (X > 0) xa = rd_a(b0, xi);
-#pragma unroll
-    for (int x = 0; x < X; ++x) {
-      xb[x] = *reinterpret_cast<const u32x4*>(smem + b0 * STAGE + xb_off[x]);
-      xs[x] = *reinterpret_cast<const uint32_t*>(smem + b0 * STAGE + xs_off[x]);
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i) a[P ^ 1][i] = rd_a(b1, i);
-    rd_scales(b1, std::integral_constant<int, P ^ 1>{});
-    copy_stage(min(t + NBUF - 1, T - 1), bc);
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<NGW>([&](auto j_c) {
-      constexpr int j = decltype(j_c)::value, slot = (P * NGW + j) % RB, g2 = j + RB;
-      const uint32_t sc = wscale(P, j >> 2);
-      static_for<MT>([&](auto i_c) {
-        constexpr int i = decltype(i_c)::value;
-        acc[j][i] = mfma_fp4_sel<j & 3, i & 3>(b[slot], a[P][i], acc[j][i], sc, sa[P]);
-      });
-      // the shared groups' MFMAs once their operands (read at the start of the step) are in
-      if constexpr (j == 1) {
-#pragma unroll
-        for (int x = 0; x < X; ++x)
-          accx[x] = mfma_fp4_sel<0, 0>(xb[x], xa, accx[x], xs[x] >> xs_sh[x], sa[P] >> (8 * xi));
-      }
-      // the refill after the group's MFMAs (a fence keeps it there: hoisted above them, the
-      // old and new operand would both be live)
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (g2 < NGW)
-        b[slot] = rd_b(b0, g2);
-      else
-        b[slot] = rd_b(b1, g2 - NGW);
-    });
-    __builtin_amdgcn_sched_barrier(0);
-    wait_copies();
-    __builtin_amdgcn_s_barrier();
-  };
-  int t = 0, b0 = 0;
-  auto nxt = [](int x) { return x + 1 == NBUF ? 0 : x + 1; };
-  auto prv = [](int x) { return x == 0 ? NBUF - 1 : x - 1; };
-  for (; t + 2 <= T; t += 2) {
-    step(t, b0, nxt(b0), prv(b0), std::integral_constant<int, 0>{});
-    b0 = nxt(b0);
-    step(t + 1, b0, nxt(b0), prv(b0), std::integral_constant<int, 1>{});
-    b0 = nxt(b0);
-  }
-  if (t < T) step(t, b0, nxt(b0), prv(b0), std::integral_constant<int, 0>{});
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-  __syncthreads();
-
-  // Epilogue: the tile staged as bf16 in LDS, then whole rows stored 16 bytes per lane; rows
-  // >= M never written.
-  constexpr int CROW = S::BN * 2 + 16;
-#pragma unroll
-  for (int j = 0; j < NGW; ++j)
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int r = 16 * (wm * MT + i) + (lane & 15);
-      const int cl = 16 * (g_lo + j) + 4 * (lane >> 4);
-      *reinterpret_cast<uint2*>(smem + r * CROW + cl * 2) =
-          pack4_bf16(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
-    }
-#pragma unroll
-  for (int x = 0; x < X; ++x) {
-    const int r = 16 * (wm * MT + xi) + (lane & 15);
-    const int cl = 16 * (4 * NGW + x) + 4 * (lane >> 4);
-    *reinterpret_cast<uint2*>(smem + r * CROW + cl * 2) = pack4_bf16(accx[x][0], accx[x][1], accx[x][2], accx[x][3]);
-  }
-  __syncthreads();
-  constexpr int CPR = S::BN / 8, TOT = S::BM * CPR;
-  const int m0 = bm * S::BM, n0 = bn * S::BN;
-#pragma unroll
-  for (int k = 0; k < (TOT + S::NTH - 1) / S::NTH; ++k) {
-    const int id = threadIdx.x + k * S::NTH;
-    const int r = id / CPR, ch = id % CPR;
-    if (id < TOT && m0 + r < M) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * CROW + ch * 16);
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)(m0 + r) * N + n0 + 8 * ch));
-    }
-  }
-}
-
 // ====================================================================== launchers
 
 // Compiled configurations (WM, WN, MT, NG, NBUF, OCC): 256 x 256 as 2 x 4 waves of 128 x 64 (two
@@ -550,47 +290,7 @@ hipError_t run_qo(int id, const void* ap, const void* wp, void* c, int M, int N,
   return hipGetLastError();
 }
 
-// Compiled wide-tile configurations (NGT, NBUF): N = 8448 (33 groups of 16 columns per tile,
-// three stages: 131 KiB) and N = 7168 (28 groups, four stages: 154 KiB).
-#define MX_QW_CONFIGS(X) X(33, 3) X(28, 4)
-
-std::atomic<uint64_t> g_qw_lds[4];
-
-template <int NGT, int NBUF>
-hipError_t run_qw(int id, const void* ap, const void* wp, void* c, int M, int N, int K, int GM, hipStream_t st) {
-  using S = QWShape<NGT, NBUF>;
-  auto kern = k_gemm_qw<NGT, NBUF>;
-  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), S::SMEM, g_qw_lds[id]);
-  if (e != hipSuccess) return e;
-  const int64_t grid = (int64_t)((M + S::BM - 1) / S::BM) * (N / S::BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(S::NTH), S::SMEM, st, static_cast<const uint8_t*>(ap),
-                     static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), M, N, K, GM);
-  return hipGetLastError();
-}
-
 }  // namespace
-
-bool qw_supported(int NGT, int NBUF) {
-#define X(ngt, nb) if (NGT == ngt && NBUF == nb) return true;
-  MX_QW_CONFIGS(X)
-#undef X
-  return false;
-}
-
-hipError_t launch_gemm_qw(int NGT, int NBUF, const void* a, const void* wp, void* c, int64_t M, int64_t N, int64_t K,
-                          int GM, void* ws, hipStream_t st) {
-  if (!qw_supported(NGT, NBUF) || N % (16 * NGT) != 0) return hipErrorInvalidValue;
-  const int64_t Mp = (M + 63) / 64 * 64;
-  hipError_t e = launch_prepare_rows(a, M, Mp, K, ws, st);
-  if (e != hipSuccess) return e;
-  int id = 0;
-#define X(ngt, nb)                                                                              \
-  if (NGT == ngt && NBUF == nb) return run_qw<ngt, nb>(id, ws, wp, c, (int)M, (int)N, (int)K, GM, st); \
-  ++id;
-  MX_QW_CONFIGS(X)
-#undef X
-  return hipErrorInvalidValue;
-}
 
 size_t qo_act_bytes(int64_t M, int64_t K) {
   const int64_t Mp = (M + 63) / 64 * 64;

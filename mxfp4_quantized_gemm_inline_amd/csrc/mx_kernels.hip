@@ -1267,7 +1267,6 @@ struct GemmConfig {
   int J = 1;                             // sweep kernel: column tiles per CTA
   bool qo = false;                       // quantize-once path (uses WM, WN, MT, NG, NBUF, OCC, GM)
   int NBUF = 4;                          // quantize-once kernel: LDS stage buffers
-  int NGT = 0;                           // > 0: the wide-tile quantize-once kernel (uses NBUF, GM)
 };
 
 #define MX_STREAM_CONFIGS(X) \
@@ -1407,7 +1406,6 @@ bool tile_supported(const GemmConfig& c) {
 
 hipError_t run_config(const GemmConfig& c, const void* a, const void* wp, void* out, float* P, int M,
                       int N, int K, hipStream_t st) {
-  if (c.qo && c.NGT > 0) return launch_gemm_qw(c.NGT, c.NBUF, a, wp, out, M, N, K, c.GM, P, st);
   if (c.qo) return launch_gemm_qo(c.WM, c.WN, c.MT, c.NG, c.NBUF, c.OCC, a, wp, out, M, N, K, c.GM, P, st);
   if (c.sweep) {
     const int T = steps_of(K);
@@ -1556,8 +1554,7 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
 
 // Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming), "t,WM,WN,MT,NG,PF,GM[,OCC[,S]]" (tiled,
 // S = K slices), "k,J,GM" (short-K sweep, J column tiles per CTA), "q,WM,WN,MT,NG,NBUF,OCC,GM"
-// (quantize-once: k_prepare of the activations into the workspace, then k_gemm_qo), "w,NGT,NBUF,GM"
-// (the same with k_gemm_qw, 128 x 16 NGT tiles)
+// (quantize-once: k_prepare of the activations into the workspace, then k_gemm_qo)
 // replaces the default choice. Returns 0 when unset, 1 when applied, -1 when the string
 // does not name a compiled configuration (the call then fails rather than silently
 // running something else).
@@ -1574,9 +1571,6 @@ int override_config(GemmConfig& c) {
     o.tile = true; o.qo = true; o.WM = v[0]; o.WN = v[1]; o.MT = v[2]; o.NG = v[3]; o.NBUF = v[4]; o.OCC = v[5];
     o.GM = v[6] < 1 ? 1 : v[6];
     if (!qo_supported(o.WM, o.WN, o.MT, o.NG, o.NBUF, o.OCC)) return -1;
-  } else if (e[0] == 'w' && std::sscanf(e, "w,%d,%d,%d", &v[0], &v[1], &v[2]) == 3) {
-    o.tile = true; o.qo = true; o.NGT = v[0]; o.NBUF = v[1]; o.GM = v[2] < 1 ? 1 : v[2];
-    if (!qw_supported(o.NGT, o.NBUF)) return -1;
   } else if (e[0] == 'k' && std::sscanf(e, "k,%d,%d", &v[0], &v[1]) == 2) {
     o.tile = true; o.sweep = true; o.J = v[0]; o.GM = v[1] < 1 ? 1 : v[1];
   } else if (e[0] == 't' && std::sscanf(e, "t,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5],
@@ -1618,7 +1612,6 @@ bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
   if (ov < 0) return false;
   if (ov > 0 && cfg.sweep && (!sweep_supported(steps_of(K), cfg.J) || N % 128 != 0)) return false;
   if (ov > 0 && cfg.qo && qo_act_bytes(M, K) > ws_bytes) return false;
-  if (ov > 0 && cfg.qo && cfg.NGT > 0 && N % (16 * cfg.NGT) != 0) return false;
   if (ov > 0 && cfg.tile && cfg.S > 1) {
     const int T = steps_of(K);
     if (cfg.S > T) cfg.S = T;
@@ -1651,9 +1644,7 @@ bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf
   const int M = (int)M64, N = (int)N64, K = (int)K64;
   GemmConfig c;
   if (!resolve_config(M, N, K, ws_bytes, c)) return false;
-  if (c.qo && c.NGT > 0) {
-    std::snprintf(buf, len, "k_prepare + k_gemm_qw<%d, %d> GM=%d", c.NGT, c.NBUF, c.GM);
-  } else if (c.qo) {
+  if (c.qo) {
     std::snprintf(buf, len, "k_prepare + k_gemm_qo<%d, %d, %d, %d, %d, %d> GM=%d", c.WM, c.WN, c.MT, c.NG, c.NBUF,
                   c.OCC, c.GM);
   } else if (c.sweep) {

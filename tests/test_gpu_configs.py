@@ -1,6 +1,6 @@
 """Every compiled GEMM configuration (streaming kernel with and without K slices, tiled
 kernel with and without masked tail tiles, several tile orders, the short-K sweep kernel and
-both quantize-once kernels) against the oracle.
+the quantize-once kernel) against the oracle.
 
 The library's tuning override (environment variable MX_GEMM_CONFIG) forces each
 configuration; an override that does not name a compiled, feasible configuration fails
@@ -133,62 +133,6 @@ def test_quantize_once_config(cfg, K):
         inline = _run("t,1,4,4,4,1,8,2", a[:M], wp, False)
         torch.cuda.synchronize()
         assert np.array_equal(got, inline), f"quantize-once {cfg} M={M} K={K}: differs from the inline kernel"
-
-
-# mirrors MX_QW_CONFIGS in mx_gemm_qo.hip: (NGT, NBUF) and the smallest valid N it tiles (a
-# multiple of both 256 and 16 NGT)
-QW = [((33, 3), 8448), ((28, 4), 1792)]
-
-
-@pytest.mark.parametrize("K", (768, 896))
-@pytest.mark.parametrize("cfg,N", QW, ids=[f"w{c}" for c, _ in QW])
-def test_quantize_once_wide_config(cfg, N, K):
-    """The wide-tile quantize-once kernel (128 x 16 NGT tiles; the column groups of each tile
-    start anywhere within a scale word, and at NGT = 33 the last group is shared out by rows)
-    against the oracle and bit for bit against the inline kernel: a ragged last row tile (300 =
-    2 x 128 + 44), a tile of fewer rows than one 64-row quad (37), several tile orders, an even
-    and an odd number of K steps (6, 7), canary rows past M."""
-    torch = torch_or_skip()
-    mx = lib_or_fail()
-    a_all = W.dense_activation(300, K, "outlier_channels", seed=23)
-    w = W.dense_weight(N, K, seed=24)
-    wp = mx.mx_prepare_weight(dev_bf16(w))
-    qw, sw = O.quantize_mx(w)
-    for M, gm in ((300, 16), (37, 1), (256, 3)):
-        a = a_all[:M]
-        full = torch.full((M + 5, N), -7.0, dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty((M + 63) // 64 * 64 * K * 17 // 32, dtype=torch.uint8, device="cuda")
-        os.environ["MX_GEMM_CONFIG"] = f"w,{cfg[0]},{cfg[1]},{gm}"
-        try:
-            mx.mx_a4w4_gemm(dev_bf16(a), wp, N, out=full[:M], workspace=ws)
-        finally:
-            del os.environ["MX_GEMM_CONFIG"]
-        torch.cuda.synchronize()
-        got = host_bits(full[:M])
-        qa, sa = O.quantize_mx(a)
-        check_gemm(got, O.gemm_from_mx(qa, sa, qw, sw), what=f"wide quantize-once {cfg} GM={gm} M={M} K={K}")
-        assert bool((full[M:] == -7.0).all()), f"wide quantize-once {cfg} M={M} K={K}: rows past M were written"
-        os.environ["MX_GEMM_CONFIG"] = "t,1,4,4,4,1,8,2"
-        try:
-            inline = host_bits(mx.mx_a4w4_gemm(dev_bf16(a), wp, N, workspace=False))
-        finally:
-            del os.environ["MX_GEMM_CONFIG"]
-        torch.cuda.synchronize()
-        assert np.array_equal(got, inline), f"wide quantize-once {cfg} M={M} K={K}: differs from the inline kernel"
-
-
-def test_quantize_once_wide_rejects_other_widths():
-    """A wide-tile override whose tile width does not divide N fails instead of running."""
-    torch = torch_or_skip()
-    mx = lib_or_fail()
-    a, wp, _ = _case(768)  # N = 768
-    ws = torch.empty(64 * 768 * 17 // 32, dtype=torch.uint8, device="cuda")
-    os.environ["MX_GEMM_CONFIG"] = "w,33,3,8"
-    try:
-        with pytest.raises(mx.MxError):
-            mx.mx_a4w4_gemm(dev_bf16(a[:64]), wp, N_TEST, workspace=ws)
-    finally:
-        del os.environ["MX_GEMM_CONFIG"]
 
 
 def test_quantize_once_needs_workspace():

@@ -7,8 +7,8 @@
 * Constant: A = 1 and W = 1 everywhere give C = K exactly (768, 4224 and 7168 are bf16 values).
 
 The dense families: the weight-streaming kernel (with and without K slices), the tiled
-kernel's 64 x 256, 128 x 512 and 64 x 64 tiles (and K slices), the short-K sweep kernel, the
-quantize-once kernel's 256 x 256 and 128 x 128 tiles and its wide 128 x 528 / 128 x 448 tiles. The grouped families: the streaming
+kernel's 64 x 256, 128 x 512 and 64 x 64 tiles (and K slices), the short-K sweep kernel and
+the quantize-once kernel's 256 x 256 and 128 x 128 tiles. The grouped families: the streaming
 and the tiled grouped kernels, rows gathered by token over a ragged segment table."""
 import os
 
@@ -87,32 +87,6 @@ def test_constant_probe_every_dense_family(cfg, K, ms, ws_fn):
     for M in ms:
         c = _run_dense(mx, torch, cfg, np.full((M, K), ONE, dtype=np.uint16), wp, N_P, K, ws_fn)
         assert np.all(O.bf16_to_f64(c) == K), f"{cfg} M={M} K={K}"
-
-
-# the wide-tile quantize-once kernel: (override, N, K); K leaves room for the one-hot diagonal
-WIDE = [("w,33,3,16", 8448, 8576), ("w,28,4,4", 1792, 2048)]
-
-
-@pytest.mark.parametrize("cfg,N,K", WIDE, ids=[w[0] for w in WIDE])
-def test_probes_wide_quantize_once(cfg, N, K):
-    """One-hot weight (C = the decoded activation columns k0 .. k0 + N - 1, exactly) and constant
-    probes through the wide-tile quantize-once kernel, every column group of every tile."""
-    torch = torch_or_skip()
-    mx = lib_or_fail()
-    k0 = 128
-    wp = mx.mx_prepare_weight(dev_bf16(_one_hot_weight(N, K, k0)))
-    a_all = W.dense_activation(300, K, "outlier_channels", seed=35)
-    ws_fn = lambda M, K_: (M + 63) // 64 * 64 * K_ * 17 // 32  # noqa: E731
-    for M in (37, 300):
-        a = a_all[:M]
-        c = _run_dense(mx, torch, cfg, a, wp, N, K, ws_fn)
-        qa, sa = O.quantize_mx(a)
-        want = O.dequantize_mx(qa, sa)[:, k0:k0 + N]
-        got = O.bf16_to_f64(c)
-        assert np.array_equal(got, want), f"{cfg} M={M}: {int((got != want).sum())} elements differ"
-    wp1 = mx.mx_prepare_weight(dev_bf16(np.full((N, K), ONE, dtype=np.uint16)))
-    c = _run_dense(mx, torch, cfg, np.full((64, K), ONE, dtype=np.uint16), wp1, N, K, ws_fn)
-    assert np.all(O.bf16_to_f64(c) == K), f"{cfg}: constant probe"
 
 
 GROUPED = ["gs,1,1", "gs,1,4", "gs,2,1", "gs,2,4", "gt,1,4,4,4,1,2", "gt,2,4,4,4,1,1", "gt,1,4,4,4,2,2",
