@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the inline-quantized A4W4 MXFP4 GEMM on one MI355X.
 
-Headline workload (one "step"): the dense GEMM N=7168, K=768 at every M of the
-microbenchmark sweep (1, 8, 32, 128, 512, 2048), one call per M, each with bf16
-activations quantized inside the kernel against a prepared MXFP4 weight; weight
-preparation is outside the timed region, as in "[gfx950][FlyDSL] Add direct dense A4W4
-MXFP4 GEMM", Kernel microbenchmark. Inputs are synthetic (seeded, see workloads/).
+Headline workload (one "step"): the dense GEMM N=8448, K=7168, the largest weight of the
+microbenchmark sweep, at every M of it (1, 8, 32, 128, 512, 2048), one call per M, each with
+bf16 activations quantized by the library (inside the kernel, or once into the workspace at
+large M) against a prepared MXFP4 weight; weight preparation is outside the timed region, as
+in "[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM", Kernel microbenchmark. Inputs are
+synthetic (seeded, see workloads/).
 
-Timing: every timed region is a HIP graph replay bracketed by HIP events on the
-stream the kernels run on. Buffers rotate over R distinct (A, prepared W, C) sets so
-the working set exceeds the 256 MB Infinity Cache ("cold"); single-set ("warm") times
-are reported as context. Per-point times are averages per launch over the replay.
+Timing: every timed region is HIP graph replays bracketed by HIP events on the stream the
+graphs are launched on. Buffers rotate over R distinct (A, prepared W, C) sets so the working
+set exceeds the 256 MB Infinity Cache ("cold"); single-set ("warm") times are reported as
+context. The step is one graph replay per step, each timed: the value is the median step,
+with the spread. Per-point times are the median over 5 replays of a graph of many launches.
 
-Output: one JSON line (rank 0, N=1) with the headline step, the roofline of the
-dominant kernel, the CPU oracle baseline, and the full sweep (all dense points and
-the grouped MoE GEMM1 points) under "sweep".
+Output: one JSON line (rank 0, N=1) with the headline step, the roofline of the dominant
+call, the CPU oracle baseline, and the full sweep (all dense points with their relative L2
+against the unquantized bf16 product, the A16WFP4 variant, and the MoE layer's grouped
+GEMMs) under "sweep".
 """
 from __future__ import annotations
 
@@ -35,9 +38,10 @@ MFMA_FP4_PEAK = 10.1e15      # flop/s, MI355X dense MXFP4
 MFMA_BF16_PEAK = 2.5e15      # flop/s, MI355X dense bf16 (the A16WFP4 variant's MFMA)
 MALL_BYTES = 256 << 20       # Infinity Cache
 ROTATE_TARGET = 1 << 30      # bytes touched per rotation cycle (4x the Infinity Cache)
-HEADLINE = "n7168_k768"
-# The pages' direct-kernel median times for this workload ("[gfx950][FlyDSL] Add direct
-# dense A4W4 MXFP4 GEMM", Kernel microbenchmark table), summed over the M sweep.
+HEADLINE = "n8448_k7168"
+REPLAYS = 5                  # graph replays per sweep point (median and spread)
+# The pages' direct-kernel median times ("[gfx950][FlyDSL] Add direct dense A4W4 MXFP4 GEMM",
+# Kernel microbenchmark table); the headline compares against their sum over its M sweep.
 PAGE_US = {("n7168_k768", 1): 12.580, ("n7168_k768", 8): 11.921, ("n7168_k768", 32): 12.120,
            ("n7168_k768", 128): 12.380, ("n7168_k768", 512): 15.520, ("n7168_k768", 2048): 31.700,
            ("n7168_k4224", 1): 15.960, ("n7168_k4224", 8): 23.041, ("n7168_k4224", 32): 23.520,
@@ -124,11 +128,17 @@ class DensePoint:
         return lambda: self.mx.mx_a4w4_gemm(a, w, self.N, out=c)
 
 
+def replay_stats(timer, g, launches, replays=REPLAYS):
+    """(median, min, max) microseconds per launch over `replays` timed replays of g."""
+    per = sorted(timer.replay_ms(g, reps=1) * 1e3 / launches for _ in range(replays))
+    return per[len(per) // 2], per[0], per[-1]
+
+
 def time_point(timer, pt, launches=200):
     g = timer.graph([pt.launch(i) for i in range(launches)])
-    ms = timer.replay_ms(g, reps=3)
+    st = replay_stats(timer, g, launches)
     del g
-    return ms * 1e3 / launches  # us per launch
+    return st
 
 
 def calibrate(torch, mx, timer):
@@ -161,12 +171,15 @@ def calibrate(torch, mx, timer):
             "cus": cus}
 
 
-def point_record(name, N, K, M, us_cold, us_warm, kernel=None):
+def point_record(name, N, K, M, cold, us_warm, kernel=None):
+    """cold: (median, min, max) us per launch over the replays."""
+    us_cold = cold[0]
     B, F = algo_bytes(M, N, K), algo_flops(M, N, K)
     t_hbm, t_mfma = B / HBM_PEAK * 1e6, F / MFMA_FP4_PEAK * 1e6
     rec = {
         "workload": name, "N": N, "K": K, "M": M,
-        "us": round(us_cold, 3), "us_warm": round(us_warm, 3),
+        "us": round(us_cold, 3), "us_min": round(cold[1], 3), "us_max": round(cold[2], 3),
+        "us_warm": round(us_warm, 3),
         "tflops": round(F / us_cold / 1e6, 2), "gbps": round(B / us_cold / 1e3, 1),
         "frac_hbm": round(t_hbm / us_cold, 4), "frac_mfma": round(t_mfma / us_cold, 4),
         "binds": "hbm" if t_hbm >= t_mfma else "mfma",
@@ -180,14 +193,16 @@ def point_record(name, N, K, M, us_cold, us_warm, kernel=None):
 
 
 def kernel_name(mx, M, N, K):
-    """The kernel instantiation(s) the library launches for this shape (its own plan)."""
-    return mx.mx_a4w4_gemm_plan(M, N, K)
+    """The kernel instantiation(s) the library launches for this shape when handed the
+    workspace it asks for (what the binding does by default)."""
+    return mx.mx_a4w4_gemm_plan(M, N, K, mx.mx_a4w4_gemm_workspace_bytes(M, N, K))
 
 
 # ----------------------------------------------------------------------------- HBM traffic
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["mxfp4_quantized_gemm_inline_amd/csrc/mx_kernels.hip",
+                  "mxfp4_quantized_gemm_inline_amd/csrc/mx_gemm_qo.hip",
                   "mxfp4_quantized_gemm_inline_amd/csrc/mx_device.h"]
 
 
@@ -195,8 +210,8 @@ LAUNCHERS_MARK = b"// ==========================================================
 
 
 def kernel_source_hash():
-    """Hash of the device code: mx_device.h and mx_kernels.hip up to its host launchers
-    (configuration selection there does not change a kernel)."""
+    """Hash of the device code: mx_device.h, and mx_kernels.hip and mx_gemm_qo.hip up to their
+    host launchers (configuration selection there does not change a kernel)."""
     import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -236,26 +251,49 @@ def _counter_rows(d):
     return rows
 
 
+def plan_kernels(plan):
+    """The kernels of a plan string, e.g. "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8" gives
+    ["k_prepare", "k_gemm_qo<2, 2, 4, 4, 4, 2>"]."""
+    import re
+    return [m.group(0) for m in re.finditer(r"\bk_\w+(<[^>]*>)?", plan)]
+
+
+def dispatch_matches(kernel, name):
+    """True when a profiler kernel name is a dispatch of `kernel` (template arguments included;
+    a plain name must be followed by its argument list, so k_prepare is not k_prepare_packed)."""
+    if "<" in kernel:
+        return kernel in name
+    return (kernel + "(") in name
+
+
 def summarize_counters(fetch_dir, write_dir, workload, M, copy_mib):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMM kernel, each scaled by the
-    factor that maps the same counter on a plain copy of copy_mib MiB to its true size."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of every kernel of the GEMM call's plan, each
+    scaled by the factor that maps the same counter on a plain copy of copy_mib MiB to its true
+    size, summed over the plan's kernels (bytes per call)."""
     import mxfp4_quantized_gemm_inline_amd as mx
     import workloads as W
     N, K = W.DENSE_CONFIGS[workload][:2]
-    plan = mx.mx_a4w4_gemm_plan(M, N, K)
-    kern = plan.split(" ")[0]
-    out = {"kernel": plan, "workload": workload, "N": N, "K": K, "M": M, "copy_mib": copy_mib}
+    plan = mx.mx_a4w4_gemm_plan(M, N, K, mx.mx_a4w4_gemm_workspace_bytes(M, N, K))
+    kernels = plan_kernels(plan)
+    out = {"kernel": plan, "workload": workload, "N": N, "K": K, "M": M, "copy_mib": copy_mib, "per_kernel": {}}
+    total = 0.0
     for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(d) if r[1] == ctr]
         copy = [v for n, c, v in rows if "copybuffer" in n.lower()]
-        gemm = [v for n, c, v in rows if kern.split("<")[0] in n and kern.split("<")[1].rstrip(">") in n]
-        if not copy or not gemm:
-            raise SystemExit(f"{ctr}: no copy ({len(copy)}) or GEMM ({len(gemm)}) dispatches under {d}")
+        if not copy:
+            raise SystemExit(f"{ctr}: no copy dispatch under {d}")
         factor = copy_mib * 1024.0 / max(copy)
-        out[ctr.lower() + "_kib_raw"] = round(sum(gemm) / len(gemm), 1)
         out[ctr.lower() + "_factor"] = round(factor, 4)
-    out["traffic_bytes"] = int((out["fetch_size_kib_raw"] * out["fetch_size_factor"] +
-                                out["write_size_kib_raw"] * out["write_size_factor"]) * 1024)
+        for k in kernels:
+            vals = [v for n, c, v in rows if dispatch_matches(k, n)]
+            if not vals:
+                raise SystemExit(f"{ctr}: no dispatch of {k} under {d}")
+            raw = sum(vals) / len(vals)
+            rec = out["per_kernel"].setdefault(k, {})
+            rec[ctr.lower() + "_kib_raw"] = round(raw, 1)
+            rec[ctr.lower() + "_bytes"] = int(raw * factor * 1024)
+            total += raw * factor * 1024
+    out["traffic_bytes"] = int(total)
     out["algorithmic_bytes"] = algo_bytes(M, N, K)
     out["source_hash"] = kernel_source_hash()
     return out
@@ -282,32 +320,43 @@ def profile_point(workload, M, launches, copy_mib):
     for i in range(launches):
         pt.launch(i)()
     torch.cuda.synchronize()
-    log(f"profiled {workload} M={M}: {launches} launches of {mx.mx_a4w4_gemm_plan(M, N, K)}")
+    log(f"profiled {workload} M={M}: {launches} launches of "
+        f"{mx.mx_a4w4_gemm_plan(M, N, K, mx.mx_a4w4_gemm_workspace_bytes(M, N, K))}")
 
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(a_by_m, w_bits, ms, reps=3):
-    """The oracle as it stands on the host cores: `reps` whole steps of the headline
-    workload (about 10 s), reported per step."""
+def cpu_baseline(a_by_m, w_bits, ms, n_cols=2048):
+    """The oracle as it stands on the host cores, on a bounded sample of one headline step:
+    the activations of every M quantized in full, and the weight's first n_cols rows quantized
+    and multiplied (decode, float64 matmul) for every M; the weight part is scaled by
+    N / n_cols to the whole step (both it and the matmul are linear in the weight rows)."""
     from oracle import mx_oracle as O
-    threads = None
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads") or 1) for p in threadpool_info()) if threadpool_info() else 1
+        info = threadpool_info()
+        blas = max((p.get("num_threads") or 1) for p in info) if info else None
     except Exception:
-        threads = None
+        blas = None
     cores = len(os.sched_getaffinity(0))
+    N = w_bits.shape[0]
+    n_cols = min(n_cols, N)
     t0 = time.perf_counter()
-    for _ in range(reps):
-        for m in ms:
-            O.gemm_ref(a_by_m[m], w_bits)
-    dt = (time.perf_counter() - t0) / reps
-    return {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": threads or cores,
+    q = {m: O.quantize_mx(a_by_m[m]) for m in ms}
+    t_act = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    qw, sw = O.quantize_mx(w_bits[:n_cols])
+    for m in ms:
+        O.gemm_from_mx(q[m][0], q[m][1], qw, sw)
+    t_w = time.perf_counter() - t0
+    step_s = t_act + t_w * N / n_cols
+    return {"value": round(step_s * 1e6, 1), "unit": "us/step", "cores": cores, "blas_threads": blas,
             "kind": "oracle",
-            "sample": f"{reps} full steps (N=7168 K=768, M in {list(ms)}: quantize A and W, decode, "
-                      f"float64 matmul), mean per step; {cores} host cores visible, BLAS threads "
-                      f"{threads} (the matmul); quantization is single-threaded numpy"}
+            "sample": f"one step of N={N} K={w_bits.shape[1]}, M in {list(ms)}: activations quantized in full "
+                      f"({t_act:.1f} s), weight rows 0..{n_cols - 1} quantized, decoded and multiplied in float64 "
+                      f"for every M ({t_w:.1f} s), scaled by N/{n_cols}; {t_act + t_w:.1f} s of CPU work on "
+                      f"{cores} host cores (matmul on {blas} BLAS threads, quantization single-threaded numpy)"}
 
 
 # ----------------------------------------------------------------------------- main
@@ -363,7 +412,7 @@ def main():
     log(f"calibration: {calib['hbm_read_GBps']:.0f} GB/s streaming read, "
         f"{calib['mfma_fp4_TFLOPs']:.0f} TFLOP/s FP4 MFMA")
 
-    # ---------------- headline: N=7168 K=768 M sweep, one call per M per step
+    # ---------------- headline: N=8448 K=7168 M sweep, one call per M per step
     N, K, ms, structure = W.DENSE_CONFIGS[HEADLINE]
     w_bits = W.dense_weight(N, K)
     a_all = W.dense_activation(max(ms), K, structure)
@@ -372,7 +421,7 @@ def main():
     torch.cuda.synchronize()
     log(f"headline {HEADLINE}: prepared weight {wp.numel()} B")
 
-    # rotating sets for the whole step
+    # rotating sets for the whole step, one graph per set (each holds one step: a call per M)
     per_step = wp.numel() + sum(2 * m * K + 2 * m * N for m in ms)
     R = max(1, min(256, math.ceil(ROTATE_TARGET / per_step)))
     sets = []
@@ -382,32 +431,37 @@ def main():
         c_r = {m: torch.empty((m, N), dtype=torch.bfloat16, device="cuda") for m in ms}
         sets.append((w_r, a_r, c_r))
 
-    def step_launches(i):
-        w_r, a_r, c_r = sets[i % R]
+    def step_launches(r):
+        w_r, a_r, c_r = sets[r]
         return [(lambda m=m: mx.mx_a4w4_gemm(a_r[m], w_r, N, out=c_r[m])) for m in ms]
 
-    warm_g = timer.graph([f for i in range(max(1, args.warmup)) for f in step_launches(i)])
-    warm_g.replay()
+    graphs = [timer.graph(step_launches(r)) for r in range(R)]
+    for g in graphs:  # first replay of each graph (upload), outside the warmup count
+        g.replay()
+    for i in range(args.warmup):
+        graphs[i % R].replay()
     torch.cuda.synchronize()
-    step_g = timer.graph([f for i in range(args.steps) for f in step_launches(i)])
-    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall0 = time.perf_counter()
-    step_ms = timer.replay_ms(step_g, reps=1) / args.steps
+    ev[0].record(stream)
+    for i in range(args.steps):
+        graphs[i % R].replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    del step_g, warm_g
-    log(f"headline step: {step_ms * 1e3:.2f} us/step over {args.steps} steps, R={R} buffer sets")
+    per_step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    step_ms = per_step_ms[len(per_step_ms) // 2]
+    mean_ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    del graphs
+    torch.cuda.empty_cache()
+    log(f"headline step: median {step_ms * 1e3:.2f} us/step (mean {mean_ms * 1e3:.2f}, min "
+        f"{per_step_ms[0] * 1e3:.2f}, max {per_step_ms[-1] * 1e3:.2f}) over {args.steps} steps, R={R} buffer sets")
 
-    # per-point detail for the headline workload (cold = rotated, warm = one set)
-    head_points = []
-    for m in ms:
-        cold = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=True)
-        us_c = time_point(timer, cold, args.launches)
-        del cold
-        warm = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=False)
-        us_w = time_point(timer, warm, args.launches)
-        del warm
-        head_points.append(point_record(HEADLINE, N, K, m, us_c, us_w, kernel_name(mx, m, N, K)))
-        log(f"  M={m}: {us_c:.2f} us cold, {us_w:.2f} us warm")
+    wdev = dev_bf16(torch, w_bits).float()
+    head_points = measure_dense(torch, mx, timer, HEADLINE, N, K, ms, wp, a_by_m, wdev, args.launches)
+    del wdev
+    torch.cuda.empty_cache()
     dom = max(head_points, key=lambda p: p["us"])
     Bd = algo_bytes(dom["M"], N, K)
     Fd = algo_flops(dom["M"], N, K)
@@ -423,9 +477,13 @@ def main():
     roof["frac_calibrated"] = round(roof["achieved"] / cal_peak, 4)
     roof["kernel"] = f"{dom['kernel']} (N={N} K={K} M={dom['M']})"
     roof["launch_us"] = dom["us"]
-    roof["traffic_note"] = ("HBM bytes per launch: rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by "
-                            "its reading on a plain copy of known size (profiles/traffic.json); null when "
-                            "the kernel sources changed since the counters were taken")
+    roof["launch_us_min_max"] = [dom["us_min"], dom["us_max"]]
+    roof["duration_note"] = ("one whole GEMM call (every kernel of its plan, back to back on one stream): "
+                             f"median over {REPLAYS} replays of a graph of {args.launches} rotated calls, "
+                             "HIP events on the replay stream")
+    roof["traffic_note"] = ("HBM bytes per call: rocprofv3 FETCH_SIZE and WRITE_SIZE of each kernel of the plan, "
+                            "each scaled by its reading on a plain copy of known size (profiles/traffic.json); "
+                            "null when the kernel sources changed since the counters were taken")
     roof["algorithmic_bytes"] = Bd
     roof["algorithmic_flops"] = Fd
 
@@ -438,37 +496,35 @@ def main():
             wb = W.dense_weight(Nn, Kk)
             wpn = mx.mx_prepare_weight(dev_bf16(torch, wb))
             aa = W.dense_activation(max(mss), Kk, st)
-            for m in mss:
-                cold = DensePoint(torch, mx, wpn, aa[:m], Nn, Kk, m, rotate=True)
-                us_c = time_point(timer, cold, args.launches)
-                del cold
-                warm = DensePoint(torch, mx, wpn, aa[:m], Nn, Kk, m, rotate=False)
-                us_w = time_point(timer, warm, args.launches)
-                del warm
-                sweep["dense"].append(point_record(name, Nn, Kk, m, us_c, us_w, kernel_name(mx, m, Nn, Kk)))
-                log(f"  {name} M={m}: {us_c:.2f} us cold, {us_w:.2f} us warm")
-            del wpn
+            wdn = dev_bf16(torch, wb).float()
+            sweep["dense"].extend(measure_dense(torch, mx, timer, name, Nn, Kk, mss, wpn,
+                                                {m: aa[:m] for m in mss}, wdn, args.launches))
+            del wpn, wdn
             torch.cuda.empty_cache()
         sweep["dense"] = [*head_points, *sweep["dense"]]
-        # the A16WFP4 variant at the headline shape (bf16 activations x decoded weight on the
-        # bf16 MFMA): context, priced against the bf16 MFMA peak
-        sweep["a16w4"] = []
-        for m in ms:
-            cold = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=True)
+        # the A16WFP4 variant (bf16 activations x decoded weight on the bf16 MFMA) at N=7168
+        # K=768, the shape of the pages' A16WFP4 call: context, priced against the bf16 MFMA peak
+        N16, K16, ms16, st16 = W.DENSE_CONFIGS["n7168_k768"]
+        wp16 = mx.mx_prepare_weight(dev_bf16(torch, W.dense_weight(N16, K16)))
+        a16 = W.dense_activation(max(ms16), K16, st16)
+        for m in ms16:
+            cold = DensePoint(torch, mx, wp16, a16[:m], N16, K16, m, rotate=True)
 
             def launch16(i, pt=cold):
                 a_r, w_r, c_r = pt.sets[i % pt.R]
-                return lambda: mx.mx_a16w4_gemm(a_r, w_r, N, out=c_r)
+                return lambda: mx.mx_a16w4_gemm(a_r, w_r, N16, out=c_r)
             g = timer.graph([launch16(i) for i in range(args.launches)])
-            us16 = timer.replay_ms(g, reps=3) * 1e3 / args.launches
+            us16, lo16, hi16 = replay_stats(timer, g, args.launches)
             del g, cold
-            Bm, Fm = algo_bytes(m, N, K), algo_flops(m, N, K)
-            sweep["a16w4"].append({"workload": HEADLINE, "N": N, "K": K, "M": m, "us": round(us16, 3),
+            Bm, Fm = algo_bytes(m, N16, K16), algo_flops(m, N16, K16)
+            sweep["a16w4"].append({"workload": "n7168_k768", "N": N16, "K": K16, "M": m, "us": round(us16, 3),
+                                   "us_min": round(lo16, 3), "us_max": round(hi16, 3),
                                    "tflops": round(Fm / us16 / 1e6, 2), "gbps": round(Bm / us16 / 1e3, 1),
                                    "frac_hbm": round(Bm / HBM_PEAK * 1e6 / us16, 4),
                                    "frac_mfma_bf16": round(Fm / MFMA_BF16_PEAK * 1e6 / us16, 4),
-                                   "kernel": mx.mx_a16w4_gemm_plan(m, N, K)})
-            log(f"  a16w4 {HEADLINE} M={m}: {us16:.2f} us cold")
+                                   "kernel": mx.mx_a16w4_gemm_plan(m, N16, K16)})
+            log(f"  a16w4 n7168_k768 M={m}: {us16:.2f} us cold")
+        del wp16
         if not args.no_grouped:
             sweep["grouped"] = grouped_sweep(torch, mx, W, timer)
 
@@ -505,8 +561,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"dense A4W4 MXFP4 GEMM N={N} K={K}, one call per M in {list(ms)} per step",
                    "N": N, "K": K, "M": list(ms), "buffer_sets": R,
-                   "a": "bf16 ~N(0,1), 1% of K channels x20", "w": "bf16 ~N(0,0.02) prepared to MXFP4",
-                   "timing": "HIP graph replay, HIP events; rotating buffer sets > Infinity Cache"},
+                   "a": "bf16 ~N(0,1); in 0.5% of rows (row 0 among them) each 32-block zeroed with "
+                        "probability 1/4, the first as -0",
+                   "w": "bf16 ~N(0,0.02) prepared to MXFP4",
+                   "timing": "one HIP graph replay per step, HIP events between steps; median step; "
+                             "rotating buffer sets > Infinity Cache"},
+        "step_us": {"median": round(value, 3), "mean": round(mean_ms * 1e3, 3),
+                    "min": round(per_step_ms[0] * 1e3, 3), "max": round(per_step_ms[-1] * 1e3, 3),
+                    "p10": round(per_step_ms[len(per_step_ms) // 10] * 1e3, 3),
+                    "p90": round(per_step_ms[(9 * len(per_step_ms)) // 10] * 1e3, 3)},
         "baseline_note": f"vs_baseline = value / {page_total:.3f} us, the sum of the pages' direct-kernel "
                          f"medians for this sweep on MI355X (lower is better)",
         "roofline": roof,
@@ -517,6 +580,29 @@ def main():
         "wall_s_timed": round(t_wall, 4),
     }
     print(json.dumps(out), flush=True)
+
+
+def measure_dense(torch, mx, timer, name, N, K, ms, wp, a_by_m, w_f32, launches):
+    """Cold (rotated) and warm (one set) time per M, and the relative L2 of the output against
+    the unquantized product: ||C - A W^T|| / ||A W^T|| with A and W the bf16 inputs, the
+    reference in fp32 on the GPU (context only: the parity tests compare with the oracle)."""
+    recs = []
+    for m in ms:
+        cold = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=True)
+        us_c = time_point(timer, cold, launches)
+        a0, w0, c0 = cold.sets[0]
+        ref = a0.float() @ w_f32.t()
+        rel = float(torch.linalg.vector_norm(c0.float() - ref) / torch.linalg.vector_norm(ref))
+        del cold, ref
+        warm = DensePoint(torch, mx, wp, a_by_m[m], N, K, m, rotate=False)
+        us_w = time_point(timer, warm, launches)[0]
+        del warm
+        rec = point_record(name, N, K, m, us_c, us_w, kernel_name(mx, m, N, K))
+        rec["rel_l2_vs_bf16"] = round(rel, 5)
+        recs.append(rec)
+        log(f"  {name} M={m}: {us_c[0]:.2f} us cold ({us_c[1]:.2f}..{us_c[2]:.2f}), {us_w:.2f} us warm, "
+            f"rel-L2 {rel:.4f}")
+    return recs
 
 
 def grouped_sweep(torch, mx, W, timer):

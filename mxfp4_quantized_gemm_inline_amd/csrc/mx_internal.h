@@ -47,6 +47,8 @@ size_t qo_act_bytes(int64_t M, int64_t K);
 bool qo_supported(int WM, int WN, int MT, int NG, int NBUF, int OCC);
 hipError_t launch_gemm_qo(int WM, int WN, int MT, int NG, int NBUF, int OCC, const void* a, const void* wp, void* c,
                           int64_t M, int64_t N, int64_t K, int GM, void* ws, hipStream_t st);
+// C [M, N] bf16 = the sum over s = 0..S-1, in order, of the FP32 partials P[s] [M, N].
+hipError_t launch_splitk_reduce(const float* P, void* c, int64_t M, int64_t N, int S, hipStream_t st);
 // Name the kernel(s) the launchers above would run (false: the tuning override is invalid).
 bool gemm_plan(int64_t M, int64_t N, int64_t K, size_t ws_bytes, char* buf, size_t len);
 bool grouped_plan(int64_t E, int64_t R_max, int64_t N, int64_t K, int64_t T, int64_t rows_hint, char* buf,
