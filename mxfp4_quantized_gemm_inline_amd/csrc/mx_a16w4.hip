@@ -4,12 +4,13 @@
 // variant as outside that change; the weight is the same prepared blob).
 //
 // Two forms: a weight-streaming kernel for decode M (at most 32 rows, below) and a tiled
-// kernel for larger M. Tile: BM = 64 rows x BN = 256 columns, four waves side by side along N, each 64 x 64
-// (four 16-row tiles x four 16-column groups). Per 128-wide K step the CTA's bf16
-// activation tile (64 x 128, 16 KiB) goes to LDS, double buffered, its 16-byte chunks
-// XOR-swizzled by row so the operand reads are conflict-free; each wave loads its weight
-// operands (1 KiB per column group, as for the A4W4 kernels) and scale word straight into
-// registers and decodes them with v_cvt_scalef32_pk_bf16_fp4.
+// kernel for larger M. Tile: BM = 64 rows x BN = 64, 128 or 256 columns, four waves side by
+// side along N, each 64 rows x BN / 64 column groups of 16 (four 16-row tiles each). Per
+// 128-wide K step the CTA's bf16 activation tile (64 x 128, 16 KiB) goes to LDS, double
+// buffered, its 16-byte chunks XOR-swizzled by row so the operand reads are conflict-free;
+// each wave loads its weight operands (1 KiB per column group, as for the A4W4 kernels) and
+// scale word straight into registers and decodes them with v_cvt_scalef32_pk_bf16_fp4. Both
+// operands are loaded two steps ahead.
 //
 // K order inside a step: MFMA j (0..3) takes, from lane quarter q, the step's elements
 // 32q + 8j .. 32q + 8j + 7 for both operands (a common permutation of k leaves every sum
@@ -18,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <utility>
 
 #include "mx_device.h"
@@ -27,68 +29,71 @@ namespace mx {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-constexpr int kA16BM = 64, kA16BN = 256, kA16Threads = 256;
+constexpr int kA16BM = 64, kA16Threads = 256;
 constexpr int kA16Row = 256;                                   // bytes of one staged activation row (128 bf16)
 constexpr int kA16Stage = 2 * kA16BM * kA16Row;                // double-buffered activation tile
-constexpr int kA16CRow = kA16BN * 2 + 16;                      // bf16 output staging row, padded
-constexpr int kA16Smem = kA16Stage > kA16BM * kA16CRow ? kA16Stage : kA16BM * kA16CRow;
 
 __device__ __forceinline__ int a16_chunk(int row, int chunk) { return chunk ^ (row & 15); }
 
+// Tile BM = 64 x BN = 64 NGW: four waves side by side along N, each 64 rows x NGW column
+// groups. Both operands run D steps ahead in registers: step t's activation block of each
+// thread and each wave's weight operands and scale word sit in slot t % D, refilled with step
+// t + D once the step has used them (the activations once stored to LDS).
+template <int NGW, int D>
 __global__ __launch_bounds__(kA16Threads, 2) void k_gemm_a16w4(const uint16_t* __restrict__ A,
                                                                const uint8_t* __restrict__ Wp,
                                                                uint16_t* __restrict__ C, int M, int N, int K) {
-  __shared__ __align__(16) uint8_t smem[kA16Smem];
+  constexpr int BN = 64 * NGW, CROW = BN * 2 + 16;
+  constexpr int SMEM = kA16Stage > kA16BM * CROW ? kA16Stage : kA16BM * CROW;
+  __shared__ __align__(16) uint8_t smem[SMEM];
   const int T = K / kStepK, G = N / 16;
-  const int tiles_m = (M + kA16BM - 1) / kA16BM, tiles_n = N / kA16BN;
-  // XCD-aware order: blocks are dealt round-robin to the 8 XCDs; each XCD walks a
-  // contiguous share of the tiles, eight row tiles at a time down a column of tiles.
-  const int total = tiles_m * tiles_n, x = blockIdx.x % 8, q8 = total / 8, r8 = total % 8;
-  const int logical = x * q8 + min(x, r8) + (int)blockIdx.x / 8;
-  const int grp = logical / (8 * tiles_n), first = grp * 8, gm = min(tiles_m - first, 8);
-  const int rem = logical - grp * 8 * tiles_n;
-  const int bm = first + rem % gm, bn = rem / gm;
+  const int tiles_m = (M + kA16BM - 1) / kA16BM, tiles_n = N / BN;
+  int bm, bn;
+  tile_coords(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, 8, bm, bn);
   const int m0 = bm * kA16BM, Mrows = min(kA16BM, M - m0);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int gw0 = bn * (kA16BN / 16) + w * 4;                  // first of this wave's four column groups
+  const int gw0 = bn * (BN / 16) + w * NGW;                    // first of this wave's column groups
   const uint8_t* __restrict__ Wsc = Wp + payload_bytes(N, K);
 
   // activation loads: thread -> row tid/4 (clamped into the valid rows), 32-block tid%4
   const int ar = tid >> 2, ab = tid & 3;
   const uint16_t* arow = A + (size_t)(m0 + min(ar, Mrows - 1)) * K + ab * kBlock;
-  const uint8_t* wb[4];
+  const uint8_t* wb[NGW];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) wb[g] = Wp + (size_t)min(gw0 + g, G - 1) * T * 1024 + lane * 16;
+  for (int g = 0; g < NGW; ++g) wb[g] = Wp + (size_t)min(gw0 + g, G - 1) * T * 1024 + lane * 16;
+  // the scale word of this wave's groups' quad, and the byte of its first group in it
   const uint8_t* sb = Wsc + (size_t)min(gw0 >> 2, G / 4 - 1) * T * 256 + lane * 4;
+  const int sh0 = 8 * (gw0 & 3);
 
-  uint32_t xa[16];
-  uint4 wq[2][4];
-  uint32_t ws[2];
-  auto load = [&](int t, auto slot_c) {
+  uint32_t xa[D][16];
+  uint4 wq[D][NGW];
+  uint32_t ws[D];
+  auto load = [&](int t, auto slot_c) {  // t past the end: the last step again, never used
     constexpr int SL = decltype(slot_c)::value;
-    load_block(arow + (size_t)t * kStepK, xa);
+    const int tt = min(t, T - 1);
+    load_block(arow + (size_t)tt * kStepK, xa[SL]);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) wq[SL][g] = *reinterpret_cast<const uint4*>(wb[g] + (size_t)t * 1024);
-    ws[SL] = *reinterpret_cast<const uint32_t*>(sb + (size_t)t * 256);
+    for (int g = 0; g < NGW; ++g) wq[SL][g] = *reinterpret_cast<const uint4*>(wb[g] + (size_t)tt * 1024);
+    ws[SL] = *reinterpret_cast<const uint32_t*>(sb + (size_t)tt * 256);
   };
   auto sa = [&](int buf, int row, int chunk) { return smem + buf * kA16BM * kA16Row + row * kA16Row + 16 * a16_chunk(row, chunk); };
 
-  v4f acc[4][4];
+  v4f acc[NGW][4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < NGW; ++g)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[g][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // step t: weights of step t in slot SL (compile time), activations of step t in xa
+  // step t, its operands in slot SL = t % D
   auto step = [&](int t, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
     const int buf = t & 1;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<uint4*>(sa(buf, ar, 4 * ab + c)) = make_uint4(xa[4 * c], xa[4 * c + 1], xa[4 * c + 2], xa[4 * c + 3]);
-    load(min(t + 1, T - 1), std::integral_constant<int, SL ^ 1>{});  // past the end: a harmless re-load
+      *reinterpret_cast<uint4*>(sa(buf, ar, 4 * ab + c)) =
+          make_uint4(xa[SL][4 * c], xa[SL][4 * c + 1], xa[SL][4 * c + 2], xa[SL][4 * c + 3]);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -97,8 +102,8 @@ __global__ __launch_bounds__(kA16Threads, 2) void k_gemm_a16w4(const uint16_t* _
       for (int mt = 0; mt < 4; ++mt)
         bop[mt] = *reinterpret_cast<const uint4*>(sa(buf, 16 * mt + (lane & 15), 4 * (lane >> 4) + j));
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t s = (ws[SL] >> (8 * g)) & 0xffu;
+      for (int g = 0; g < NGW; ++g) {
+        const uint32_t s = (ws[SL] >> (sh0 + 8 * g)) & 0xffu;
         const float sc = __builtin_bit_cast(float, s ? (s << 23) : 0x00400000u);
         const uint32_t codes = j == 0 ? wq[SL][g].x : j == 1 ? wq[SL][g].y : j == 2 ? wq[SL][g].z : wq[SL][g].w;
         uint32_t d[4];
@@ -113,35 +118,36 @@ __global__ __launch_bounds__(kA16Threads, 2) void k_gemm_a16w4(const uint16_t* _
                                                                0, 0, 0);
       }
     }
+    load(t + D, std::integral_constant<int, SL>{});  // the slot is free: refill it with step t + D
     __syncthreads();  // the buffer written two steps on is free only once every wave has read it
   };
 
-  load(0, std::integral_constant<int, 0>{});
+  static_for<D>([&](auto u_c) { load(decltype(u_c)::value, u_c); });
   int t = 0;
-  for (; t + 2 <= T; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    step(t + 1, std::integral_constant<int, 1>{});
-  }
-  if (t < T) step(t, std::integral_constant<int, 0>{});
+  for (; t + D <= T; t += D) static_for<D>([&](auto u_c) { step(t + decltype(u_c)::value, u_c); });
+  static_for<D>([&](auto u_c) {
+    if (t + decltype(u_c)::value < T) step(t + decltype(u_c)::value, u_c);
+  });
 
   // Epilogue: lane l holds C[m = 16 mt + l % 16][n = 16 g + 4 (l / 16) .. + 3] of its wave's
   // columns; stage the tile as bf16 in LDS, then write whole rows 16 bytes per lane.
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < NGW; ++g)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int r = 16 * mt + (lane & 15), cl = 16 * (w * 4 + g) + 4 * (lane >> 4);
-      *reinterpret_cast<uint2*>(smem + r * kA16CRow + cl * 2) =
+      const int r = 16 * mt + (lane & 15), cl = 16 * (w * NGW + g) + 4 * (lane >> 4);
+      *reinterpret_cast<uint2*>(smem + r * CROW + cl * 2) =
           pack4_bf16(acc[g][mt][0], acc[g][mt][1], acc[g][mt][2], acc[g][mt][3]);
     }
   __syncthreads();
-  const int n0 = bn * kA16BN;
+  const int n0 = bn * BN;
+  static_assert(kA16BM * (BN / 8) % kA16Threads == 0, "every thread stores the same number of chunks");
 #pragma unroll
-  for (int i = 0; i < kA16BM * (kA16BN / 8) / kA16Threads; ++i) {
+  for (int i = 0; i < kA16BM * (BN / 8) / kA16Threads; ++i) {
     const int id = tid + i * kA16Threads;
-    const int r = id / (kA16BN / 8), ch = id % (kA16BN / 8);
+    const int r = id / (BN / 8), ch = id % (BN / 8);
     if (r < Mrows) {
-      const uint4 v = *reinterpret_cast<const uint4*>(smem + r * kA16CRow + ch * 16);
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + r * CROW + ch * 16);
       *reinterpret_cast<uint4*>(C + (size_t)(m0 + r) * N + n0 + 8 * ch) = v;
     }
   }
@@ -291,6 +297,32 @@ hipError_t run_a16_stream_mt(const A16StreamCfg& cfg, const void* a, const void*
 
 constexpr int64_t kA16StreamMaxM = 32;
 
+// Compiled tiled forms (NGW, D).
+#define MX_A16_TILE_CONFIGS(X) X(4, 2) X(2, 2) X(1, 2)
+
+struct A16TileCfg {
+  int NGW, D;
+};
+// Tiled form: the widest tile (64 x 256, 64 x 128 or 64 x 64) that still gives about 200 CTAs
+// or more (N = 7168, K = 768: 64 x 64 at M = 128, 6.7 us against 10.8 us for 64 x 256 tiles;
+// 64 x 256 from M = 449 on), loads two steps ahead (three or more measured no faster).
+// Tuning only: MX_A16W4_CONFIG="NGW,D" replaces the choice (a pair not compiled fails the call).
+bool a16_tile_cfg(int64_t M, int64_t N, A16TileCfg& c) {
+  const int64_t tm = (M + kA16BM - 1) / kA16BM;
+  c.NGW = tm * (N / 256) >= 200 ? 4 : tm * (N / 128) >= 200 ? 2 : 1;
+  c.D = 2;
+  const char* e = std::getenv("MX_A16W4_CONFIG");
+  if (e && *e) {
+    if (std::sscanf(e, "%d,%d", &c.NGW, &c.D) != 2) return false;
+    bool ok = false;
+#define X(ngw, d) ok = ok || (c.NGW == ngw && c.D == d);
+    MX_A16_TILE_CONFIGS(X)
+#undef X
+    return ok;
+  }
+  return true;
+}
+
 }  // namespace
 
 bool a16w4_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t len) {
@@ -300,7 +332,9 @@ bool a16w4_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t len) {
     const A16StreamCfg c = a16_stream_cfg(M, N, K);
     std::snprintf(buf, len, "k_gemm_a16w4_stream<%d, %d, %d, %d>", c.MT, c.NG, c.WK, c.PD);
   } else {
-    std::snprintf(buf, len, "k_gemm_a16w4 (64 x 256 tiles)");
+    A16TileCfg c;
+    if (!a16_tile_cfg(M, N, c)) return false;
+    std::snprintf(buf, len, "k_gemm_a16w4<%d, %d> (64 x %d tiles)", c.NGW, c.D, 64 * c.NGW);
   }
   return true;
 }
@@ -312,12 +346,23 @@ hipError_t launch_a16w4(const void* a, const void* wp, void* c, int64_t M, int64
     return cfg.MT == 2 ? run_a16_stream_mt<2>(cfg, a, wp, c, (int)M, (int)N, (int)K, st)
                        : run_a16_stream_mt<1>(cfg, a, wp, c, (int)M, (int)N, (int)K, st);
   }
-  const int64_t tiles = ((M + kA16BM - 1) / kA16BM) * (N / kA16BN);
+  A16TileCfg cfg;
+  if (!a16_tile_cfg(M, N, cfg)) return hipErrorInvalidValue;
+  const int64_t tiles = ((M + kA16BM - 1) / kA16BM) * (N / (64 * cfg.NGW));
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gemm_a16w4, dim3((unsigned)tiles), dim3(kA16Threads), 0, st, static_cast<const uint16_t*>(a),
-                     static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), (int)M, (int)N, (int)K);
-  return hipGetLastError();
+  const auto* A = static_cast<const uint16_t*>(a);
+  const auto* W = static_cast<const uint8_t*>(wp);
+  auto* C = static_cast<uint16_t*>(c);
+  const dim3 grid((unsigned)tiles), block(kA16Threads);
+#define X(ngw, d)                                                                                        \
+  if (cfg.NGW == ngw && cfg.D == d) {                                                                    \
+    hipLaunchKernelGGL((k_gemm_a16w4<ngw, d>), grid, block, 0, st, A, W, C, (int)M, (int)N, (int)K);     \
+    return hipGetLastError();                                                                            \
+  }
+  MX_A16_TILE_CONFIGS(X)
+#undef X
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mx

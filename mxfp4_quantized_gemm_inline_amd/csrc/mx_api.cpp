@@ -240,7 +240,10 @@ mx_status mx_a4w4_gemm_grouped_act_quant_plan(int64_t E, int64_t R_max, int64_t 
 mx_status mx_a16w4_gemm_plan(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
   if (M < 0 || !gemm_shape_ok(N, K) || M > kMaxRows) return MX_ERR_SHAPE;
   if (!buf || buf_len == 0) return MX_ERR_NULL;
-  mx::a16w4_plan(M, N, K, buf, buf_len);
+  if (!mx::a16w4_plan(M, N, K, buf, buf_len)) {  // the tuning override names nothing compiled
+    buf[0] = '\0';
+    return MX_ERR_HIP;
+  }
   return MX_OK;
 }
 

@@ -178,7 +178,11 @@ def test_a16w4_plan_names_the_selected_kernel():
     assert mx.mx_a16w4_gemm_plan(16, 8448, 7168) == "k_gemm_a16w4_stream<1, 1, 8, 8>"
     assert mx.mx_a16w4_gemm_plan(17, 7168, 768) == "k_gemm_a16w4_stream<2, 2, 4, 2>"
     assert mx.mx_a16w4_gemm_plan(32, 8448, 7168) == "k_gemm_a16w4_stream<2, 1, 8, 4>"
-    assert mx.mx_a16w4_gemm_plan(33, 7168, 768) == "k_gemm_a16w4 (64 x 256 tiles)"
+    # tiled form: the widest tile that still gives about 200 CTAs
+    assert mx.mx_a16w4_gemm_plan(33, 7168, 768) == "k_gemm_a16w4<1, 2> (64 x 64 tiles)"
+    assert mx.mx_a16w4_gemm_plan(128, 7168, 768) == "k_gemm_a16w4<1, 2> (64 x 64 tiles)"
+    assert mx.mx_a16w4_gemm_plan(256, 7168, 768) == "k_gemm_a16w4<2, 2> (64 x 128 tiles)"
+    assert mx.mx_a16w4_gemm_plan(2048, 7168, 768) == "k_gemm_a16w4<4, 2> (64 x 256 tiles)"
     for bad in ((1, 100, 768), (1, 7168, 100), (-1, 7168, 768)):
         with pytest.raises(mx.MxError):
             mx.mx_a16w4_gemm_plan(*bad)

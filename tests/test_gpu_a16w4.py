@@ -1,7 +1,7 @@
 """GPU parity of the A16WFP4 variant (bf16 activations x decoded MXFP4 weight on the bf16
 MFMA) against the oracle (oracle/mx_oracle.py: gemm_a16w4_ref), within the GEMM tolerance
 |gpu - exact| <= 2^-7 |exact| + 1e-3 rms(exact): every output for ragged M over several
-64-row tiles and both K forms (K = 768, 4224), the decode form (M <= 32) over its launch
+64-row tiles and K = 256 .. 4224 (2 to 33 steps), each tile width of the tiled form, the decode form (M <= 32) over its launch
 shapes, sampled rows at the headline shape
 (N = 7168, K = 768, M = 2048, the launch the bench times); a one-hot activation probe that
 must reproduce the decoded weight bit for bit; canary rows past M left untouched."""
@@ -16,7 +16,7 @@ from gpu_util import check_gemm, dev_bf16, host_bits, lib_or_fail, sample_rows, 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("K", [768, 4224])
+@pytest.mark.parametrize("K", [256, 768, 1024, 4224])
 @pytest.mark.parametrize("M", [1, 37, 64, 100, 300])
 def test_a16w4_matches_oracle(M, K):
     torch = torch_or_skip()
@@ -53,6 +53,28 @@ def test_a16w4_decode_form_matches_oracle(N, K, M):
     torch.cuda.synchronize()
     assert np.all(O.bf16_to_f64(c[M:]) == 5.0)
     check_gemm(c[:M], O.gemm_a16w4_ref(a, w), what=f"a16w4 decode N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("M,ngw", [(100, 1), (256, 2), (300, 2), (512, 4), (520, 4)])
+def test_a16w4_tile_widths_match_oracle(M, ngw):
+    """The tiled form at N = 7168, K = 1024 (8 steps, loads two steps ahead) in each of its tile
+    widths, 64 x 64 NGW, every output against the oracle, ragged last row tiles, canary rows
+    past M. (K = 256, 768, 1024 and 4224 in the test above give 2, 6, 8 and 33 steps: an odd
+    count takes the loop's remainder path.)"""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    N, K = 7168, 1024
+    plan = mx.mx_a16w4_gemm_plan(M, N, K)
+    assert plan == f"k_gemm_a16w4<{ngw}, 2> (64 x {64 * ngw} tiles)", plan
+    a = W.dense_activation(M, K, "outlier_channels", seed=76)
+    w = W.dense_weight(N, K, seed=77)
+    wp = mx.mx_prepare_weight(dev_bf16(w))
+    out = torch.full((M + 3, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    mx.mx_a16w4_gemm(dev_bf16(a), wp, N, out=out[:M])
+    c = host_bits(out)
+    torch.cuda.synchronize()
+    assert np.all(O.bf16_to_f64(c[M:]) == 5.0)
+    check_gemm(c[:M], O.gemm_a16w4_ref(a, w), what=f"a16w4 tiles 64x{64 * ngw} M={M}")
 
 
 def test_a16w4_headline_shape_sampled():
