@@ -284,8 +284,12 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restr
   extern __shared__ __align__(16) uint8_t smem[];
   const int T = steps_of(K);
   const int ks0 = min(T, (int)blockIdx.y * TS), ks1 = min(T, ks0 + TS);
+  // column chunks dealt to the XCDs in contiguous ranges: the CTAs that share a weight scale
+  // word (four column groups) mostly share an L2
+  int unused, cg;
+  tile_coords(blockIdx.x, gridDim.x, 1, gridDim.x, 1, unused, cg);
   StreamCTA<MT, NG, WK, PD, QB> cta;
-  cta.init(Wp, N, K, blockIdx.x * NG, ks0, ks1, TS, min(M, 16 * MT), smem);
+  cta.init(Wp, N, K, cg * NG, ks0, ks1, TS, min(M, 16 * MT), smem);
   const DenseRows rows{A, K};
   cta.quant(rows, M, [&] { if (cta.S > 0) cta.load_w(cta.t0); });
   __syncthreads();
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restr
   const int lane = threadIdx.x & 63;
   cta.reduce_store(acc, smem, [&](int g, int mt, const v4f& v) {
     const int m = 16 * mt + (lane & 15);
-    const int n = 16 * (blockIdx.x * NG + g) + 4 * (lane >> 4);
+    const int n = 16 * (cg * NG + g) + 4 * (lane >> 4);
     if (m < M) {
       if (P) *reinterpret_cast<v4f*>(P + ((size_t)blockIdx.y * M + m) * N + n) = v;
       else *reinterpret_cast<uint2*>(C + (size_t)m * N + n) = pack4_bf16(v[0], v[1], v[2], v[3]);
