@@ -155,6 +155,16 @@ def calibrate(torch, mx, timer):
         read.append((buf.numel() / ms / 1e6, per_cu))
     del buf
     torch.cuda.empty_cache()
+    # the floor for streaming the largest prepared weight once: a cold 32 MiB read, rotating
+    # over 32 buffers (1 GiB) so each read comes from HBM, best launch shape
+    small = [torch.zeros(32 << 20, dtype=torch.uint8, device="cuda") for _ in range(32)]
+    read32 = []
+    for ctas in (cus * 2, cus * 8):
+        g = timer.graph([lambda b=small[i % 32], c=ctas: mx.mx_calib_read(b, c, sink) for i in range(64)])
+        read32.append(replay_stats(timer, g, 64)[0])
+        del g
+    del small
+    torch.cuda.empty_cache()
     mfma = []
     iters = 2048
     for per_cu in (2, 4):
@@ -165,6 +175,9 @@ def calibrate(torch, mx, timer):
         mfma.append((mx.mx_calib_mfma_flops(ctas, iters) / ms / 1e9, per_cu))
     best_r, best_m = max(read), max(mfma)
     return {"hbm_read_GBps": round(best_r[0], 1), "mfma_fp4_TFLOPs": round(best_m[0], 1),
+            "read_32mb_us": round(min(read32), 3),
+            "read_32mb": "cold 32 MiB streaming read (rotating over 1 GiB), median of 5 replays of 64 reads, "
+                         "best of 2 and 8 CTAs per CU: the floor for streaming the 8448 x 7168 weight once",
             "read": "1 GiB streaming read, 16-byte coalesced loads, %d CTAs of 256 threads per CU" % best_r[1],
             "mfma": "16x16x128 block-scaled FP4 MFMA on registers, 8 chains per wave, %d CTAs of 4 waves "
                     "per CU" % best_m[1],
