@@ -111,9 +111,12 @@ mx_status mx_quant_act(const void* a_bf16, int64_t M, int64_t K, void* a_fp4, vo
 /*
  * Workspace the dense GEMM can use at this shape: FP32 partial sums of a split-K
  * reduction (few rows), or, at large M, the activations quantized once into the
- * prepared layout (M rounded up to 64, times K * 17 / 32 bytes). It is always optional:
- * with a NULL or smaller workspace the library picks a configuration that needs none,
- * with the same results. 0 for an invalid shape.
+ * prepared layout (M rounded up to 64, times K * 17 / 32 bytes), followed, when the
+ * 128 x 128 output tiles slightly exceed one round of the chip, by the FP32 partial tiles
+ * of the tail tiles' K slices (from the next 256-byte boundary). It is always optional:
+ * with a NULL or smaller workspace the library picks a configuration that needs less or
+ * none; results stay within the same bound, and are bitwise equal where no K slices are
+ * involved (K slices add their partial sums in slice order). 0 for an invalid shape.
  */
 size_t mx_a4w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

@@ -44,6 +44,24 @@ mx_status mx_calib_mfma(int64_t ctas, int64_t iters, void* sink, hipStream_t str
 /* Floating-point operations of one mx_calib_mfma launch (2 * 16 * 16 * 128 per MFMA). */
 double mx_calib_mfma_flops(int64_t ctas, int64_t iters);
 
+/*
+ * The MFMA ceiling on given operand data. The rate of the block-scaled FP4 MFMA depends on
+ * the operand bits (the device lowers its clock under the multipliers' power draw), so a
+ * GEMM is best compared with the rate on its own operands. One launch of `ctas` workgroups
+ * of 256 threads (four waves, one per SIMD); each wave reads one 16 KiB window of `ops`
+ * (wave w takes window w modulo floor(bytes / 16384)): sixteen 1 KiB operand blocks in the
+ * prepared layout (lane l's 16 bytes at 16 l of each block), then issues `iters` rounds of
+ * the 64 block products of an 8 x 8 block tile with unit scales, accumulating in place. No
+ * memory traffic after the first reads but one conditional 4-byte store to `sink`, as
+ * above. bytes >= 16384; ops 16-byte aligned; ctas in [1, 2^20], iters in [1, 2^24].
+ * Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE (not gfx950), MX_ERR_HIP.
+ */
+mx_status mx_calib_mfma_operands(const void* ops, size_t bytes, int64_t ctas, int64_t iters, void* sink,
+                                 hipStream_t stream);
+
+/* Floating-point operations of one mx_calib_mfma_operands launch (64 MFMAs per wave and round). */
+double mx_calib_mfma_operands_flops(int64_t ctas, int64_t iters);
+
 #ifdef __cplusplus
 }
 #endif

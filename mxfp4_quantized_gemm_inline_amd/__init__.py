@@ -45,6 +45,8 @@ SIGNATURES = {
     "mx_calib_read": (_c_int, [_vp, _c_sz, _c_i64, _vp, _vp]),
     "mx_calib_mfma": (_c_int, [_c_i64, _c_i64, _vp, _vp]),
     "mx_calib_mfma_flops": (ctypes.c_double, [_c_i64, _c_i64]),
+    "mx_calib_mfma_operands": (_c_int, [_vp, _c_sz, _c_i64, _c_i64, _vp, _vp]),
+    "mx_calib_mfma_operands_flops": (ctypes.c_double, [_c_i64, _c_i64]),
 }
 
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE, MX_ERR_WORKSPACE, MX_ERR_HIP = range(7)
@@ -436,6 +438,21 @@ def mx_calib_mfma_flops(ctas: int, iters: int) -> float:
     return float(lib().mx_calib_mfma_flops(int(ctas), int(iters)))
 
 
+def mx_calib_mfma_operands(ops, ctas: int, iters: int, sink, stream=None) -> None:
+    """The MFMA loop on the operand bytes of `ops` (a contiguous device tensor of at least
+    16 KiB, e.g. a prepared weight); `sink` is a device tensor of at least 4 bytes."""
+    _dev(ops, None, "ops")
+    _dev(sink, None, "sink")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    _check(lib().mx_calib_mfma_operands(ops.data_ptr(), ops.numel() * ops.element_size(), int(ctas), int(iters),
+                                        sink.data_ptr(), _stream_ptr(stream)), "mx_calib_mfma_operands")
+
+
+def mx_calib_mfma_operands_flops(ctas: int, iters: int) -> float:
+    return float(lib().mx_calib_mfma_operands_flops(int(ctas), int(iters)))
+
+
 __all__ = [
     "LIB_PATH", "MxError", "lib", "status_string", "mx_prepared_layout_version",
     "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
@@ -443,5 +460,5 @@ __all__ = [
     "mx_a4w4_gemm_plan", "mx_a16w4_gemm_plan", "mx_a4w4_gemm_grouped_plan", "mx_a4w4_gemm_grouped_act_quant",
     "mx_a4w4_gemm_grouped_act_quant_plan", "mx_a4w4_gemm_grouped_mx", "mx_a4w4_gemm_grouped_mx_plan",
     "mx_moe_combine", "mx_a16w4_gemm", "MX_ACT_SILU", "MX_ACT_SWIGLU", "mx_calib_read", "mx_calib_mfma",
-    "mx_calib_mfma_flops",
+    "mx_calib_mfma_flops", "mx_calib_mfma_operands", "mx_calib_mfma_operands_flops",
 ]

@@ -54,6 +54,46 @@ __global__ __launch_bounds__(kThreads, 2) void k_calib_mfma(int iters, float* __
   if (s == 1.2345678e-30f) sink[0] = s;
 }
 
+// The same MFMA on caller-supplied operands: the multipliers' power draw, and with it the
+// clock the device holds, depends on the operand bits (on MI355X the rate with uniformly
+// random E2M1 codes is about three quarters of that with constant codes), so a ceiling
+// for a GEMM is measured on that GEMM's own data. Each wave takes a 16 KiB window of the
+// buffer (wave w: window w modulo the number of whole windows) as eight 1 KiB operand blocks
+// per side, in the prepared layout's lane order, and issues `iters` rounds of the 8 x 8 block
+// products a 128 x 128 wave tile of the register-direct GEMM issues per K step: 64
+// accumulators in the AGPRs, one wave per SIMD, unit scales.
+constexpr int kOpWindow = 16384;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_calib_mfma_ops(const u32x4* __restrict__ ops, int64_t windows, int iters, float* __restrict__ sink) {
+  const uint32_t l = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const u32x4* base = ops + (gw % windows) * (kOpWindow / 16);
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = base[i * 64 + l];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = base[512 + j * 64 + l];
+  v4f acc[8][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  const uint32_t unit = 0x7F7F7F7Fu;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx::mfma_fp4_tied<0, 0>(acc[j][i], b[j], a[i], unit, unit);
+  }
+  mx::mfma_drain();
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += acc[j][i][0] + acc[j][i][3];
+  if (s == 1.2345678e-30f) sink[0] = s;
+}
+
 }  // namespace
 
 extern "C" mx_status mx_calib_read(const void* buf, size_t bytes, int64_t ctas, void* sink, hipStream_t stream) {
@@ -80,4 +120,20 @@ extern "C" mx_status mx_calib_mfma(int64_t ctas, int64_t iters, void* sink, hipS
 
 extern "C" double mx_calib_mfma_flops(int64_t ctas, int64_t iters) {
   return (double)ctas * (kThreads / 64) * (double)iters * kChains * (2.0 * 16 * 16 * 128);
+}
+
+extern "C" mx_status mx_calib_mfma_operands(const void* ops, size_t bytes, int64_t ctas, int64_t iters, void* sink,
+                                            hipStream_t stream) {
+  if (!ops || !sink) return MX_ERR_NULL;
+  if (bytes < (size_t)kOpWindow || ctas < 1 || ctas > kMaxCtas || iters < 1 || iters > kMaxIters) return MX_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(ops) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0) return MX_ERR_ALIGN;
+  const mx_status d = mx::check_device();
+  if (d != MX_OK) return d;
+  hipLaunchKernelGGL(k_calib_mfma_ops, dim3((unsigned)ctas), dim3(kThreads), 0, stream, static_cast<const u32x4*>(ops),
+                     (int64_t)(bytes / kOpWindow), (int)iters, static_cast<float*>(sink));
+  return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_HIP;
+}
+
+extern "C" double mx_calib_mfma_operands_flops(int64_t ctas, int64_t iters) {
+  return (double)ctas * (kThreads / 64) * (double)iters * 64 * (2.0 * 16 * 16 * 128);
 }

@@ -145,17 +145,20 @@ __device__ __forceinline__ void zero_block(uint32_t (&x)[16]) {
 // L2, so CTA i is given logical tile (its XCD's contiguous share) and logical tiles walk
 // GM tile-rows at a time; the CTAs resident on one XCD then share activation rows and
 // weight columns in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int i, int total, int tiles_m, int tiles_n, int GM, int& bm,
-                                            int& bn) {
-  const int q = total / 8, r = total % 8;
-  const int x = i % 8, j = i / 8;
-  const int logical = x * q + min(x, r) + j;
+// Logical tile -> (tile row, tile column): GM tile-rows at a time, down the rows first.
+__device__ __forceinline__ void logical_tile(int logical, int tiles_m, int tiles_n, int GM, int& bm, int& bn) {
   const int gsize = GM * tiles_n;
   const int grp = logical / gsize, first = grp * GM;
   const int gm = min(tiles_m - first, GM);
   const int rem = logical - grp * gsize;
   bm = first + rem % gm;
   bn = rem / gm;
+}
+__device__ __forceinline__ void tile_coords(int i, int total, int tiles_m, int tiles_n, int GM, int& bm,
+                                            int& bn) {
+  const int q = total / 8, r = total % 8;
+  const int x = i % 8, j = i / 8;
+  logical_tile(x * q + min(x, r) + j, tiles_m, tiles_n, GM, bm, bn);
 }
 
 template <int N_, typename F>
@@ -189,6 +192,45 @@ __device__ __forceinline__ v4f mfma_fp4_sel(const u32x4& a, const u32x4& b, v4f 
   v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, SA, (int)sa, SB, (int)sb);
+}
+
+// The block-scaled FP4 MFMA through inline assembly with the accumulator tied to the
+// destination ("+a", an AGPR tuple), for waves whose 64 accumulators fill the AGPRs: through
+// the builtin the compiler picked the untied form at that register pressure and rotated
+// accumulators through copies every step. The compiler still places the s_waitcnt for the
+// operands (it sees the assembly read them); what it cannot see is the MFMA's own result
+// latency, so a VALU read of an accumulator after the last MFMA needs mfma_drain() first.
+template <int SA, int SB>
+__device__ __forceinline__ void mfma_fp4_tied(v4f& acc, const u32x4& a, const u32x4& b, uint32_t sa, uint32_t sb) {
+  // scale byte select: A byte = op_sel[0] | 2 op_sel_hi[0], B byte = op_sel[1] | 2 op_sel_hi[1]
+#define MXQ(A0, A1, B0, B1)                                                                                  \
+  asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #A0 "," #B0 ",0] op_sel_hi:[" #A1 \
+      "," #B1 ",0] cbsz:4 blgp:4"                                                                           \
+      : "+a"(acc)                                                                                         \
+      : "v"(a), "v"(b), "v"(sa), "v"(sb))
+  if constexpr (SA == 0 && SB == 0) MXQ(0, 0, 0, 0);
+  else if constexpr (SA == 0 && SB == 1) MXQ(0, 0, 1, 0);
+  else if constexpr (SA == 0 && SB == 2) MXQ(0, 0, 0, 1);
+  else if constexpr (SA == 0 && SB == 3) MXQ(0, 0, 1, 1);
+  else if constexpr (SA == 1 && SB == 0) MXQ(1, 0, 0, 0);
+  else if constexpr (SA == 1 && SB == 1) MXQ(1, 0, 1, 0);
+  else if constexpr (SA == 1 && SB == 2) MXQ(1, 0, 0, 1);
+  else if constexpr (SA == 1 && SB == 3) MXQ(1, 0, 1, 1);
+  else if constexpr (SA == 2 && SB == 0) MXQ(0, 1, 0, 0);
+  else if constexpr (SA == 2 && SB == 1) MXQ(0, 1, 1, 0);
+  else if constexpr (SA == 2 && SB == 2) MXQ(0, 1, 0, 1);
+  else if constexpr (SA == 2 && SB == 3) MXQ(0, 1, 1, 1);
+  else if constexpr (SA == 3 && SB == 0) MXQ(1, 1, 0, 0);
+  else if constexpr (SA == 3 && SB == 1) MXQ(1, 1, 1, 0);
+  else if constexpr (SA == 3 && SB == 2) MXQ(1, 1, 0, 1);
+  else MXQ(1, 1, 1, 1);
+#undef MXQ
+}
+
+// 32 wait states between the last MFMA's accumulator write and the moves that read them.
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace mx

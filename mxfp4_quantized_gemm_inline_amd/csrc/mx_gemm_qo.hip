@@ -255,6 +255,188 @@ void k_gemm_qo(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
   store_tile<S::BM, S::BN, MT, NG, WN>(acc, smem, C, M, N, bm, bn);
 }
 
+// ---------------------------------------------------------------------- k_gemm_qr
+//
+// The register-direct form: one wave per SIMD owns a 16 MT x 16 NG output tile (128 x 128)
+// and streams both prepared operands straight from global memory into its registers, D steps
+// ahead, with no LDS and no barrier in the K loop, so no wave ever waits for another. Its
+// MT x NG = 64 accumulators fill the 256 AGPRs (mfma_fp4_tied). Every step's loads are
+// fenced as a group ahead of its MFMAs so that D steps stay in flight.
+//
+// The chip holds one such wave per SIMD (1024). When the tiles exceed that by a little
+// (8448 x 2048: 1056 tiles) the last `tail` logical tiles would run as a second, nearly
+// empty round; instead each is cut into `slices` K ranges run by CTAs of their own, which
+// write FP32 partial tiles, and k_qr_tail_reduce adds them in slice order. The other tiles
+// sum their K steps in order 0..T-1, as every inline kernel does.
+
+template <int MT, int NG>
+struct QRShape {
+  static constexpr int BM = 16 * MT, BN = 16 * NG;
+  static constexpr int CROW = BN * 2 + 16;  // bf16 staging row, padded by 16 bytes
+  static constexpr int SMEM = BM * CROW;
+  static_assert(MT % 4 == 0 && NG % 4 == 0, "a wave's tiles cover whole scale words");
+};
+
+// Ap: activations in the prepared layout for Mp = round_up(M, 64) rows; Wp: the prepared
+// weight [N, K] (N % 16 NG == 0); C: bf16 [M, N]. CTAs 0 .. full - 1 (full = tiles - tail)
+// own whole tiles, dealt in the XCD-aware order over the first `full` logical tiles; CTA
+// full + u (u < tail * slices) computes K slice u % slices of logical tile full + u / slices
+// into P[u] (BM x BN FP32, row-major). Rows >= M are computed from clamped operand blocks and
+// never stored.
+template <int MT, int NG, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
+               float* __restrict__ P, int M, int N, int K, int GM, int tail, int slices) {
+  using S_ = QRShape<MT, NG>;
+  constexpr int S = D + 1;  // register sets in the ring
+  constexpr int MQ = MT / 4, NQ = NG / 4;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int T = steps_of(K);
+  const int Mp = (M + 63) / 64 * 64;
+  const int GAall = Mp / 16;
+  const int tiles_m = (M + S_::BM - 1) / S_::BM, tiles_n = N / S_::BN;
+  const int full = tiles_m * tiles_n - tail;
+  int bm, bn, t0 = 0, t1 = T;
+  const bool part = (int)blockIdx.x >= full;
+  if (!part) {
+    tile_coords(blockIdx.x, full, tiles_m, tiles_n, GM, bm, bn);
+  } else {
+    const int u = blockIdx.x - full, TS = (T + slices - 1) / slices;
+    logical_tile(full + u / slices, tiles_m, tiles_n, GM, bm, bn);
+    t0 = min(T, (u % slices) * TS);
+    t1 = min(T, t0 + TS);
+  }
+  const int lane = threadIdx.x;
+  const uint8_t* pa[MT];
+  const uint8_t* pw[NG];
+  const uint8_t* psa[MQ];
+  const uint8_t* psw[NQ];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) pa[i] = Ap + (size_t)min(bm * MT + i, GAall - 1) * T * 1024;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) pw[j] = Wp + (size_t)(bn * NG + j) * T * 1024;
+#pragma unroll
+  for (int q = 0; q < MQ; ++q)
+    psa[q] = Ap + payload_bytes(Mp, K) + (size_t)min(bm * MQ + q, GAall / 4 - 1) * T * 256;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) psw[q] = Wp + payload_bytes(N, K) + (size_t)(bn * NQ + q) * T * 256;
+
+  // ring set s holds step t's operands for (t - t0) % S == s; steps past the last load the
+  // last step again (never used)
+  u32x4 a[S][MT], b[S][NG];
+  uint32_t sa[S][MQ], sb[S][NQ];
+  const int tlast = max(t1 - 1, 0);
+  auto load = [&](int t, auto s_c) {
+    constexpr int s = decltype(s_c)::value;
+    const uint32_t tt = (uint32_t)min(t, tlast);
+    const uint32_t o = tt * 1024 + lane * 16, os = tt * 256 + lane * 4;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) a[s][i] = *reinterpret_cast<const u32x4*>(pa[i] + o);
+#pragma unroll
+    for (int j = 0; j < NG; ++j) b[s][j] = *reinterpret_cast<const u32x4*>(pw[j] + o);
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) sa[s][q] = *reinterpret_cast<const uint32_t*>(psa[q] + os);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) sb[s][q] = *reinterpret_cast<const uint32_t*>(psw[q] + os);
+  };
+  v4f acc[NG][MT];
+#pragma unroll
+  for (int j = 0; j < NG; ++j)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto mfmas = [&](auto s_c) {
+    constexpr int s = decltype(s_c)::value;
+    static_for<NG>([&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      static_for<MT>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        mfma_fp4_tied<j & 3, i & 3>(acc[j][i], b[s][j], a[s][i], sb[s][j >> 2], sa[s][i >> 2]);
+      });
+    });
+  };
+
+  static_for<D>([&](auto s_c) { load(t0 + decltype(s_c)::value, s_c); });
+  int t = t0;
+  for (; t + S <= t1; t += S) {
+    static_for<S>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      load(t + s + D, std::integral_constant<int, (s + D) % S>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s_c);
+    });
+  }
+  // the last (t1 - t0) % S steps (their operands are in sets 0 .. (t1 - t0) % S - 1)
+  static_for<S - 1>([&](auto s_c) {
+    if (t + decltype(s_c)::value < t1) mfmas(s_c);
+  });
+  mfma_drain();
+
+  if (part) {
+    // FP32 partial tile, row-major: lane l holds rows 16 i + l % 16, columns 16 j + 4 (l / 16) + 0..3
+    float* Pt = P + (size_t)(blockIdx.x - full) * S_::BM * S_::BN;
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int r = 16 * i + (lane & 15), cl = 16 * j + 4 * (lane >> 4);
+        *reinterpret_cast<v4f*>(Pt + r * S_::BN + cl) = acc[j][i];
+      }
+    return;
+  }
+  // epilogue: stage the bf16 tile in this wave's LDS, then store whole rows, 16 bytes a lane
+#pragma unroll
+  for (int j = 0; j < NG; ++j)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int r = 16 * i + (lane & 15), cl = 16 * j + 4 * (lane >> 4);
+      *reinterpret_cast<uint2*>(smem + r * S_::CROW + cl * 2) =
+          pack4_bf16(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+    }
+  __syncthreads();
+  constexpr int CPR = S_::BN / 8;  // 16-byte chunks per tile row
+  const int m0 = bm * S_::BM, n0 = bn * S_::BN;
+#pragma unroll
+  for (int k = 0; k < S_::BM * CPR / 64; ++k) {
+    const int id = lane + 64 * k;
+    const int r = id / CPR, ch = id % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * S_::CROW + ch * 16);
+    if (m0 + r < M)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)(m0 + r) * N + n0 + 8 * ch));
+  }
+}
+
+// The tail tiles of k_gemm_qr: tile v (logical tile full + v) is the sum of P[v * slices + s]
+// over s = 0 .. slices - 1 in that order, written as bf16 (rows < M). One CTA of 256 threads
+// per tile; a thread adds 8 adjacent columns of BM / 32 rows.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void k_qr_tail_reduce(const float* __restrict__ P, uint16_t* __restrict__ C, int M,
+                                                       int N, int GM, int full, int slices) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+  int bm, bn;
+  logical_tile(full + blockIdx.x, tiles_m, tiles_n, GM, bm, bn);
+  constexpr int CPR = BN / 8, RPP = 256 / CPR;  // 8-column chunks per row, rows per pass
+  const int ch = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+  const float* Pv = P + (size_t)blockIdx.x * slices * BM * BN;
+  for (int r = r0; r < BM; r += RPP) {
+    const int m = bm * BM + r;
+    if (m >= M) break;
+    float x[8];
+    const float* q = Pv + r * BN + ch * 8;
+    const v4f lo = *reinterpret_cast<const v4f*>(q), hi = *reinterpret_cast<const v4f*>(q + 4);
+    x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3]; x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
+    for (int s = 1; s < slices; ++s) {
+      const float* qs = q + (size_t)s * BM * BN;
+      const v4f l2 = *reinterpret_cast<const v4f*>(qs), h2 = *reinterpret_cast<const v4f*>(qs + 4);
+      x[0] += l2[0]; x[1] += l2[1]; x[2] += l2[2]; x[3] += l2[3];
+      x[4] += h2[0]; x[5] += h2[1]; x[6] += h2[2]; x[7] += h2[3];
+    }
+    const uint2 p0 = pack4_bf16(x[0], x[1], x[2], x[3]), p1 = pack4_bf16(x[4], x[5], x[6], x[7]);
+    const u32x4 v = {p0.x, p0.y, p1.x, p1.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * N + bn * BN + ch * 8));
+  }
+}
+
 // ====================================================================== launchers
 
 // Compiled configurations (WM, WN, MT, NG, NBUF, OCC): 256 x 256 as 2 x 4 waves of 128 x 64 (two
@@ -290,7 +472,62 @@ hipError_t run_qo(int id, const void* ap, const void* wp, void* c, int M, int N,
   return hipGetLastError();
 }
 
+// Register-direct configurations (MT, NG, D).
+#define MX_QR_CONFIGS(X) X(8, 8, 2)
+
+template <int MT, int NG, int D>
+hipError_t run_qr(const void* ap, const void* wp, void* c, float* P, int M, int N, int K, int GM, int tail,
+                  int slices, hipStream_t st) {
+  using S = QRShape<MT, NG>;
+  const int64_t tiles = (int64_t)((M + S::BM - 1) / S::BM) * (N / S::BN);
+  const int64_t grid = tiles - tail + (int64_t)tail * slices;
+  hipLaunchKernelGGL((k_gemm_qr<MT, NG, D>), dim3((unsigned)grid), dim3(64), S::SMEM, st,
+                     static_cast<const uint8_t*>(ap), static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), P,
+                     M, N, K, GM, tail, slices);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || tail == 0) return e;
+  hipLaunchKernelGGL((k_qr_tail_reduce<S::BM, S::BN>), dim3((unsigned)tail), dim3(256), 0, st,
+                     static_cast<const float*>(P), static_cast<uint16_t*>(c), M, N, GM, (int)(tiles - tail), slices);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool qr_supported(int MT, int NG, int D) {
+#define X(mt, ng, d) if (MT == mt && NG == ng && D == d) return true;
+  MX_QR_CONFIGS(X)
+#undef X
+  return false;
+}
+
+// Tail tiles split into K slices: the tiles beyond one wave per SIMD of the chip (256 CUs x
+// 4), when they are at most a quarter round; none otherwise.
+int qr_tail_tiles(int64_t M, int64_t N, int MT, int NG) {
+  const int64_t tiles = (M + 16 * MT - 1) / (16 * MT) * (N / (16 * NG));
+  constexpr int64_t kSlots = 256 * 4;
+  return tiles > kSlots && tiles <= kSlots + kSlots / 4 ? (int)(tiles - kSlots) : 0;
+}
+
+size_t qr_workspace_bytes(int64_t M, int64_t N, int64_t K, int MT, int NG, int slices) {
+  const size_t act = (qo_act_bytes(M, K) + 255) / 256 * 256;
+  return act + (size_t)qr_tail_tiles(M, N, MT, NG) * slices * (16 * MT) * (16 * NG) * 4;
+}
+
+hipError_t launch_gemm_qr(int MT, int NG, int D, int slices, const void* a, const void* wp, void* c, int64_t M,
+                          int64_t N, int64_t K, int GM, void* ws, hipStream_t st) {
+  if (!qr_supported(MT, NG, D) || N % (16 * NG) != 0 || slices < 1) return hipErrorInvalidValue;
+  const int64_t Mp = (M + 63) / 64 * 64;
+  const int tail = slices > 1 ? qr_tail_tiles(M, N, MT, NG) : 0;
+  float* P = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (qo_act_bytes(M, K) + 255) / 256 * 256);
+  hipError_t e = launch_prepare_rows(a, M, Mp, K, ws, st);
+  if (e != hipSuccess) return e;
+#define X(mt, ng, d)                                                                                     \
+  if (MT == mt && NG == ng && D == d)                                                                    \
+    return run_qr<mt, ng, d>(ws, wp, c, P, (int)M, (int)N, (int)K, GM, tail, slices, st);
+  MX_QR_CONFIGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
 
 size_t qo_act_bytes(int64_t M, int64_t K) {
   const int64_t Mp = (M + 63) / 64 * 64;

@@ -47,6 +47,15 @@ size_t qo_act_bytes(int64_t M, int64_t K);
 bool qo_supported(int WM, int WN, int MT, int NG, int NBUF, int OCC);
 hipError_t launch_gemm_qo(int WM, int WN, int MT, int NG, int NBUF, int OCC, const void* a, const void* wp, void* c,
                           int64_t M, int64_t N, int64_t K, int GM, void* ws, hipStream_t st);
+// The register-direct form: k_prepare as above, then k_gemm_qr<MT, NG, D> (one wave per
+// 16 MT x 16 NG tile, operands D steps ahead in registers; N % (16 NG) == 0). With slices > 1
+// the tiles beyond one round of the chip (qr_tail_tiles) run as `slices` K slices each into
+// FP32 partials after the activations in ws, added in slice order by k_qr_tail_reduce.
+bool qr_supported(int MT, int NG, int D);
+int qr_tail_tiles(int64_t M, int64_t N, int MT, int NG);
+size_t qr_workspace_bytes(int64_t M, int64_t N, int64_t K, int MT, int NG, int slices);
+hipError_t launch_gemm_qr(int MT, int NG, int D, int slices, const void* a, const void* wp, void* c, int64_t M,
+                          int64_t N, int64_t K, int GM, void* ws, hipStream_t st);
 // C [M, N] bf16 = the sum over s = 0..S-1, in order, of the FP32 partials P[s] [M, N].
 hipError_t launch_splitk_reduce(const float* P, void* c, int64_t M, int64_t N, int S, hipStream_t st);
 // Name the kernel(s) the launchers above would run (false: the tuning override is invalid).

@@ -1277,7 +1277,8 @@ struct GemmConfig {
   bool sweep = false;                    // short-K sweep kernel (uses J, GM)
   int J = 1;                             // sweep kernel: column tiles per CTA
   bool qo = false;                       // quantize-once path (uses WM, WN, MT, NG, NBUF, OCC, GM)
-  int NBUF = 4;                          // quantize-once kernel: LDS stage buffers
+  int NBUF = 4;                          // quantize-once kernel: LDS stage buffers (register-direct: steps ahead)
+  bool qr = false;                       // quantize-once, register-direct kernel (qo too; uses MT, NG, NBUF, GM)
 };
 
 #define MX_STREAM_CONFIGS(X) \
@@ -1411,6 +1412,7 @@ bool tile_supported(const GemmConfig& c) {
 
 hipError_t run_config(const GemmConfig& c, const void* a, const void* wp, void* out, float* P, int M,
                       int N, int K, hipStream_t st) {
+  if (c.qr) return launch_gemm_qr(c.MT, c.NG, c.NBUF, c.S, a, wp, out, M, N, K, c.GM, P, st);
   if (c.qo) return launch_gemm_qo(c.WM, c.WN, c.MT, c.NG, c.NBUF, c.OCC, a, wp, out, M, N, K, c.GM, P, st);
   if (c.sweep) {
     const int T = steps_of(K);
@@ -1508,6 +1510,13 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   // N=1536 (48 tiles) the inline kernel with K slices stays ahead (21 against 28 us).
   const int64_t t256 = ((int64_t)M + 255) / 256 * ((N + 255) / 256);
   const int64_t t128 = ((int64_t)M + 127) / 128 * ((N + 127) / 128);
+  // Slightly more 128 x 128 tiles than one wave per SIMD of the chip (8448 x 7168 at M=2048:
+  // 1056): the register-direct kernel, the tiles past one round in four K slices (90 -> 86 us
+  // there; with the whole last round 96 us, and eight slices 93 us).
+  if (T >= 16 && qr_tail_tiles(M, N, 8, 8) > 0 && qr_workspace_bytes(M, N, K, 8, 8, 4) <= ws_bytes) {
+    c.qo = true; c.qr = true; c.MT = 8; c.NG = 8; c.NBUF = 2; c.GM = 8; c.S = 4;
+    return c;
+  }
   if (M >= 512 && T >= 16 && t128 >= 150 && qo_act_bytes(M, K) <= ws_bytes) {
     c.qo = true; c.GM = 8; c.OCC = 2;
     if (t256 >= 200 && t256 <= 256) { c.WM = 2; c.WN = 4; c.MT = 8; c.NG = 4; c.NBUF = 4; }
@@ -1566,7 +1575,8 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
 
 // Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming), "t,WM,WN,MT,NG,PF,GM[,OCC[,S]]" (tiled,
 // S = K slices), "k,J,GM" (short-K sweep, J column tiles per CTA), "q,WM,WN,MT,NG,NBUF,OCC,GM"
-// (quantize-once: k_prepare of the activations into the workspace, then k_gemm_qo)
+// (quantize-once: k_prepare of the activations into the workspace, then k_gemm_qo), "r,MT,NG,D,GM[,S]"
+// (the same with the register-direct k_gemm_qr, operands D steps ahead, tail tiles in S K slices)
 // replaces the default choice. Returns 0 when unset, 1 when applied, -1 when the string
 // does not name a compiled configuration (the call then fails rather than silently
 // running something else).
@@ -1583,6 +1593,10 @@ int override_config(GemmConfig& c) {
     o.tile = true; o.qo = true; o.WM = v[0]; o.WN = v[1]; o.MT = v[2]; o.NG = v[3]; o.NBUF = v[4]; o.OCC = v[5];
     o.GM = v[6] < 1 ? 1 : v[6];
     if (!qo_supported(o.WM, o.WN, o.MT, o.NG, o.NBUF, o.OCC)) return -1;
+  } else if (e[0] == 'r' && std::sscanf(e, "r,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4]) >= 4) {
+    o.tile = true; o.qo = true; o.qr = true; o.MT = v[0]; o.NG = v[1]; o.NBUF = v[2]; o.GM = v[3] < 1 ? 1 : v[3];
+    o.S = v[4] < 1 ? 1 : v[4];
+    if (!qr_supported(o.MT, o.NG, o.NBUF) || o.S > 16) return -1;
   } else if (e[0] == 'k' && std::sscanf(e, "k,%d,%d", &v[0], &v[1]) == 2) {
     o.tile = true; o.sweep = true; o.J = v[0]; o.GM = v[1] < 1 ? 1 : v[1];
   } else if (e[0] == 't' && std::sscanf(e, "t,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5],
@@ -1603,6 +1617,7 @@ int override_config(GemmConfig& c) {
 // Workspace a configuration needs: split-K partials, or the quantized activations of the
 // quantize-once kernel.
 size_t config_workspace(const GemmConfig& c, int64_t M, int64_t N, int64_t K) {
+  if (c.qr) return qr_workspace_bytes(M, N, K, c.MT, c.NG, c.S);
   if (c.qo) return qo_act_bytes(M, K);
   return c.S > 1 ? (size_t)c.S * (size_t)M * (size_t)N * 4 : 0;
 }
@@ -1623,8 +1638,9 @@ bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
   const int ov = override_config(cfg);
   if (ov < 0) return false;
   if (ov > 0 && cfg.sweep && (!sweep_supported(steps_of(K), cfg.J) || N % 128 != 0)) return false;
-  if (ov > 0 && cfg.qo && qo_act_bytes(M, K) > ws_bytes) return false;
-  if (ov > 0 && cfg.tile && cfg.S > 1) {
+  if (ov > 0 && cfg.qo && config_workspace(cfg, M, N, K) > ws_bytes) return false;
+  if (ov > 0 && cfg.qr && (N % (16 * cfg.NG) != 0 || cfg.S > steps_of(K))) return false;
+  if (ov > 0 && cfg.tile && !cfg.qo && cfg.S > 1) {
     const int T = steps_of(K);
     if (cfg.S > T) cfg.S = T;
     if ((size_t)cfg.S * M * N * 4 > ws_bytes) return false;
@@ -1656,7 +1672,12 @@ bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf
   const int M = (int)M64, N = (int)N64, K = (int)K64;
   GemmConfig c;
   if (!resolve_config(M, N, K, ws_bytes, c)) return false;
-  if (c.qo) {
+  if (c.qr) {
+    const int tail = c.S > 1 ? qr_tail_tiles(M, N, c.MT, c.NG) : 0;
+    char tl[64] = "";
+    if (tail > 0) std::snprintf(tl, sizeof tl, " tail=%dx%d + k_qr_tail_reduce", tail, c.S);
+    std::snprintf(buf, len, "k_prepare + k_gemm_qr<%d, %d, %d> GM=%d%s", c.MT, c.NG, c.NBUF, c.GM, tl);
+  } else if (c.qo) {
     std::snprintf(buf, len, "k_prepare + k_gemm_qo<%d, %d, %d, %d, %d, %d> GM=%d", c.WM, c.WN, c.MT, c.NG, c.NBUF,
                   c.OCC, c.GM);
   } else if (c.sweep) {

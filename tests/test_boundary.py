@@ -127,15 +127,21 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     # then both prepared operands are multiplied (k_gemm_qo); without that workspace the
     # inline kernels run
     assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_prepare + k_gemm_qo<2, 4, 8, 4, 4, 2> GM=8"
-    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
+    # 1056 tiles of 128 x 128, a little over one wave per SIMD: the register-direct kernel, the
+    # 32 tiles past the first round in four K slices
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == \
+        "k_prepare + k_gemm_qr<8, 8, 2> GM=8 tail=32x4 + k_qr_tail_reduce"
     assert mx.mx_a4w4_gemm_plan(512, 8448, 7168) == "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
     assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224, workspace_bytes=0) == "k_gemm_tile<1, 8, 8, 4, 1, 2> GM=8"
     assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=0) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
     # the quantize-once workspace: the activations of M rows padded to 64, in the prepared layout
-    assert mx.mx_a4w4_gemm_workspace_bytes(2048, 8448, 7168) == 2048 * 7168 * 17 // 32
+    # (then, for the register-direct kernel, 256-byte aligned FP32 partials of its tail slices)
+    act = 2048 * 7168 * 17 // 32
+    assert mx.mx_a4w4_gemm_workspace_bytes(2048, 8448, 7168) == (act + 255) // 256 * 256 + 32 * 4 * 128 * 128 * 4
     assert mx.mx_a4w4_gemm_workspace_bytes(520, 8448, 7168) == 576 * 7168 * 17 // 32
-    ws = mx.mx_a4w4_gemm_workspace_bytes(2048, 8448, 7168)
-    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=ws - 1).startswith("k_gemm_tile<")
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act) == \
+        "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act - 1).startswith("k_gemm_tile<")
     # N = 1536 at M = 512 gives 48 tiles of 128 x 128: too few, K slices keep it inline
     assert "k_gemm_qo" not in mx.mx_a4w4_gemm_plan(512, 1536, 7168)
     # mid M: 64 x 64 tiles while the activation re-reads stay modest, K slices beyond
@@ -234,6 +240,15 @@ def test_calibration_argument_errors():
     assert L.mx_calib_mfma(8, (1 << 24) + 1, sink, None) == mx.MX_ERR_SHAPE
     # 256 CTAs x 4 waves x 100 rounds x 8 MFMAs x 65,536 flop
     assert mx.mx_calib_mfma_flops(256, 100) == 256 * 4 * 100 * 8 * 65536
+    assert L.mx_calib_mfma_operands(None, 16384, 8, 16, sink, None) == mx.MX_ERR_NULL
+    assert L.mx_calib_mfma_operands(A, 16384, 8, 16, None, None) == mx.MX_ERR_NULL
+    assert L.mx_calib_mfma_operands(A, 16383, 8, 16, sink, None) == mx.MX_ERR_SHAPE  # less than one window
+    assert L.mx_calib_mfma_operands(A, 16384, 0, 16, sink, None) == mx.MX_ERR_SHAPE
+    assert L.mx_calib_mfma_operands(A, 16384, 8, 0, sink, None) == mx.MX_ERR_SHAPE
+    assert L.mx_calib_mfma_operands(A, 16384, 8, (1 << 24) + 1, sink, None) == mx.MX_ERR_SHAPE
+    assert L.mx_calib_mfma_operands(MIS, 16384, 8, 16, sink, None) == mx.MX_ERR_ALIGN
+    # 256 CTAs x 4 waves x 100 rounds x 64 MFMAs x 65,536 flop
+    assert mx.mx_calib_mfma_operands_flops(256, 100) == 256 * 4 * 100 * 64 * 65536
 
 
 def test_gemm2_plan_picks_the_sweep_for_long_segments_at_short_k(monkeypatch):
@@ -390,3 +405,23 @@ def test_binding_checks_sizes_before_any_pointer_is_taken():
         mx.mx_moe_combine(_meta((R, N2), bf), _meta((T, 16), i32), _meta((T, 16), f32), out=_meta((T, N2 - 8), bf))
     with pytest.raises(TypeError):
         mx.mx_moe_combine(_meta((R, N2), bf), _meta((T, 16), torch.int64), _meta((T, 16), f32))
+
+
+def test_register_direct_override_plans(monkeypatch):
+    """The tuning override for the register-direct quantize-once kernel: tail slices only
+    when the tiles pass one wave per SIMD, a workspace that holds their partials, and no
+    configuration that is not compiled."""
+    monkeypatch.setenv("MX_GEMM_CONFIG", "r,8,8,2,8")
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_prepare + k_gemm_qr<8, 8, 2> GM=8"
+    monkeypatch.setenv("MX_GEMM_CONFIG", "r,8,8,2,16,4")
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_prepare + k_gemm_qr<8, 8, 2> GM=16"  # 896 tiles
+    big = 1 << 30
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=big) == \
+        "k_prepare + k_gemm_qr<8, 8, 2> GM=16 tail=32x4 + k_qr_tail_reduce"
+    act = (2048 * 7168 * 17 // 32 + 255) // 256 * 256
+    with pytest.raises(mx.MxError):  # no room for the partials
+        mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act + 32 * 4 * 65536 - 1)
+    for bad in ("r,8,8,3,8", "r,4,8,2,8", "r,8,8,2,8,17"):
+        monkeypatch.setenv("MX_GEMM_CONFIG", bad)
+        with pytest.raises(mx.MxError):
+            mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=big)

@@ -16,6 +16,9 @@ def test_calibration_kernels_run():
         mx.mx_calib_read(buf, ctas, sink)
     mx.mx_calib_read(buf[:4112], 2, sink)  # a ragged tail after the unrolled rounds
     mx.mx_calib_mfma(8, 16, sink)
+    ops = torch.randint(0, 256, (3 * 16384 + 100,), dtype=torch.uint8, device="cuda")
+    for ctas in (1, 5):  # 4 and 20 waves over the 3 whole windows of the buffer
+        mx.mx_calib_mfma_operands(ops, ctas, 16, sink)
     torch.cuda.synchronize()
     assert sink.cpu().tolist() == [7, 7, 7, 7]
     with pytest.raises(mx.MxError):

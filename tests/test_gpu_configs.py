@@ -26,6 +26,8 @@ TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8,
         (1, 8, 8, 4, 1, 2), (1, 4, 4, 1, 2, 1), (1, 4, 4, 1, 2, 2)]
 # mirrors MX_QO_CONFIGS in mx_gemm_qo.hip: (WM, WN, MT, NG, NBUF, OCC)
 QO = [(2, 4, 8, 4, 4, 2), (2, 2, 4, 4, 4, 2), (2, 2, 4, 4, 5, 2), (1, 4, 8, 4, 3, 2)]
+# mirrors MX_QR_CONFIGS in mx_gemm_qo.hip: (MT, NG, D)
+QR = [(8, 8, 2)]
 SWEEP_K = (256, 512, 768, 1024)  # the short-K sweep kernel's compiled step counts 2, 4, 6, 8
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
 K_TESTS = (4224, 768)  # 33 and 6 steps of 128
@@ -133,6 +135,86 @@ def test_quantize_once_config(cfg, K):
         inline = _run("t,1,4,4,4,1,8,2", a[:M], wp, False)
         torch.cuda.synchronize()
         assert np.array_equal(got, inline), f"quantize-once {cfg} M={M} K={K}: differs from the inline kernel"
+
+
+@pytest.mark.parametrize("K", (128, 256, 512) + K_TESTS + (7168,))
+@pytest.mark.parametrize("cfg", QR, ids=[f"r{c}" for c in QR])
+def test_register_direct_config(cfg, K):
+    """The register-direct quantize-once kernel (one wave per 128 x 128 tile, operands two
+    steps ahead in registers) at every remainder of its three-step ring (T = 1, 2, 4, 6, 33,
+    56 steps), on a ragged last row tile, a tile of fewer rows than one 64-row quad, several
+    tile orders and canary rows past M; compared with the oracle and bit for bit with the
+    inline kernel (same per-element K order)."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    a, wp, exact = _case(K)
+    for M, gm in ((300, 8), (37, 1), (256, 3)):
+        full = torch.full((M + 5, N_TEST), -7.0, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty((M + 63) // 64 * 64 * K * 17 // 32, dtype=torch.uint8, device="cuda")
+        os.environ["MX_GEMM_CONFIG"] = "r," + ",".join(map(str, cfg)) + f",{gm}"
+        try:
+            mx.mx_a4w4_gemm(dev_bf16(a[:M]), wp, N_TEST, out=full[:M], workspace=ws)
+        finally:
+            del os.environ["MX_GEMM_CONFIG"]
+        torch.cuda.synchronize()
+        got = host_bits(full[:M])
+        check_gemm(got, exact[:M], what=f"register-direct {cfg} GM={gm} M={M} K={K}")
+        assert bool((full[M:] == -7.0).all()), f"register-direct {cfg} M={M} K={K}: rows past M were written"
+        inline = _run("t,1,4,4,4,1,8,2", a[:M], wp, False)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, inline), f"register-direct {cfg} M={M} K={K}: differs from the inline kernel"
+
+
+def _logical_tile(logical, tiles_m, tiles_n, gm):
+    """(tile row, tile column) of a logical tile: GM tile-rows at a time, rows first (the
+    kernels' tile order)."""
+    gsize = gm * tiles_n
+    grp, rem = divmod(logical, gsize)
+    first = grp * gm
+    g = min(tiles_m - first, gm)
+    return first + rem % g, rem // g
+
+
+@pytest.mark.parametrize("K,slices", ((512, 4), (640, 4), (768, 4), (768, 3)))
+def test_register_direct_tail_slices(K, slices):
+    """More 128 x 128 tiles than one wave per SIMD of the chip (1152 > 1024 at M = 1152,
+    N = 16384): the last 128 logical tiles run as K slices (with a slice of one step, of a
+    remainder, and an empty one at T = 6 over 4 slices) whose FP32 partials are added in slice
+    order. Every tile is checked against the oracle; the whole-tile tiles must equal, bit for
+    bit, the run without the split."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    M, N, gm = 1152, 16384, 8
+    a = W.dense_activation(M, K, "plain", seed=25)
+    w = W.dense_weight(N, K, seed=26)
+    qa, sa = O.quantize_mx(a)
+    qw, sw = O.quantize_mx(w)
+    exact = O.gemm_from_mx(qa, sa, qw, sw)
+    wp = mx.mx_prepare_weight(dev_bf16(w))
+    ad = dev_bf16(a)
+    outs = {}
+    for sl in (1, slices):
+        cfg = f"r,8,8,2,{gm},{sl}"
+        os.environ["MX_GEMM_CONFIG"] = cfg
+        try:
+            plan = mx.mx_a4w4_gemm_plan(M, N, K, 1 << 31)
+            assert (f"tail=128x{sl}" in plan) == (sl > 1), plan
+            out = torch.full((M + 3, N), -7.0, dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(48 << 20, dtype=torch.uint8, device="cuda")  # activations + 128 x 4 partial tiles
+            mx.mx_a4w4_gemm(ad, wp, N, out=out[:M], workspace=ws)
+        finally:
+            del os.environ["MX_GEMM_CONFIG"]
+        torch.cuda.synchronize()
+        assert bool((out[M:] == -7.0).all()), f"{cfg}: rows past M were written"
+        outs[sl] = host_bits(out[:M])
+        check_gemm(outs[sl], exact, what=f"register-direct {cfg} M={M} N={N} K={K}")
+    tiles_m, tiles_n = M // 128, N // 128
+    tail = tiles_m * tiles_n - 1024
+    same = np.ones((M, N), dtype=bool)
+    for v in range(tail):
+        bm, bn = _logical_tile(1024 + v, tiles_m, tiles_n, gm)
+        same[bm * 128:(bm + 1) * 128, bn * 128:(bn + 1) * 128] = False
+    assert np.array_equal(outs[1][same], outs[slices][same]), "whole tiles changed with the tail split"
 
 
 def test_quantize_once_needs_workspace():
