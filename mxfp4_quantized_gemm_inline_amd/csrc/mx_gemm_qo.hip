@@ -437,6 +437,155 @@ __global__ __launch_bounds__(256) void k_qr_tail_reduce(const float* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------- k_gemm_qk
+//
+// The register-direct wave of k_gemm_qr, four to a CTA (one per SIMD) on the same 128 x 128
+// tile, each over its own quarter of the CTA's K range: for calls with too few tiles to give
+// every SIMD one (7168 x 4224 at M = 512: 224 tiles, one CTA per CU). The four partial tiles
+// are added through LDS in wave order, half a tile at a time (4 x 64 rows of FP32, rows
+// padded to 132 floats so the 16 rows a wave's float4 store covers fall in distinct banks),
+// and written once. With slices > 1 a CTA covers one of `slices` K ranges of its tile and
+// writes FP32 partials P[slice][M][N], which k_splitk_reduce adds in slice order.
+
+template <int MT, int NG>
+struct QKShape {
+  static constexpr int BM = 16 * MT, BN = 16 * NG;
+  static constexpr int HR = BM / 2;           // rows per reduction half
+  static constexpr int PROW = BN + 4;         // padded FP32 row
+  static constexpr int SMEM = 4 * HR * PROW * 4;
+  static_assert(MT % 4 == 0 && NG % 4 == 0 && MT % 2 == 0, "whole scale words, two halves");
+  static_assert(HR == 64 && BN % 8 == 0, "a wave sums 16 rows of each half, 8 columns a chunk");
+};
+
+template <int MT, int NG, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_qk(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
+               float* __restrict__ P, int M, int N, int K, int GM, int slices) {
+  using S_ = QKShape<MT, NG>;
+  constexpr int S = D + 1;  // register sets in the ring
+  constexpr int MQ = MT / 4, NQ = NG / 4;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int T = steps_of(K);
+  const int Mp = (M + 63) / 64 * 64;
+  const int GAall = Mp / 16;
+  const int tiles_m = (M + S_::BM - 1) / S_::BM, tiles_n = N / S_::BN;
+  // units = (tile, slice), a tile's slices consecutive; units dealt to the XCDs as tiles are
+  const int units = tiles_m * tiles_n * slices;
+  const int q8 = units / 8, r8 = units % 8, x8 = blockIdx.x % 8;
+  const int unit = x8 * q8 + min(x8, r8) + (int)blockIdx.x / 8;
+  const int slice = unit % slices;
+  int bm, bn;
+  logical_tile(unit / slices, tiles_m, tiles_n, GM, bm, bn);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int TSl = (T + slices - 1) / slices;
+  const int k0 = min(T, slice * TSl), k1 = min(T, k0 + TSl);
+  const int TW = (k1 - k0 + 3) / 4;
+  const int t0 = min(k1, k0 + w * TW), t1 = min(k1, t0 + TW);
+
+  const uint8_t* pa[MT];
+  const uint8_t* pw[NG];
+  const uint8_t* psa[MQ];
+  const uint8_t* psw[NQ];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) pa[i] = Ap + (size_t)min(bm * MT + i, GAall - 1) * T * 1024;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) pw[j] = Wp + (size_t)(bn * NG + j) * T * 1024;
+#pragma unroll
+  for (int q = 0; q < MQ; ++q)
+    psa[q] = Ap + payload_bytes(Mp, K) + (size_t)min(bm * MQ + q, GAall / 4 - 1) * T * 256;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) psw[q] = Wp + payload_bytes(N, K) + (size_t)(bn * NQ + q) * T * 256;
+
+  u32x4 a[S][MT], b[S][NG];
+  uint32_t sa[S][MQ], sb[S][NQ];
+  const int tlast = max(t1 - 1, 0);
+  auto load = [&](int t, auto s_c) {
+    constexpr int s = decltype(s_c)::value;
+    const uint32_t tt = (uint32_t)min(t, tlast);
+    const uint32_t o = tt * 1024 + lane * 16, os = tt * 256 + lane * 4;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) a[s][i] = *reinterpret_cast<const u32x4*>(pa[i] + o);
+#pragma unroll
+    for (int j = 0; j < NG; ++j) b[s][j] = *reinterpret_cast<const u32x4*>(pw[j] + o);
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) sa[s][q] = *reinterpret_cast<const uint32_t*>(psa[q] + os);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) sb[s][q] = *reinterpret_cast<const uint32_t*>(psw[q] + os);
+  };
+  v4f acc[NG][MT];
+#pragma unroll
+  for (int j = 0; j < NG; ++j)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto mfmas = [&](auto s_c) {
+    constexpr int s = decltype(s_c)::value;
+    static_for<NG>([&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      static_for<MT>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        mfma_fp4_tied<j & 3, i & 3>(acc[j][i], b[s][j], a[s][i], sb[s][j >> 2], sa[s][i >> 2]);
+      });
+    });
+  };
+
+  static_for<D>([&](auto s_c) { load(t0 + decltype(s_c)::value, s_c); });
+  int t = t0;
+  for (; t + S <= t1; t += S) {
+    static_for<S>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      load(t + s + D, std::integral_constant<int, (s + D) % S>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(s_c);
+    });
+  }
+  static_for<S - 1>([&](auto s_c) {
+    if (t + decltype(s_c)::value < t1) mfmas(s_c);
+  });
+  mfma_drain();
+
+  float* red = reinterpret_cast<float*>(smem);  // [4 waves][64 rows][PROW]
+  const int m0 = bm * S_::BM, n0 = bn * S_::BN;
+  static_for<2>([&](auto h_c) {
+    constexpr int h = decltype(h_c)::value;
+    if constexpr (h == 1) __syncthreads();  // every wave has summed the first half
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int i = h * MT / 2; i < (h + 1) * MT / 2; ++i) {
+        const int r = 16 * (i - h * MT / 2) + (lane & 15), cl = 16 * j + 4 * (lane >> 4);
+        *reinterpret_cast<v4f*>(red + (w * S_::HR + r) * S_::PROW + cl) = acc[j][i];
+      }
+    __syncthreads();
+    // wave w adds rows 16 w .. 16 w + 15 of this half over the four waves, 8 columns a chunk
+    constexpr int CPR = S_::BN / 8;
+#pragma unroll
+    for (int c = 0; c < 16 * CPR / 64; ++c) {
+      const int id = lane + 64 * c;
+      const int r = 16 * w + id / CPR, ch = id % CPR;
+      const float* q = red + r * S_::PROW + 8 * ch;
+      v4f lo = *reinterpret_cast<const v4f*>(q), hi = *reinterpret_cast<const v4f*>(q + 4);
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) {
+        lo += *reinterpret_cast<const v4f*>(q + ww * S_::HR * S_::PROW);
+        hi += *reinterpret_cast<const v4f*>(q + ww * S_::HR * S_::PROW + 4);
+      }
+      const int m = m0 + h * S_::HR + r, n = n0 + 8 * ch;
+      if (m < M) {
+        if (slices > 1) {
+          float* dst = P + ((size_t)slice * M + m) * N + n;
+          *reinterpret_cast<v4f*>(dst) = lo;
+          *reinterpret_cast<v4f*>(dst + 4) = hi;
+        } else {
+          const uint2 p0 = pack4_bf16(lo[0], lo[1], lo[2], lo[3]), p1 = pack4_bf16(hi[0], hi[1], hi[2], hi[3]);
+          const u32x4 v = {p0.x, p0.y, p1.x, p1.y};
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * N + n));
+        }
+      }
+    }
+  });
+}
+
 // ====================================================================== launchers
 
 // Compiled configurations (WM, WN, MT, NG, NBUF, OCC): 256 x 256 as 2 x 4 waves of 128 x 64 (two
@@ -491,7 +640,56 @@ hipError_t run_qr(const void* ap, const void* wp, void* c, float* P, int M, int 
   return hipGetLastError();
 }
 
+// Four-wave configurations (MT, NG, D).
+#define MX_QK_CONFIGS(X) X(8, 8, 2)
+
+std::atomic<uint64_t> g_qk_lds[1];
+
+template <int MT, int NG, int D>
+hipError_t run_qk(const void* ap, const void* wp, void* c, float* P, int M, int N, int K, int GM, int slices,
+                  hipStream_t st) {
+  using S = QKShape<MT, NG>;
+  auto kern = k_gemm_qk<MT, NG, D>;
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), S::SMEM, g_qk_lds[0]);
+  if (e != hipSuccess) return e;
+  const int64_t grid = (int64_t)((M + S::BM - 1) / S::BM) * (N / S::BN) * slices;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), S::SMEM, st, static_cast<const uint8_t*>(ap),
+                     static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), P, M, N, K, GM, slices);
+  e = hipGetLastError();
+  if (e != hipSuccess || slices == 1) return e;
+  return launch_splitk_reduce(P, c, M, N, slices, st);
+}
+
 }  // namespace
+
+bool qk_supported(int MT, int NG, int D) {
+#define X(mt, ng, d) if (MT == mt && NG == ng && D == d) return true;
+  MX_QK_CONFIGS(X)
+#undef X
+  return false;
+}
+
+// Workspace: the prepared activations, then (256-byte aligned) the FP32 partials of `slices`
+// K slices when there are several.
+size_t qk_workspace_bytes(int64_t M, int64_t N, int64_t K, int slices) {
+  const size_t act = (qo_act_bytes(M, K) + 255) / 256 * 256;
+  return slices > 1 ? act + (size_t)slices * M * N * 4 : act;
+}
+
+hipError_t launch_gemm_qk(int MT, int NG, int D, int slices, const void* a, const void* wp, void* c, int64_t M,
+                          int64_t N, int64_t K, int GM, void* ws, hipStream_t st) {
+  if (!qk_supported(MT, NG, D) || N % (16 * NG) != 0 || slices < 1 || 4 * slices > steps_of((int)K))
+    return hipErrorInvalidValue;
+  const int64_t Mp = (M + 63) / 64 * 64;
+  float* P = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (qo_act_bytes(M, K) + 255) / 256 * 256);
+  hipError_t e = launch_prepare_rows(a, M, Mp, K, ws, st);
+  if (e != hipSuccess) return e;
+#define X(mt, ng, d) \
+  if (MT == mt && NG == ng && D == d) return run_qk<mt, ng, d>(ws, wp, c, P, (int)M, (int)N, (int)K, GM, slices, st);
+  MX_QK_CONFIGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
 
 bool qr_supported(int MT, int NG, int D) {
 #define X(mt, ng, d) if (MT == mt && NG == ng && D == d) return true;

@@ -56,6 +56,14 @@ int qr_tail_tiles(int64_t M, int64_t N, int MT, int NG);
 size_t qr_workspace_bytes(int64_t M, int64_t N, int64_t K, int MT, int NG, int slices);
 hipError_t launch_gemm_qr(int MT, int NG, int D, int slices, const void* a, const void* wp, void* c, int64_t M,
                           int64_t N, int64_t K, int GM, void* ws, hipStream_t st);
+// Four register-direct waves per CTA on one tile, each over a quarter of the CTA's K range,
+// added through LDS: k_prepare as above, then k_gemm_qk<MT, NG, D>; with slices > 1 the CTAs
+// of a tile split K `slices` ways into FP32 partials after the activations in ws, added by
+// k_splitk_reduce. Needs 4 * slices <= K / 128.
+bool qk_supported(int MT, int NG, int D);
+size_t qk_workspace_bytes(int64_t M, int64_t N, int64_t K, int slices);
+hipError_t launch_gemm_qk(int MT, int NG, int D, int slices, const void* a, const void* wp, void* c, int64_t M,
+                          int64_t N, int64_t K, int GM, void* ws, hipStream_t st);
 // C [M, N] bf16 = the sum over s = 0..S-1, in order, of the FP32 partials P[s] [M, N].
 hipError_t launch_splitk_reduce(const float* P, void* c, int64_t M, int64_t N, int S, hipStream_t st);
 // Name the kernel(s) the launchers above would run (false: the tuning override is invalid).

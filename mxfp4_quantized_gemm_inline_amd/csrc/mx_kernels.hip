@@ -1278,7 +1278,8 @@ struct GemmConfig {
   int J = 1;                             // sweep kernel: column tiles per CTA
   bool qo = false;                       // quantize-once path (uses WM, WN, MT, NG, NBUF, OCC, GM)
   int NBUF = 4;                          // quantize-once kernel: LDS stage buffers (register-direct: steps ahead)
-  bool qr = false;                       // quantize-once, register-direct kernel (qo too; uses MT, NG, NBUF, GM)
+  bool qr = false;                       // quantize-once, register-direct kernel (qo too; uses MT, NG, NBUF, GM, S)
+  bool qk = false;                       // the same, four waves per tile splitting K (qo too; MT, NG, NBUF, GM, S)
 };
 
 #define MX_STREAM_CONFIGS(X) \
@@ -1413,6 +1414,7 @@ bool tile_supported(const GemmConfig& c) {
 hipError_t run_config(const GemmConfig& c, const void* a, const void* wp, void* out, float* P, int M,
                       int N, int K, hipStream_t st) {
   if (c.qr) return launch_gemm_qr(c.MT, c.NG, c.NBUF, c.S, a, wp, out, M, N, K, c.GM, P, st);
+  if (c.qk) return launch_gemm_qk(c.MT, c.NG, c.NBUF, c.S, a, wp, out, M, N, K, c.GM, P, st);
   if (c.qo) return launch_gemm_qo(c.WM, c.WN, c.MT, c.NG, c.NBUF, c.OCC, a, wp, out, M, N, K, c.GM, P, st);
   if (c.sweep) {
     const int T = steps_of(K);
@@ -1517,6 +1519,13 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
     c.qo = true; c.qr = true; c.MT = 8; c.NG = 8; c.NBUF = 2; c.GM = 8; c.S = 4;
     return c;
   }
+  // Too few 128 x 128 tiles for one wave per SIMD but enough for one CTA per CU, at long K:
+  // four register-direct waves per tile splitting K (1536 x 7168 M=2048, 192 tiles: 32.2 ->
+  // 27.9 us; at K = 4224 with 224 tiles it only ties the LDS kernel).
+  if (M >= 512 && T >= 48 && t128 >= 150 && t128 <= 256 && qk_workspace_bytes(M, N, K, 1) <= ws_bytes) {
+    c.qo = true; c.qk = true; c.MT = 8; c.NG = 8; c.NBUF = 2; c.GM = 8; c.S = 1;
+    return c;
+  }
   if (M >= 512 && T >= 16 && t128 >= 150 && qo_act_bytes(M, K) <= ws_bytes) {
     c.qo = true; c.GM = 8; c.OCC = 2;
     if (t256 >= 200 && t256 <= 256) { c.WM = 2; c.WN = 4; c.MT = 8; c.NG = 4; c.NBUF = 4; }
@@ -1576,7 +1585,8 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
 // Tuning only: MX_GEMM_CONFIG="s,MT,NG,WK,S" (streaming), "t,WM,WN,MT,NG,PF,GM[,OCC[,S]]" (tiled,
 // S = K slices), "k,J,GM" (short-K sweep, J column tiles per CTA), "q,WM,WN,MT,NG,NBUF,OCC,GM"
 // (quantize-once: k_prepare of the activations into the workspace, then k_gemm_qo), "r,MT,NG,D,GM[,S]"
-// (the same with the register-direct k_gemm_qr, operands D steps ahead, tail tiles in S K slices)
+// (the same with the register-direct k_gemm_qr, operands D steps ahead, tail tiles in S K slices),
+// "x,MT,NG,D,GM[,S]" (four register-direct waves per tile splitting K, k_gemm_qk, S K slices)
 // replaces the default choice. Returns 0 when unset, 1 when applied, -1 when the string
 // does not name a compiled configuration (the call then fails rather than silently
 // running something else).
@@ -1597,6 +1607,10 @@ int override_config(GemmConfig& c) {
     o.tile = true; o.qo = true; o.qr = true; o.MT = v[0]; o.NG = v[1]; o.NBUF = v[2]; o.GM = v[3] < 1 ? 1 : v[3];
     o.S = v[4] < 1 ? 1 : v[4];
     if (!qr_supported(o.MT, o.NG, o.NBUF) || o.S > 16) return -1;
+  } else if (e[0] == 'x' && std::sscanf(e, "x,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4]) >= 4) {
+    o.tile = true; o.qo = true; o.qk = true; o.MT = v[0]; o.NG = v[1]; o.NBUF = v[2]; o.GM = v[3] < 1 ? 1 : v[3];
+    o.S = v[4] < 1 ? 1 : v[4];
+    if (!qk_supported(o.MT, o.NG, o.NBUF) || o.S > 16) return -1;
   } else if (e[0] == 'k' && std::sscanf(e, "k,%d,%d", &v[0], &v[1]) == 2) {
     o.tile = true; o.sweep = true; o.J = v[0]; o.GM = v[1] < 1 ? 1 : v[1];
   } else if (e[0] == 't' && std::sscanf(e, "t,%d,%d,%d,%d,%d,%d,%d,%d", &v[0], &v[1], &v[2], &v[3], &v[4], &v[5],
@@ -1618,6 +1632,7 @@ int override_config(GemmConfig& c) {
 // quantize-once kernel.
 size_t config_workspace(const GemmConfig& c, int64_t M, int64_t N, int64_t K) {
   if (c.qr) return qr_workspace_bytes(M, N, K, c.MT, c.NG, c.S);
+  if (c.qk) return qk_workspace_bytes(M, N, K, c.S);
   if (c.qo) return qo_act_bytes(M, K);
   return c.S > 1 ? (size_t)c.S * (size_t)M * (size_t)N * 4 : 0;
 }
@@ -1640,6 +1655,7 @@ bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
   if (ov > 0 && cfg.sweep && (!sweep_supported(steps_of(K), cfg.J) || N % 128 != 0)) return false;
   if (ov > 0 && cfg.qo && config_workspace(cfg, M, N, K) > ws_bytes) return false;
   if (ov > 0 && cfg.qr && (N % (16 * cfg.NG) != 0 || cfg.S > steps_of(K))) return false;
+  if (ov > 0 && cfg.qk && (N % (16 * cfg.NG) != 0 || 4 * cfg.S > steps_of(K))) return false;
   if (ov > 0 && cfg.tile && !cfg.qo && cfg.S > 1) {
     const int T = steps_of(K);
     if (cfg.S > T) cfg.S = T;
@@ -1677,6 +1693,10 @@ bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf
     char tl[64] = "";
     if (tail > 0) std::snprintf(tl, sizeof tl, " tail=%dx%d + k_qr_tail_reduce", tail, c.S);
     std::snprintf(buf, len, "k_prepare + k_gemm_qr<%d, %d, %d> GM=%d%s", c.MT, c.NG, c.NBUF, c.GM, tl);
+  } else if (c.qk) {
+    char split[40] = "";
+    if (c.S > 1) std::snprintf(split, sizeof split, " S=%d + k_splitk_reduce", c.S);
+    std::snprintf(buf, len, "k_prepare + k_gemm_qk<%d, %d, %d> GM=%d%s", c.MT, c.NG, c.NBUF, c.GM, split);
   } else if (c.qo) {
     std::snprintf(buf, len, "k_prepare + k_gemm_qo<%d, %d, %d, %d, %d, %d> GM=%d", c.WM, c.WN, c.MT, c.NG, c.NBUF,
                   c.OCC, c.GM);

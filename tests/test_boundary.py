@@ -425,3 +425,24 @@ def test_register_direct_override_plans(monkeypatch):
         monkeypatch.setenv("MX_GEMM_CONFIG", bad)
         with pytest.raises(mx.MxError):
             mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=big)
+
+
+def test_four_wave_override_plans(monkeypatch):
+    """The tuning override for the four-wave register-direct kernel: K slices need a
+    workspace for their partials and at least one K step per wave."""
+    monkeypatch.setenv("MX_GEMM_CONFIG", "x,8,8,2,8")
+    assert mx.mx_a4w4_gemm_plan(512, 7168, 4224) == "k_prepare + k_gemm_qk<8, 8, 2> GM=8"
+    monkeypatch.setenv("MX_GEMM_CONFIG", "x,8,8,2,8,3")
+    act = (128 * 7168 * 17 // 32 + 255) // 256 * 256
+    need = act + 3 * 128 * 8448 * 4
+    assert mx.mx_a4w4_gemm_plan(128, 8448, 7168, workspace_bytes=need) == \
+        "k_prepare + k_gemm_qk<8, 8, 2> GM=8 S=3 + k_splitk_reduce"
+    with pytest.raises(mx.MxError):
+        mx.mx_a4w4_gemm_plan(128, 8448, 7168, workspace_bytes=need - 1)
+    monkeypatch.setenv("MX_GEMM_CONFIG", "x,8,8,2,8,2")
+    with pytest.raises(mx.MxError):  # 6 steps cannot give 2 x 4 waves a step each
+        mx.mx_a4w4_gemm_plan(512, 7168, 768, workspace_bytes=1 << 30)
+    for bad in ("x,8,8,3,8", "x,4,4,2,8", "x,8,8,2,8,17"):
+        monkeypatch.setenv("MX_GEMM_CONFIG", bad)
+        with pytest.raises(mx.MxError):
+            mx.mx_a4w4_gemm_plan(512, 7168, 4224, workspace_bytes=1 << 30)

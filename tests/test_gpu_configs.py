@@ -26,8 +26,9 @@ TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8,
         (1, 8, 8, 4, 1, 2), (1, 4, 4, 1, 2, 1), (1, 4, 4, 1, 2, 2)]
 # mirrors MX_QO_CONFIGS in mx_gemm_qo.hip: (WM, WN, MT, NG, NBUF, OCC)
 QO = [(2, 4, 8, 4, 4, 2), (2, 2, 4, 4, 4, 2), (2, 2, 4, 4, 5, 2), (1, 4, 8, 4, 3, 2)]
-# mirrors MX_QR_CONFIGS in mx_gemm_qo.hip: (MT, NG, D)
+# mirrors MX_QR_CONFIGS / MX_QK_CONFIGS in mx_gemm_qo.hip: (MT, NG, D)
 QR = [(8, 8, 2)]
+QK = [(8, 8, 2)]
 SWEEP_K = (256, 512, 768, 1024)  # the short-K sweep kernel's compiled step counts 2, 4, 6, 8
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
 K_TESTS = (4224, 768)  # 33 and 6 steps of 128
@@ -163,6 +164,31 @@ def test_register_direct_config(cfg, K):
         inline = _run("t,1,4,4,4,1,8,2", a[:M], wp, False)
         torch.cuda.synchronize()
         assert np.array_equal(got, inline), f"register-direct {cfg} M={M} K={K}: differs from the inline kernel"
+
+
+@pytest.mark.parametrize("K,slices", ((512, 1), (640, 1), (768, 1), (4224, 1), (4224, 2), (4224, 8), (7168, 3)))
+@pytest.mark.parametrize("cfg", QK, ids=[f"x{c}" for c in QK])
+def test_four_wave_config(cfg, K, slices):
+    """Four register-direct waves per 128 x 128 tile, each over a quarter of the CTA's K range
+    (T = 4, 5 (one wave with no step), 6, 33, 56 steps), added through LDS in wave order, with
+    and without K slices across CTAs (FP32 partials added by the split-K reduce); on a ragged
+    last row tile, a tile of fewer rows than one 64-row quad, several tile orders and canary
+    rows past M. Compared with the oracle (the sum order differs from the inline kernel's)."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    a, wp, exact = _case(K)
+    for M, gm in ((300, 8), (37, 1), (256, 3)):
+        full = torch.full((M + 5, N_TEST), -7.0, dtype=torch.bfloat16, device="cuda")
+        act = (M + 63) // 64 * 64 * K * 17 // 32
+        ws = torch.empty((act + 255) // 256 * 256 + slices * M * N_TEST * 4, dtype=torch.uint8, device="cuda")
+        os.environ["MX_GEMM_CONFIG"] = "x," + ",".join(map(str, cfg)) + f",{gm},{slices}"
+        try:
+            mx.mx_a4w4_gemm(dev_bf16(a[:M]), wp, N_TEST, out=full[:M], workspace=ws)
+        finally:
+            del os.environ["MX_GEMM_CONFIG"]
+        torch.cuda.synchronize()
+        check_gemm(host_bits(full[:M]), exact[:M], what=f"four-wave {cfg} S={slices} GM={gm} M={M} K={K}")
+        assert bool((full[M:] == -7.0).all()), f"four-wave {cfg} M={M} K={K}: rows past M were written"
 
 
 def _logical_tile(logical, tiles_m, tiles_n, gm):
