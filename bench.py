@@ -289,10 +289,11 @@ def plan_kernels(plan):
 
 def dispatch_matches(kernel, name):
     """True when a profiler kernel name is a dispatch of `kernel` (template arguments included;
-    a plain name must be followed by its argument list, so k_prepare is not k_prepare_packed)."""
+    a plain name must be followed by its argument or template list, so k_prepare is not
+    k_prepare_packed)."""
     if "<" in kernel:
         return kernel in name
-    return (kernel + "(") in name
+    return (kernel + "(") in name or (kernel + "<") in name
 
 
 def summarize_counters(fetch_dir, write_dir, workload, M, copy_mib):

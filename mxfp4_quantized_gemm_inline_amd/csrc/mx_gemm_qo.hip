@@ -407,34 +407,40 @@ void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
 }
 
 // The tail tiles of k_gemm_qr: tile v (logical tile full + v) is the sum of P[v * slices + s]
-// over s = 0 .. slices - 1 in that order, written as bf16 (rows < M). One CTA of 256 threads
-// per tile; a thread adds 8 adjacent columns of BM / 32 rows.
+// over s = 0 .. slices - 1 in that order, written as bf16 (rows < M). CTA (v, c) of 256
+// threads takes rows 16 c .. 16 c + 15 of tile v, a thread 8 adjacent columns of one row; its
+// slices are loaded eight at a time, all in flight before the first add.
 template <int BM, int BN>
 __global__ __launch_bounds__(256) void k_qr_tail_reduce(const float* __restrict__ P, uint16_t* __restrict__ C, int M,
                                                        int N, int GM, int full, int slices) {
+  static_assert(BN == 128 && BM % 16 == 0, "16 rows of 16 eight-column chunks per CTA");
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+  const int v = blockIdx.x / (BM / 16), c = blockIdx.x % (BM / 16);
   int bm, bn;
-  logical_tile(full + blockIdx.x, tiles_m, tiles_n, GM, bm, bn);
-  constexpr int CPR = BN / 8, RPP = 256 / CPR;  // 8-column chunks per row, rows per pass
-  const int ch = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
-  const float* Pv = P + (size_t)blockIdx.x * slices * BM * BN;
-  for (int r = r0; r < BM; r += RPP) {
-    const int m = bm * BM + r;
-    if (m >= M) break;
-    float x[8];
-    const float* q = Pv + r * BN + ch * 8;
-    const v4f lo = *reinterpret_cast<const v4f*>(q), hi = *reinterpret_cast<const v4f*>(q + 4);
-    x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3]; x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
-    for (int s = 1; s < slices; ++s) {
-      const float* qs = q + (size_t)s * BM * BN;
-      const v4f l2 = *reinterpret_cast<const v4f*>(qs), h2 = *reinterpret_cast<const v4f*>(qs + 4);
-      x[0] += l2[0]; x[1] += l2[1]; x[2] += l2[2]; x[3] += l2[3];
-      x[4] += h2[0]; x[5] += h2[1]; x[6] += h2[2]; x[7] += h2[3];
+  logical_tile(full + v, tiles_m, tiles_n, GM, bm, bn);
+  const int r = 16 * c + threadIdx.x / 16, ch = threadIdx.x % 16;
+  const int m = bm * BM + r;
+  if (m >= M) return;
+  const float* q = P + (size_t)v * slices * BM * BN + r * BN + ch * 8;
+  v4f lo = *reinterpret_cast<const v4f*>(q), hi = *reinterpret_cast<const v4f*>(q + 4);
+  for (int s0 = 1; s0 < slices; s0 += 8) {
+    v4f xl[8], xh[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* qs = q + (size_t)min(s0 + u, slices - 1) * BM * BN;
+      xl[u] = *reinterpret_cast<const v4f*>(qs);
+      xh[u] = *reinterpret_cast<const v4f*>(qs + 4);
     }
-    const uint2 p0 = pack4_bf16(x[0], x[1], x[2], x[3]), p1 = pack4_bf16(x[4], x[5], x[6], x[7]);
-    const u32x4 v = {p0.x, p0.y, p1.x, p1.y};
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)m * N + bn * BN + ch * 8));
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < slices) {
+        lo += xl[u];
+        hi += xh[u];
+      }
   }
+  const uint2 p0 = pack4_bf16(lo[0], lo[1], lo[2], lo[3]), p1 = pack4_bf16(hi[0], hi[1], hi[2], hi[3]);
+  const u32x4 o = {p0.x, p0.y, p1.x, p1.y};
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(C + (size_t)m * N + bn * BN + ch * 8));
 }
 
 // ---------------------------------------------------------------------- k_gemm_qk
@@ -635,7 +641,7 @@ hipError_t run_qr(const void* ap, const void* wp, void* c, float* P, int M, int 
                      M, N, K, GM, tail, slices);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tail == 0) return e;
-  hipLaunchKernelGGL((k_qr_tail_reduce<S::BM, S::BN>), dim3((unsigned)tail), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_qr_tail_reduce<S::BM, S::BN>), dim3((unsigned)(tail * (S::BM / 16))), dim3(256), 0, st,
                      static_cast<const float*>(P), static_cast<uint16_t*>(c), M, N, GM, (int)(tiles - tail), slices);
   return hipGetLastError();
 }

@@ -307,13 +307,23 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restr
   });
 }
 
-// C = bf16(sum over slices s = 0..S-1, in order, of P[s]); four elements per thread.
+// C = bf16(sum over slices s = 0..S-1, in order, of P[s]); four elements per thread. The
+// slices are loaded eight at a time, all eight loads in flight before the first add (a
+// load-add loop waits out one memory latency per slice); slices past S re-load the last one
+// and are not added.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ P,
                                                        uint16_t* __restrict__ C, int64_t MN, int S) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= MN) return;
   v4f acc = *reinterpret_cast<const v4f*>(P + i);
-  for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const v4f*>(P + (size_t)s * MN + i);
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    v4f x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const v4f*>(P + (size_t)min(s0 + u, S - 1) * MN + i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) acc += x[u];
+  }
   *reinterpret_cast<uint2*>(C + i) = pack4_bf16(acc[0], acc[1], acc[2], acc[3]);
 }
 
