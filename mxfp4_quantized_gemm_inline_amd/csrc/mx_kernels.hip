@@ -102,6 +102,10 @@ __global__ __launch_bounds__(256) void k_unprepare(const uint8_t* __restrict__ W
 // then their scales [R][4 TS], R = the rows a launch stages (at most 16 MT; reads of rows
 // past the valid count are clamped to the last one); reused for the cross-wave reduction.
 constexpr int kSkinnyPD = 16;
+// The dense streaming kernel affords twice the weight operands in flight (it holds no
+// resident weight chunk): at 8448 x 7168 a wave's seven steps of four column groups then go
+// out at once (M = 8: 12.6 -> 11.6 us, M = 16: 15.0 -> 13.6 us).
+constexpr int kStreamPD = 32;
 
 // Rows of a dense row-major A.
 struct DenseRows {
@@ -1304,10 +1308,11 @@ struct GemmConfig {
   X(1, 4, 4, 1, 2, 1) X(1, 4, 4, 1, 2, 2)
 
 // Weight prefetch depth: enough registers for a wave's whole K share when it fits (4, 8 or
-// 16 steps of NG operands, at most kSkinnyPD operands), so no registers go to duplicate
-// loads. This is the PD the streaming and grouped launchers instantiate.
-int pick_pd(int NG, int steps_per_wave) {
-  const int cap = kSkinnyPD / NG;
+// 16 steps of NG operands, at most `ops` operands: kSkinnyPD for the grouped kernels,
+// kStreamPD for the dense streaming one), so no registers go to duplicate loads. This is
+// the PD the streaming and grouped launchers instantiate.
+int pick_pd(int NG, int steps_per_wave, int ops = kSkinnyPD) {
+  const int cap = std::min(16, ops / NG);
   int pd = 4;
   while (pd < steps_per_wave && pd < cap) pd *= 2;
   return pd > cap ? cap : pd;
@@ -1335,9 +1340,9 @@ hipError_t launch_stream(const void* a, const void* wp, void* c, float* P, int M
 template <int MT, int NG, int WK, int QB>
 hipError_t launch_stream_pd(int pd, const void* a, const void* wp, void* c, float* P, int M, int N, int K,
                             int S, int TS, size_t lds, hipStream_t st) {
-  if constexpr (kSkinnyPD / NG >= 16)
+  if constexpr (kStreamPD / NG >= 16)
     if (pd >= 16) return launch_stream<MT, NG, WK, 16, QB>(a, wp, c, P, M, N, K, S, TS, lds, st);
-  if constexpr (kSkinnyPD / NG >= 8)
+  if constexpr (kStreamPD / NG >= 8)
     if (pd >= 8) return launch_stream<MT, NG, WK, 8, QB>(a, wp, c, P, M, N, K, S, TS, lds, st);
   return launch_stream<MT, NG, WK, 4, QB>(a, wp, c, P, M, N, K, S, TS, lds, st);
 }
@@ -1350,7 +1355,7 @@ hipError_t run_stream(const void* a, const void* wp, void* c, float* P, int M, i
   const size_t lds = stream_lds_bytes(min(M, 16 * MT), TS, MT, NG, WK);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   const int per = (TS + WK - 1) / WK;
-  const int pd = pick_pd(NG, per);
+  const int pd = pick_pd(NG, per, kStreamPD);
   hipError_t e = stream_qb(M, per) == 1 ? launch_stream_pd<MT, NG, WK, 1>(pd, a, wp, c, P, M, N, K, S, TS, lds, st)
                                         : launch_stream_pd<MT, NG, WK, 4>(pd, a, wp, c, P, M, N, K, S, TS, lds, st);
   if (e != hipSuccess || S == 1) return e;
@@ -1717,7 +1722,7 @@ bool gemm_plan(int64_t M64, int64_t N64, int64_t K64, size_t ws_bytes, char* buf
                   c.GM, split);
   } else {
     const int T = steps_of(K), TS = (T + c.S - 1) / c.S, per = (TS + c.WK - 1) / c.WK;
-    std::snprintf(buf, len, "k_gemm_stream<%d, %d, %d, %d, %d> S=%d%s", c.MT, c.NG, c.WK, pick_pd(c.NG, per),
+    std::snprintf(buf, len, "k_gemm_stream<%d, %d, %d, %d, %d> S=%d%s", c.MT, c.NG, c.WK, pick_pd(c.NG, per, kStreamPD),
                   stream_qb(M, per), c.S, c.S > 1 ? " + k_splitk_reduce" : "");
   }
   return true;
