@@ -68,3 +68,31 @@ def test_noalloc_rejects_plans_beyond_the_scratch():
         mx.mx_a4w4_gemm_noalloc(a, wp, N, out=out)
     torch.cuda.synchronize()
     assert bool((out == 3.0).all()), "nothing is launched when the plan does not fit"
+
+
+def test_noalloc_register_direct_plans():
+    """The register-direct plans through the scratch array: 2048 x 8448 at K = 2048 (1056 tiles
+    of 128 x 128, the 32 past one round in K slices whose FP32 partials follow the activations
+    in the array), then 2048 x 1536 at K = 7168 (the four-wave kernel) over the same bytes;
+    bit for bit against mx_a4w4_gemm with its own workspace, and against the oracle."""
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    for M, N, K, kern in ((2048, 8448, 2048, "k_gemm_qr"), (2048, 1536, 7168, "k_gemm_qk")):
+        need = mx.mx_a4w4_gemm_workspace_bytes(M, N, K)
+        assert 0 < need <= mx.mx_noalloc_scratch_bytes()
+        plan = mx.mx_a4w4_gemm_plan(M, N, K, need)
+        assert kern in plan and (kern != "k_gemm_qr" or "tail=" in plan), plan
+        w = W.dense_weight(N, K, seed=63)
+        a = W.dense_activation(M, K, "outlier_channels", seed=64)
+        wp = mx.mx_prepare_weight(dev_bf16(w))
+        da = dev_bf16(a)
+        ref = mx.mx_a4w4_gemm(da, wp, N)
+        out = torch.full((M + 2, N), -5.0, dtype=torch.bfloat16, device="cuda")
+        mx.mx_a4w4_gemm_noalloc(da, wp, N, out=out[:M])
+        torch.cuda.synchronize()
+        got = host_bits(out[:M])
+        assert np.array_equal(got, host_bits(ref)), f"M={M} N={N} K={K} ({plan}): differs"
+        assert bool((out[M:] == -5.0).all()), f"M={M} N={N} K={K}: rows past M were written"
+        qa, sa = O.quantize_mx(a)
+        qw, sw = O.quantize_mx(w)
+        check_gemm(got, O.gemm_from_mx(qa, sa, qw, sw), what=f"noalloc M={M} N={N} K={K}")
