@@ -200,14 +200,24 @@ __device__ __forceinline__ v4f mfma_fp4_sel(const u32x4& a, const u32x4& b, v4f 
 // accumulators through copies every step. The compiler still places the s_waitcnt for the
 // operands (it sees the assembly read them); what it cannot see is the MFMA's own result
 // latency, so a VALU read of an accumulator after the last MFMA needs mfma_drain() first.
-template <int SA, int SB>
+// VACC = true keeps the accumulator in VGPRs instead ("+v"), for tiles with more accumulators
+// than the AGPRs hold.
+template <int SA, int SB, bool VACC = false>
 __device__ __forceinline__ void mfma_fp4_tied(v4f& acc, const u32x4& a, const u32x4& b, uint32_t sa, uint32_t sb) {
   // scale byte select: A byte = op_sel[0] | 2 op_sel_hi[0], B byte = op_sel[1] | 2 op_sel_hi[1]
-#define MXQ(A0, A1, B0, B1)                                                                                  \
-  asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #A0 "," #B0 ",0] op_sel_hi:[" #A1 \
-      "," #B1 ",0] cbsz:4 blgp:4"                                                                           \
-      : "+a"(acc)                                                                                         \
-      : "v"(a), "v"(b), "v"(sa), "v"(sb))
+#define MXQ(A0, A1, B0, B1)                                                                                    \
+  do {                                                                                                        \
+    if constexpr (VACC)                                                                                       \
+      asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #A0 "," #B0 ",0] op_sel_hi:[" #A1 \
+          "," #B1 ",0] cbsz:4 blgp:4"                                                                         \
+          : "+v"(acc)                                                                                       \
+          : "v"(a), "v"(b), "v"(sa), "v"(sb));                                                              \
+    else                                                                                                      \
+      asm("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #A0 "," #B0 ",0] op_sel_hi:[" #A1 \
+          "," #B1 ",0] cbsz:4 blgp:4"                                                                         \
+          : "+a"(acc)                                                                                       \
+          : "v"(a), "v"(b), "v"(sa), "v"(sb));                                                              \
+  } while (0)
   if constexpr (SA == 0 && SB == 0) MXQ(0, 0, 0, 0);
   else if constexpr (SA == 0 && SB == 1) MXQ(0, 0, 1, 0);
   else if constexpr (SA == 0 && SB == 2) MXQ(0, 0, 0, 1);

@@ -257,74 +257,70 @@ void k_gemm_qo(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
 
 // ---------------------------------------------------------------------- k_gemm_qr
 //
-// The register-direct form: one wave per SIMD owns a 16 MT x 16 NG output tile (128 x 128)
-// and streams both prepared operands straight from global memory into its registers, D steps
-// ahead, with no LDS and no barrier in the K loop, so no wave ever waits for another. Its
-// MT x NG = 64 accumulators fill the 256 AGPRs (mfma_fp4_tied). Every step's loads are
+// The register-direct form: one wave per SIMD owns a 16 MT x 16 NG output tile and streams
+// both prepared operands straight from global memory into its registers, D steps ahead,
+// with no LDS and no barrier in the K loop, so no wave ever waits for another. Its
+// accumulators are tied in place (mfma_fp4_tied): the first 64 (a 128 x 128 tile) fill the
+// 256 AGPRs, further accumulator rows (NG > 64 / MT) live in VGPRs. Every step's loads are
 // fenced as a group ahead of its MFMAs so that D steps stay in flight.
 //
-// The chip holds one such wave per SIMD (1024). When the tiles exceed that by a little
-// (8448 x 2048: 1056 tiles) the last `tail` logical tiles would run as a second, nearly
-// empty round; instead each is cut into `slices` K ranges run by CTAs of their own, which
-// write FP32 partial tiles, and k_qr_tail_reduce adds them in slice order. The other tiles
-// sum their K steps in order 0..T-1, as every inline kernel does.
+// NG need not be a multiple of four: then a tile's first weight column group g0 = NG bn can
+// sit at any byte of a scale word, and each step's weight scale words are realigned by
+// g0 % 4 bytes (one v_alignbyte per word) so that group j's scale is byte j % 4 of word j / 4
+// for the compile-time op_sel. The last column tile may reach past N: its loads are clamped
+// to the last column group and its columns >= N never stored. Tile widths that are not a
+// power of two let the tile count fit the chip (8448 x 2048 in 128 x 144 tiles: 944 waves,
+// one round, where 128 x 128 tiles number 1056).
+//
+// When the tiles exceed one wave per SIMD (1024) by a little the last `tail` logical tiles
+// would run as a second, nearly empty round; instead each is cut into `slices` K ranges run
+// by CTAs of their own, which write FP32 partial tiles, and k_qr_tail_reduce adds them in
+// slice order. The other tiles sum their K steps in order 0..T-1, as every inline kernel
+// does.
 
 template <int MT, int NG>
-struct QRShape {
+struct RDWave {
   static constexpr int BM = 16 * MT, BN = 16 * NG;
-  static constexpr int CROW = BN * 2 + 16;  // bf16 staging row, padded by 16 bytes
-  static constexpr int SMEM = BM * CROW;
-  static_assert(MT % 4 == 0 && NG % 4 == 0, "a wave's tiles cover whole scale words");
+  static constexpr int MQ = MT / 4;                               // activation scale words
+  static constexpr bool WAL = NG % 4 == 0;                         // g0 % 4 == 0 for every tile
+  static constexpr int NQL = WAL ? NG / 4 : (NG + 2) / 4 + 1;      // weight scale words loaded
+  static constexpr int NQ = (NG + 3) / 4;                          // ... after realignment
+  static constexpr int JA = 64 / MT;                               // accumulator rows in the AGPRs
+  static_assert(MT % 4 == 0 && MT <= 16 && NG >= 1, "whole activation scale words");
 };
 
-// Ap: activations in the prepared layout for Mp = round_up(M, 64) rows; Wp: the prepared
-// weight [N, K] (N % 16 NG == 0); C: bf16 [M, N]. CTAs 0 .. full - 1 (full = tiles - tail)
-// own whole tiles, dealt in the XCD-aware order over the first `full` logical tiles; CTA
-// full + u (u < tail * slices) computes K slice u % slices of logical tile full + u / slices
-// into P[u] (BM x BN FP32, row-major). Rows >= M are computed from clamped operand blocks and
-// never stored.
+// One wave's K steps t0 .. t1 - 1 of output tile (bm, bn) into acc (zeroed here). Ap holds the
+// activations prepared for Mp = round_up(M, 64) rows, Wp the prepared weight [N, K].
 template <int MT, int NG, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
-               float* __restrict__ P, int M, int N, int K, int GM, int tail, int slices) {
-  using S_ = QRShape<MT, NG>;
+__device__ __forceinline__ void rd_steps(v4f (&acc)[NG][MT], const uint8_t* __restrict__ Ap,
+                                         const uint8_t* __restrict__ Wp, int M, int N, int K, int bm, int bn,
+                                         int t0, int t1, int lane) {
+  using R = RDWave<MT, NG>;
   constexpr int S = D + 1;  // register sets in the ring
-  constexpr int MQ = MT / 4, NQ = NG / 4;
-  extern __shared__ __align__(16) uint8_t smem[];
   const int T = steps_of(K);
   const int Mp = (M + 63) / 64 * 64;
-  const int GAall = Mp / 16;
-  const int tiles_m = (M + S_::BM - 1) / S_::BM, tiles_n = N / S_::BN;
-  const int full = tiles_m * tiles_n - tail;
-  int bm, bn, t0 = 0, t1 = T;
-  const bool part = (int)blockIdx.x >= full;
-  if (!part) {
-    tile_coords(blockIdx.x, full, tiles_m, tiles_n, GM, bm, bn);
-  } else {
-    const int u = blockIdx.x - full, TS = (T + slices - 1) / slices;
-    logical_tile(full + u / slices, tiles_m, tiles_n, GM, bm, bn);
-    t0 = min(T, (u % slices) * TS);
-    t1 = min(T, t0 + TS);
-  }
-  const int lane = threadIdx.x;
+  const int GAall = Mp / 16, GW = N / 16;
+  const int g0 = bn * NG;
+  const uint32_t vsh = (uint32_t)(g0 & 3);
   const uint8_t* pa[MT];
   const uint8_t* pw[NG];
-  const uint8_t* psa[MQ];
-  const uint8_t* psw[NQ];
+  const uint8_t* psa[R::MQ];
+  const uint8_t* psw[R::NQL];
 #pragma unroll
   for (int i = 0; i < MT; ++i) pa[i] = Ap + (size_t)min(bm * MT + i, GAall - 1) * T * 1024;
 #pragma unroll
-  for (int j = 0; j < NG; ++j) pw[j] = Wp + (size_t)(bn * NG + j) * T * 1024;
+  for (int j = 0; j < NG; ++j) pw[j] = Wp + (size_t)min(g0 + j, GW - 1) * T * 1024;
 #pragma unroll
-  for (int q = 0; q < MQ; ++q)
-    psa[q] = Ap + payload_bytes(Mp, K) + (size_t)min(bm * MQ + q, GAall / 4 - 1) * T * 256;
+  for (int q = 0; q < R::MQ; ++q)
+    psa[q] = Ap + payload_bytes(Mp, K) + (size_t)min(bm * R::MQ + q, GAall / 4 - 1) * T * 256;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) psw[q] = Wp + payload_bytes(N, K) + (size_t)(bn * NQ + q) * T * 256;
+  for (int q = 0; q < R::NQL; ++q)
+    psw[q] = Wp + payload_bytes(N, K) + (size_t)min((g0 >> 2) + q, GW / 4 - 1) * T * 256;
 
   // ring set s holds step t's operands for (t - t0) % S == s; steps past the last load the
   // last step again (never used)
   u32x4 a[S][MT], b[S][NG];
-  uint32_t sa[S][MQ], sb[S][NQ];
+  uint32_t sa[S][R::MQ], sb[S][R::NQL];
   const int tlast = max(t1 - 1, 0);
   auto load = [&](int t, auto s_c) {
     constexpr int s = decltype(s_c)::value;
@@ -335,22 +331,29 @@ void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
 #pragma unroll
     for (int j = 0; j < NG; ++j) b[s][j] = *reinterpret_cast<const u32x4*>(pw[j] + o);
 #pragma unroll
-    for (int q = 0; q < MQ; ++q) sa[s][q] = *reinterpret_cast<const uint32_t*>(psa[q] + os);
+    for (int q = 0; q < R::MQ; ++q) sa[s][q] = *reinterpret_cast<const uint32_t*>(psa[q] + os);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) sb[s][q] = *reinterpret_cast<const uint32_t*>(psw[q] + os);
+    for (int q = 0; q < R::NQL; ++q) sb[s][q] = *reinterpret_cast<const uint32_t*>(psw[q] + os);
   };
-  v4f acc[NG][MT];
 #pragma unroll
   for (int j = 0; j < NG; ++j)
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
   auto mfmas = [&](auto s_c) {
     constexpr int s = decltype(s_c)::value;
+    uint32_t sw[R::NQ];
+    static_for<R::NQ>([&](auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      if constexpr (R::WAL)
+        sw[q] = sb[s][q];
+      else  // bytes g0 % 4 + 4 q .. + 3 of the loaded words
+        sw[q] = __builtin_amdgcn_alignbyte(sb[s][q + 1 < R::NQL ? q + 1 : R::NQL - 1], sb[s][q], vsh);
+    });
     static_for<NG>([&](auto j_c) {
       constexpr int j = decltype(j_c)::value;
       static_for<MT>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
-        mfma_fp4_tied<j & 3, i & 3>(acc[j][i], b[s][j], a[s][i], sb[s][j >> 2], sa[s][i >> 2]);
+        mfma_fp4_tied<j & 3, i & 3, (j >= R::JA)>(acc[j][i], b[s][j], a[s][i], sw[j >> 2], sa[s][i >> 2]);
       });
     });
   };
@@ -371,6 +374,43 @@ void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
     if (t + decltype(s_c)::value < t1) mfmas(s_c);
   });
   mfma_drain();
+}
+
+template <int MT, int NG>
+struct QRShape {
+  static constexpr int BM = 16 * MT, BN = 16 * NG;
+  static constexpr int CROW = BN * 2 + 16;  // bf16 staging row, padded by 16 bytes
+  static constexpr int SMEM = BM * CROW;
+};
+
+// Ap: activations in the prepared layout for Mp = round_up(M, 64) rows; Wp: the prepared
+// weight [N, K] (N % 64 == 0); C: bf16 [M, N]. Tiles: ceil(M / BM) x ceil(N / BN). CTAs
+// 0 .. full - 1 (full = tiles - tail) own whole tiles, dealt in the XCD-aware order over the
+// first `full` logical tiles; CTA full + u (u < tail * slices) computes K slice u % slices of
+// logical tile full + u / slices into P[u] (BM x BN FP32, row-major). Rows >= M and columns
+// >= N are computed from clamped operand blocks and never stored.
+template <int MT, int NG, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
+               float* __restrict__ P, int M, int N, int K, int GM, int tail, int slices) {
+  using S_ = QRShape<MT, NG>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int T = steps_of(K);
+  const int tiles_m = (M + S_::BM - 1) / S_::BM, tiles_n = (N + S_::BN - 1) / S_::BN;
+  const int full = tiles_m * tiles_n - tail;
+  int bm, bn, t0 = 0, t1 = T;
+  const bool part = (int)blockIdx.x >= full;
+  if (!part) {
+    tile_coords(blockIdx.x, full, tiles_m, tiles_n, GM, bm, bn);
+  } else {
+    const int u = blockIdx.x - full, TS = (T + slices - 1) / slices;
+    logical_tile(full + u / slices, tiles_m, tiles_n, GM, bm, bn);
+    t0 = min(T, (u % slices) * TS);
+    t1 = min(T, t0 + TS);
+  }
+  const int lane = threadIdx.x;
+  v4f acc[NG][MT];
+  rd_steps<MT, NG, D>(acc, Ap, Wp, M, N, K, bm, bn, t0, t1, lane);
 
   if (part) {
     // FP32 partial tile, row-major: lane l holds rows 16 i + l % 16, columns 16 j + 4 (l / 16) + 0..3
@@ -396,31 +436,33 @@ void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
   __syncthreads();
   constexpr int CPR = S_::BN / 8;  // 16-byte chunks per tile row
   const int m0 = bm * S_::BM, n0 = bn * S_::BN;
+  static_assert(S_::BM * CPR % 64 == 0, "whole rounds of 64 chunks");
 #pragma unroll
   for (int k = 0; k < S_::BM * CPR / 64; ++k) {
     const int id = lane + 64 * k;
     const int r = id / CPR, ch = id % CPR;
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * S_::CROW + ch * 16);
-    if (m0 + r < M)
+    if (m0 + r < M && n0 + 8 * ch < N)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + (size_t)(m0 + r) * N + n0 + 8 * ch));
   }
 }
 
 // The tail tiles of k_gemm_qr: tile v (logical tile full + v) is the sum of P[v * slices + s]
-// over s = 0 .. slices - 1 in that order, written as bf16 (rows < M). CTA (v, c) of 256
-// threads takes rows 16 c .. 16 c + 15 of tile v, a thread 8 adjacent columns of one row; its
-// slices are loaded eight at a time, all in flight before the first add.
+// over s = 0 .. slices - 1 in that order, written as bf16 (rows < M, columns < N). CTA (v, c)
+// of 2 BN threads takes rows 16 c .. 16 c + 15 of tile v, a thread 8 adjacent columns of one
+// row; its slices are loaded eight at a time, all in flight before the first add.
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void k_qr_tail_reduce(const float* __restrict__ P, uint16_t* __restrict__ C, int M,
-                                                       int N, int GM, int full, int slices) {
-  static_assert(BN == 128 && BM % 16 == 0, "16 rows of 16 eight-column chunks per CTA");
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+__global__ __launch_bounds__(2 * BN) void k_qr_tail_reduce(const float* __restrict__ P, uint16_t* __restrict__ C,
+                                                           int M, int N, int GM, int full, int slices) {
+  static_assert(BN % 8 == 0 && BM % 16 == 0, "16 rows of BN / 8 eight-column chunks per CTA");
+  constexpr int CPR = BN / 8;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int v = blockIdx.x / (BM / 16), c = blockIdx.x % (BM / 16);
   int bm, bn;
   logical_tile(full + v, tiles_m, tiles_n, GM, bm, bn);
-  const int r = 16 * c + threadIdx.x / 16, ch = threadIdx.x % 16;
-  const int m = bm * BM + r;
-  if (m >= M) return;
+  const int r = 16 * c + threadIdx.x / CPR, ch = threadIdx.x % CPR;
+  const int m = bm * BM + r, n = bn * BN + ch * 8;
+  if (m >= M || n >= N) return;
   const float* q = P + (size_t)v * slices * BM * BN + r * BN + ch * 8;
   v4f lo = *reinterpret_cast<const v4f*>(q), hi = *reinterpret_cast<const v4f*>(q + 4);
   for (int s0 = 1; s0 < slices; s0 += 8) {
@@ -440,18 +482,18 @@ __global__ __launch_bounds__(256) void k_qr_tail_reduce(const float* __restrict_
   }
   const uint2 p0 = pack4_bf16(lo[0], lo[1], lo[2], lo[3]), p1 = pack4_bf16(hi[0], hi[1], hi[2], hi[3]);
   const u32x4 o = {p0.x, p0.y, p1.x, p1.y};
-  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(C + (size_t)m * N + bn * BN + ch * 8));
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(C + (size_t)m * N + n));
 }
 
 // ---------------------------------------------------------------------- k_gemm_qk
 //
-// The register-direct wave of k_gemm_qr, four to a CTA (one per SIMD) on the same 128 x 128
-// tile, each over its own quarter of the CTA's K range: for calls with too few tiles to give
-// every SIMD one (7168 x 4224 at M = 512: 224 tiles, one CTA per CU). The four partial tiles
-// are added through LDS in wave order, half a tile at a time (4 x 64 rows of FP32, rows
-// padded to 132 floats so the 16 rows a wave's float4 store covers fall in distinct banks),
-// and written once. With slices > 1 a CTA covers one of `slices` K ranges of its tile and
-// writes FP32 partials P[slice][M][N], which k_splitk_reduce adds in slice order.
+// The register-direct wave of k_gemm_qr, four to a CTA (one per SIMD) on the same
+// 16 MT x 16 NG tile, each over its own quarter of the CTA's K range: for calls with too few
+// tiles to give every SIMD one (1536 x 2048: 192 tiles of 128 x 128, one CTA per CU). The
+// four partial tiles are added through LDS in wave order, half a tile at a time (4 x 64 rows
+// of FP32, rows padded by 4 floats so the 16 rows a wave's float4 store covers fall in
+// distinct banks), and written once. With slices > 1 a CTA covers one of `slices` K ranges of
+// its tile and writes FP32 partials P[slice][M][N], which k_splitk_reduce adds in slice order.
 
 template <int MT, int NG>
 struct QKShape {
@@ -459,8 +501,8 @@ struct QKShape {
   static constexpr int HR = BM / 2;           // rows per reduction half
   static constexpr int PROW = BN + 4;         // padded FP32 row
   static constexpr int SMEM = 4 * HR * PROW * 4;
-  static_assert(MT % 4 == 0 && NG % 4 == 0 && MT % 2 == 0, "whole scale words, two halves");
   static_assert(HR == 64 && BN % 8 == 0, "a wave sums 16 rows of each half, 8 columns a chunk");
+  static_assert(SMEM <= 160 * 1024, "the four partial half tiles fit the LDS");
 };
 
 template <int MT, int NG, int D>
@@ -468,13 +510,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_qk(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, uint16_t* __restrict__ C,
                float* __restrict__ P, int M, int N, int K, int GM, int slices) {
   using S_ = QKShape<MT, NG>;
-  constexpr int S = D + 1;  // register sets in the ring
-  constexpr int MQ = MT / 4, NQ = NG / 4;
   extern __shared__ __align__(16) uint8_t smem[];
   const int T = steps_of(K);
-  const int Mp = (M + 63) / 64 * 64;
-  const int GAall = Mp / 16;
-  const int tiles_m = (M + S_::BM - 1) / S_::BM, tiles_n = N / S_::BN;
+  const int tiles_m = (M + S_::BM - 1) / S_::BM, tiles_n = (N + S_::BN - 1) / S_::BN;
   // units = (tile, slice), a tile's slices consecutive; units dealt to the XCDs as tiles are
   const int units = tiles_m * tiles_n * slices;
   const int q8 = units / 8, r8 = units % 8, x8 = blockIdx.x % 8;
@@ -487,68 +525,8 @@ void k_gemm_qk(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
   const int k0 = min(T, slice * TSl), k1 = min(T, k0 + TSl);
   const int TW = (k1 - k0 + 3) / 4;
   const int t0 = min(k1, k0 + w * TW), t1 = min(k1, t0 + TW);
-
-  const uint8_t* pa[MT];
-  const uint8_t* pw[NG];
-  const uint8_t* psa[MQ];
-  const uint8_t* psw[NQ];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) pa[i] = Ap + (size_t)min(bm * MT + i, GAall - 1) * T * 1024;
-#pragma unroll
-  for (int j = 0; j < NG; ++j) pw[j] = Wp + (size_t)(bn * NG + j) * T * 1024;
-#pragma unroll
-  for (int q = 0; q < MQ; ++q)
-    psa[q] = Ap + payload_bytes(Mp, K) + (size_t)min(bm * MQ + q, GAall / 4 - 1) * T * 256;
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) psw[q] = Wp + payload_bytes(N, K) + (size_t)(bn * NQ + q) * T * 256;
-
-  u32x4 a[S][MT], b[S][NG];
-  uint32_t sa[S][MQ], sb[S][NQ];
-  const int tlast = max(t1 - 1, 0);
-  auto load = [&](int t, auto s_c) {
-    constexpr int s = decltype(s_c)::value;
-    const uint32_t tt = (uint32_t)min(t, tlast);
-    const uint32_t o = tt * 1024 + lane * 16, os = tt * 256 + lane * 4;
-#pragma unroll
-    for (int i = 0; i < MT; ++i) a[s][i] = *reinterpret_cast<const u32x4*>(pa[i] + o);
-#pragma unroll
-    for (int j = 0; j < NG; ++j) b[s][j] = *reinterpret_cast<const u32x4*>(pw[j] + o);
-#pragma unroll
-    for (int q = 0; q < MQ; ++q) sa[s][q] = *reinterpret_cast<const uint32_t*>(psa[q] + os);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) sb[s][q] = *reinterpret_cast<const uint32_t*>(psw[q] + os);
-  };
   v4f acc[NG][MT];
-#pragma unroll
-  for (int j = 0; j < NG; ++j)
-#pragma unroll
-    for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto mfmas = [&](auto s_c) {
-    constexpr int s = decltype(s_c)::value;
-    static_for<NG>([&](auto j_c) {
-      constexpr int j = decltype(j_c)::value;
-      static_for<MT>([&](auto i_c) {
-        constexpr int i = decltype(i_c)::value;
-        mfma_fp4_tied<j & 3, i & 3>(acc[j][i], b[s][j], a[s][i], sb[s][j >> 2], sa[s][i >> 2]);
-      });
-    });
-  };
-
-  static_for<D>([&](auto s_c) { load(t0 + decltype(s_c)::value, s_c); });
-  int t = t0;
-  for (; t + S <= t1; t += S) {
-    static_for<S>([&](auto s_c) {
-      constexpr int s = decltype(s_c)::value;
-      __builtin_amdgcn_sched_barrier(0);
-      load(t + s + D, std::integral_constant<int, (s + D) % S>{});
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(s_c);
-    });
-  }
-  static_for<S - 1>([&](auto s_c) {
-    if (t + decltype(s_c)::value < t1) mfmas(s_c);
-  });
-  mfma_drain();
+  rd_steps<MT, NG, D>(acc, Ap, Wp, M, N, K, bm, bn, t0, t1, lane);
 
   float* red = reinterpret_cast<float*>(smem);  // [4 waves][64 rows][PROW]
   const int m0 = bm * S_::BM, n0 = bn * S_::BN;
@@ -566,8 +544,9 @@ void k_gemm_qk(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
     // wave w adds rows 16 w .. 16 w + 15 of this half over the four waves, 8 columns a chunk
     constexpr int CPR = S_::BN / 8;
 #pragma unroll
-    for (int c = 0; c < 16 * CPR / 64; ++c) {
+    for (int c = 0; c < (16 * CPR + 63) / 64; ++c) {
       const int id = lane + 64 * c;
+      if (16 * CPR % 64 != 0 && id >= 16 * CPR) break;
       const int r = 16 * w + id / CPR, ch = id % CPR;
       const float* q = red + r * S_::PROW + 8 * ch;
       v4f lo = *reinterpret_cast<const v4f*>(q), hi = *reinterpret_cast<const v4f*>(q + 4);
@@ -577,7 +556,7 @@ void k_gemm_qk(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
         hi += *reinterpret_cast<const v4f*>(q + ww * S_::HR * S_::PROW + 4);
       }
       const int m = m0 + h * S_::HR + r, n = n0 + 8 * ch;
-      if (m < M) {
+      if (m < M && n < N) {
         if (slices > 1) {
           float* dst = P + ((size_t)slice * M + m) * N + n;
           *reinterpret_cast<v4f*>(dst) = lo;
@@ -627,38 +606,42 @@ hipError_t run_qo(int id, const void* ap, const void* wp, void* c, int M, int N,
   return hipGetLastError();
 }
 
-// Register-direct configurations (MT, NG, D).
-#define MX_QR_CONFIGS(X) X(8, 8, 2)
+// Register-direct configurations (MT, NG, D): 128 x 128 tiles two steps ahead; 128 x 144
+// (72 accumulators, the ninth row of 16 columns in VGPRs) one step ahead, since two steps of
+// its operands leave too few registers for the rest. Measured at 8448 x 7168 M=2048: 128 x 144
+// two steps ahead 77.6 against 75.3 us one step ahead; 128 x 160 (80 accumulators) 114.9 us.
+#define MX_QR_CONFIGS(X) X(8, 8, 2) X(8, 9, 1)
 
 template <int MT, int NG, int D>
 hipError_t run_qr(const void* ap, const void* wp, void* c, float* P, int M, int N, int K, int GM, int tail,
                   int slices, hipStream_t st) {
   using S = QRShape<MT, NG>;
-  const int64_t tiles = (int64_t)((M + S::BM - 1) / S::BM) * (N / S::BN);
+  const int64_t tiles = (int64_t)((M + S::BM - 1) / S::BM) * ((N + S::BN - 1) / S::BN);
   const int64_t grid = tiles - tail + (int64_t)tail * slices;
   hipLaunchKernelGGL((k_gemm_qr<MT, NG, D>), dim3((unsigned)grid), dim3(64), S::SMEM, st,
                      static_cast<const uint8_t*>(ap), static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), P,
                      M, N, K, GM, tail, slices);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tail == 0) return e;
-  hipLaunchKernelGGL((k_qr_tail_reduce<S::BM, S::BN>), dim3((unsigned)(tail * (S::BM / 16))), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_qr_tail_reduce<S::BM, S::BN>), dim3((unsigned)(tail * (S::BM / 16))), dim3(2 * S::BN), 0, st,
                      static_cast<const float*>(P), static_cast<uint16_t*>(c), M, N, GM, (int)(tiles - tail), slices);
   return hipGetLastError();
 }
 
-// Four-wave configurations (MT, NG, D).
-#define MX_QK_CONFIGS(X) X(8, 8, 2)
+// Four-wave configurations (MT, NG, D): tiles 128 x 96 .. 128 x 144 (the widest holds its four
+// partial half tiles in 148 KiB of LDS).
+#define MX_QK_CONFIGS(X) X(8, 8, 2) X(8, 9, 1) X(8, 7, 2) X(8, 6, 2)
 
-std::atomic<uint64_t> g_qk_lds[1];
+std::atomic<uint64_t> g_qk_lds[8];
 
 template <int MT, int NG, int D>
-hipError_t run_qk(const void* ap, const void* wp, void* c, float* P, int M, int N, int K, int GM, int slices,
+hipError_t run_qk(int id, const void* ap, const void* wp, void* c, float* P, int M, int N, int K, int GM, int slices,
                   hipStream_t st) {
   using S = QKShape<MT, NG>;
   auto kern = k_gemm_qk<MT, NG, D>;
-  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), S::SMEM, g_qk_lds[0]);
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), S::SMEM, g_qk_lds[id]);
   if (e != hipSuccess) return e;
-  const int64_t grid = (int64_t)((M + S::BM - 1) / S::BM) * (N / S::BN) * slices;
+  const int64_t grid = (int64_t)((M + S::BM - 1) / S::BM) * ((N + S::BN - 1) / S::BN) * slices;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), S::SMEM, st, static_cast<const uint8_t*>(ap),
                      static_cast<const uint8_t*>(wp), static_cast<uint16_t*>(c), P, M, N, K, GM, slices);
   e = hipGetLastError();
@@ -684,14 +667,17 @@ size_t qk_workspace_bytes(int64_t M, int64_t N, int64_t K, int slices) {
 
 hipError_t launch_gemm_qk(int MT, int NG, int D, int slices, const void* a, const void* wp, void* c, int64_t M,
                           int64_t N, int64_t K, int GM, void* ws, hipStream_t st) {
-  if (!qk_supported(MT, NG, D) || N % (16 * NG) != 0 || slices < 1 || 4 * slices > steps_of((int)K))
+  if (!qk_supported(MT, NG, D) || N % 64 != 0 || slices < 1 || 4 * slices > steps_of((int)K))
     return hipErrorInvalidValue;
   const int64_t Mp = (M + 63) / 64 * 64;
   float* P = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (qo_act_bytes(M, K) + 255) / 256 * 256);
   hipError_t e = launch_prepare_rows(a, M, Mp, K, ws, st);
   if (e != hipSuccess) return e;
-#define X(mt, ng, d) \
-  if (MT == mt && NG == ng && D == d) return run_qk<mt, ng, d>(ws, wp, c, P, (int)M, (int)N, (int)K, GM, slices, st);
+  int id = 0;
+#define X(mt, ng, d)                                                                                   \
+  if (MT == mt && NG == ng && D == d)                                                                  \
+    return run_qk<mt, ng, d>(id, ws, wp, c, P, (int)M, (int)N, (int)K, GM, slices, st);               \
+  ++id;
   MX_QK_CONFIGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -707,7 +693,7 @@ bool qr_supported(int MT, int NG, int D) {
 // Tail tiles split into K slices: the tiles beyond one wave per SIMD of the chip (256 CUs x
 // 4), when they are at most a quarter round; none otherwise.
 int qr_tail_tiles(int64_t M, int64_t N, int MT, int NG) {
-  const int64_t tiles = (M + 16 * MT - 1) / (16 * MT) * (N / (16 * NG));
+  const int64_t tiles = (M + 16 * MT - 1) / (16 * MT) * ((N + 16 * NG - 1) / (16 * NG));
   constexpr int64_t kSlots = 256 * 4;
   return tiles > kSlots && tiles <= kSlots + kSlots / 4 ? (int)(tiles - kSlots) : 0;
 }
@@ -719,7 +705,7 @@ size_t qr_workspace_bytes(int64_t M, int64_t N, int64_t K, int MT, int NG, int s
 
 hipError_t launch_gemm_qr(int MT, int NG, int D, int slices, const void* a, const void* wp, void* c, int64_t M,
                           int64_t N, int64_t K, int GM, void* ws, hipStream_t st) {
-  if (!qr_supported(MT, NG, D) || N % (16 * NG) != 0 || slices < 1) return hipErrorInvalidValue;
+  if (!qr_supported(MT, NG, D) || N % 64 != 0 || slices < 1) return hipErrorInvalidValue;
   const int64_t Mp = (M + 63) / 64 * 64;
   const int tail = slices > 1 ? qr_tail_tiles(M, N, MT, NG) : 0;
   float* P = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (qo_act_bytes(M, K) + 255) / 256 * 256);

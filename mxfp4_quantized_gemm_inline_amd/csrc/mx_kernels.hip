@@ -1524,18 +1524,33 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   const int64_t t256 = ((int64_t)M + 255) / 256 * ((N + 255) / 256);
   const int64_t t128 = ((int64_t)M + 127) / 128 * ((N + 127) / 128);
   // Slightly more 128 x 128 tiles than one wave per SIMD of the chip (8448 x 7168 at M=2048:
-  // 1056): the register-direct kernel, the tiles past one round in four K slices (90 -> 86 us
-  // there; with the whole last round 96 us, and eight slices 93 us).
+  // 1056): the register-direct kernel. 128 x 144 tiles (72 accumulators) when they fit one
+  // round (there: 944 tiles, 80.0 -> 75.2 us); else 128 x 128 with the tiles past one round
+  // in four K slices (90 -> 86 us there; with the whole last round 96 us, eight slices 93 us).
+  const int64_t tm128 = ((int64_t)M + 127) / 128;
+  if (T >= 16 && t128 > 1024 && tm128 * ((N + 143) / 144) <= 1024 && qr_workspace_bytes(M, N, K, 8, 9, 1) <= ws_bytes) {
+    c.qo = true; c.qr = true; c.MT = 8; c.NG = 9; c.NBUF = 1; c.GM = 8; c.S = 1;
+    return c;
+  }
   if (T >= 16 && qr_tail_tiles(M, N, 8, 8) > 0 && qr_workspace_bytes(M, N, K, 8, 8, 4) <= ws_bytes) {
     c.qo = true; c.qr = true; c.MT = 8; c.NG = 8; c.NBUF = 2; c.GM = 8; c.S = 4;
     return c;
   }
   // Too few 128 x 128 tiles for one wave per SIMD but enough for one CTA per CU, at long K:
-  // four register-direct waves per tile splitting K (1536 x 7168 M=2048, 192 tiles: 32.2 ->
-  // 27.9 us; at K = 4224 with 224 tiles it only ties the LDS kernel).
-  if (M >= 512 && T >= 48 && t128 >= 150 && t128 <= 256 && qk_workspace_bytes(M, N, K, 1) <= ws_bytes) {
-    c.qo = true; c.qk = true; c.MT = 8; c.NG = 8; c.NBUF = 2; c.GM = 8; c.S = 1;
-    return c;
+  // four register-direct waves per tile splitting K, the tile width 16 NG (NG = 6 .. 9) the
+  // narrowest whose tiles fit one round of 256 CTAs, when that round holds at least 150.
+  // 1536 x 7168 M=2048: 256 tiles of 128 x 96, 28.3 -> 26.0 us (32.2 us on the LDS kernel);
+  // 8448 x 7168 M=512: 236 tiles of 128 x 144, 34.3 -> 28.7 us (128 x 128: 264 tiles, two
+  // rounds, 40.0 us). At K = 4224 (7168 x 4224 M=512, 256 tiles of 128 x 112) it only ties
+  // the LDS kernel.
+  if (M >= 512 && T >= 48 && qk_workspace_bytes(M, N, K, 1) <= ws_bytes) {
+    for (int ng = 6; ng <= 9; ++ng) {
+      const int64_t tiles = tm128 * ((N + 16 * ng - 1) / (16 * ng));
+      if (tiles > 256) continue;
+      if (tiles < 150) break;
+      c.qo = true; c.qk = true; c.MT = 8; c.NG = ng; c.NBUF = ng == 9 ? 1 : 2; c.GM = 4; c.S = 1;
+      return c;
+    }
   }
   if (M >= 512 && T >= 16 && t128 >= 150 && qo_act_bytes(M, K) <= ws_bytes) {
     c.qo = true; c.GM = 8; c.OCC = 2;
@@ -1665,8 +1680,8 @@ bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
   if (ov < 0) return false;
   if (ov > 0 && cfg.sweep && (!sweep_supported(steps_of(K), cfg.J) || N % 128 != 0)) return false;
   if (ov > 0 && cfg.qo && config_workspace(cfg, M, N, K) > ws_bytes) return false;
-  if (ov > 0 && cfg.qr && (N % (16 * cfg.NG) != 0 || cfg.S > steps_of(K))) return false;
-  if (ov > 0 && cfg.qk && (N % (16 * cfg.NG) != 0 || 4 * cfg.S > steps_of(K))) return false;
+  if (ov > 0 && cfg.qr && cfg.S > steps_of(K)) return false;
+  if (ov > 0 && cfg.qk && 4 * cfg.S > steps_of(K)) return false;
   if (ov > 0 && cfg.tile && !cfg.qo && cfg.S > 1) {
     const int T = steps_of(K);
     if (cfg.S > T) cfg.S = T;

@@ -127,21 +127,30 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     # then both prepared operands are multiplied (k_gemm_qo); without that workspace the
     # inline kernels run
     assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_prepare + k_gemm_qo<2, 4, 8, 4, 4, 2> GM=8"
-    # 1056 tiles of 128 x 128, a little over one wave per SIMD: the register-direct kernel, the
-    # 32 tiles past the first round in four K slices
-    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == \
-        "k_prepare + k_gemm_qr<8, 8, 2> GM=8 tail=32x4 + k_qr_tail_reduce"
-    assert mx.mx_a4w4_gemm_plan(512, 8448, 7168) == "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
+    # 1056 tiles of 128 x 128, a little over one wave per SIMD: the register-direct kernel on
+    # 944 tiles of 128 x 144; at 1188 tiles (M = 2304) 128 x 144 tiles still number 1062, so
+    # 128 x 128 tiles run with the 164 past the first round in four K slices
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_prepare + k_gemm_qr<8, 9, 1> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2304, 8448, 7168) == \
+        "k_prepare + k_gemm_qr<8, 8, 2> GM=8 tail=164x4 + k_qr_tail_reduce"
+    # one CTA of four register-direct waves per tile, the narrowest tile that fits one round
+    # of 256 CTAs: 236 of 128 x 144, 256 of 128 x 96
+    assert mx.mx_a4w4_gemm_plan(512, 8448, 7168) == "k_prepare + k_gemm_qk<8, 9, 1> GM=4"
+    assert mx.mx_a4w4_gemm_plan(2048, 1536, 7168) == "k_prepare + k_gemm_qk<8, 6, 2> GM=4"
     assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224, workspace_bytes=0) == "k_gemm_tile<1, 8, 8, 4, 1, 2> GM=8"
     assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=0) == "k_gemm_tile<1, 4, 4, 4, 1, 2> GM=8"
     # the quantize-once workspace: the activations of M rows padded to 64, in the prepared layout
     # (then, for the register-direct kernel, 256-byte aligned FP32 partials of its tail slices)
     act = 2048 * 7168 * 17 // 32
-    assert mx.mx_a4w4_gemm_workspace_bytes(2048, 8448, 7168) == (act + 255) // 256 * 256 + 32 * 4 * 128 * 128 * 4
+    assert mx.mx_a4w4_gemm_workspace_bytes(2048, 8448, 7168) == (act + 255) // 256 * 256
+    act_t = (2304 * 7168 * 17 // 32 + 255) // 256 * 256
+    assert mx.mx_a4w4_gemm_workspace_bytes(2304, 8448, 7168) == act_t + 164 * 4 * 128 * 128 * 4
     assert mx.mx_a4w4_gemm_workspace_bytes(520, 8448, 7168) == 576 * 7168 * 17 // 32
-    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act) == \
-        "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act) == "k_prepare + k_gemm_qr<8, 9, 1> GM=8"
     assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act - 1).startswith("k_gemm_tile<")
+    # no room for the tail partials: the LDS quantize-once kernel
+    assert mx.mx_a4w4_gemm_plan(2304, 8448, 7168, workspace_bytes=act_t) == \
+        "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
     # N = 1536 at M = 512 gives 48 tiles of 128 x 128: too few, K slices keep it inline
     assert "k_gemm_qo" not in mx.mx_a4w4_gemm_plan(512, 1536, 7168)
     # mid M: 64 x 64 tiles while the activation re-reads stay modest, K slices beyond
@@ -421,7 +430,10 @@ def test_register_direct_override_plans(monkeypatch):
     act = (2048 * 7168 * 17 // 32 + 255) // 256 * 256
     with pytest.raises(mx.MxError):  # no room for the partials
         mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act + 32 * 4 * 65536 - 1)
-    for bad in ("r,8,8,3,8", "r,4,8,2,8", "r,8,8,2,8,17"):
+    # 128 x 144 tiles, one step ahead: 7168 / 144 leaves a last column tile of 112 columns
+    monkeypatch.setenv("MX_GEMM_CONFIG", "r,8,9,1,4")
+    assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_prepare + k_gemm_qr<8, 9, 1> GM=4"
+    for bad in ("r,8,8,3,8", "r,4,8,2,8", "r,8,8,2,8,17", "r,8,9,2,8", "r,8,10,1,8"):
         monkeypatch.setenv("MX_GEMM_CONFIG", bad)
         with pytest.raises(mx.MxError):
             mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=big)
@@ -442,7 +454,11 @@ def test_four_wave_override_plans(monkeypatch):
     monkeypatch.setenv("MX_GEMM_CONFIG", "x,8,8,2,8,2")
     with pytest.raises(mx.MxError):  # 6 steps cannot give 2 x 4 waves a step each
         mx.mx_a4w4_gemm_plan(512, 7168, 768, workspace_bytes=1 << 30)
-    for bad in ("x,8,8,3,8", "x,4,4,2,8", "x,8,8,2,8,17"):
+    for cfg, plan in (("x,8,9,1,8", "k_gemm_qk<8, 9, 1> GM=8"), ("x,8,7,2,2", "k_gemm_qk<8, 7, 2> GM=2"),
+                      ("x,8,6,2,4", "k_gemm_qk<8, 6, 2> GM=4")):
+        monkeypatch.setenv("MX_GEMM_CONFIG", cfg)
+        assert mx.mx_a4w4_gemm_plan(512, 7168, 4224) == "k_prepare + " + plan
+    for bad in ("x,8,8,3,8", "x,4,4,2,8", "x,8,8,2,8,17", "x,8,9,2,8", "x,8,10,1,8"):
         monkeypatch.setenv("MX_GEMM_CONFIG", bad)
         with pytest.raises(mx.MxError):
             mx.mx_a4w4_gemm_plan(512, 7168, 4224, workspace_bytes=1 << 30)

@@ -27,8 +27,8 @@ TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8,
 # mirrors MX_QO_CONFIGS in mx_gemm_qo.hip: (WM, WN, MT, NG, NBUF, OCC)
 QO = [(2, 4, 8, 4, 4, 2), (2, 2, 4, 4, 4, 2), (2, 2, 4, 4, 5, 2), (1, 4, 8, 4, 3, 2)]
 # mirrors MX_QR_CONFIGS / MX_QK_CONFIGS in mx_gemm_qo.hip: (MT, NG, D)
-QR = [(8, 8, 2)]
-QK = [(8, 8, 2)]
+QR = [(8, 8, 2), (8, 9, 1)]
+QK = [(8, 8, 2), (8, 9, 1), (8, 7, 2), (8, 6, 2)]
 SWEEP_K = (256, 512, 768, 1024)  # the short-K sweep kernel's compiled step counts 2, 4, 6, 8
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
 K_TESTS = (4224, 768)  # 33 and 6 steps of 128
@@ -141,11 +141,13 @@ def test_quantize_once_config(cfg, K):
 @pytest.mark.parametrize("K", (128, 256, 512) + K_TESTS + (7168,))
 @pytest.mark.parametrize("cfg", QR, ids=[f"r{c}" for c in QR])
 def test_register_direct_config(cfg, K):
-    """The register-direct quantize-once kernel (one wave per 128 x 128 tile, operands two
-    steps ahead in registers) at every remainder of its three-step ring (T = 1, 2, 4, 6, 33,
-    56 steps), on a ragged last row tile, a tile of fewer rows than one 64-row quad, several
-    tile orders and canary rows past M; compared with the oracle and bit for bit with the
-    inline kernel (same per-element K order)."""
+    """The register-direct quantize-once kernel (one wave per 128 x 16 NG tile, operands D
+    steps ahead in registers) at every remainder of its ring of two or three steps (T = 1, 2,
+    4, 6, 33, 56 steps), on a ragged last row tile, a tile of fewer rows than one 64-row quad,
+    several tile orders and canary rows past M. At N = 768 the 128 x 144 tiles start at every
+    byte of a weight scale word (first groups 0, 9, 18, 27, ...) and the last one holds 48
+    columns. Compared with the oracle and bit for bit with the inline kernel (same
+    per-element K order)."""
     torch = torch_or_skip()
     mx = lib_or_fail()
     a, wp, exact = _case(K)
@@ -169,11 +171,13 @@ def test_register_direct_config(cfg, K):
 @pytest.mark.parametrize("K,slices", ((512, 1), (640, 1), (768, 1), (4224, 1), (4224, 2), (4224, 8), (7168, 3)))
 @pytest.mark.parametrize("cfg", QK, ids=[f"x{c}" for c in QK])
 def test_four_wave_config(cfg, K, slices):
-    """Four register-direct waves per 128 x 128 tile, each over a quarter of the CTA's K range
-    (T = 4, 5 (one wave with no step), 6, 33, 56 steps), added through LDS in wave order, with
-    and without K slices across CTAs (FP32 partials added by the split-K reduce); on a ragged
-    last row tile, a tile of fewer rows than one 64-row quad, several tile orders and canary
-    rows past M. Compared with the oracle (the sum order differs from the inline kernel's)."""
+    """Four register-direct waves per 128 x 16 NG tile, each over a quarter of the CTA's K
+    range (T = 4, 5 (one wave with no step), 6, 33, 56 steps), added through LDS in wave order,
+    with and without K slices across CTAs (FP32 partials added by the split-K reduce); on a
+    ragged last row tile, a tile of fewer rows than one 64-row quad, several tile orders and
+    canary rows past M. Tile widths 96, 112 and 144 start at every byte offset within a weight
+    scale word, and at N = 768 the last 112- and 144-wide tiles are partial. Compared with the
+    oracle (the sum order differs from the inline kernel's)."""
     torch = torch_or_skip()
     mx = lib_or_fail()
     a, wp, exact = _case(K)

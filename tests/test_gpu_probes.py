@@ -37,7 +37,11 @@ DENSE = [
     ("q,2,4,8,4,4,2,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
     ("q,2,2,4,4,4,2,8", 7168, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
     ("r,8,8,2,8", 7168, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
+    ("r,8,9,1,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
     ("x,8,8,2,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
+    ("x,8,9,1,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
+    ("x,8,7,2,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
+    ("x,8,6,2,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
     ("x,8,8,2,8,3", 7168, (37, 300),
      lambda M, K: ((M + 63) // 64 * 64 * K * 17 // 32 + 255) // 256 * 256 + 3 * M * N_P * 4),
 ]
