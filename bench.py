@@ -200,6 +200,28 @@ def calibrate_mfma_data(torch, mx, timer, ops, cus):
     return round(max(rates), 1)
 
 
+def calibrate_mfma_clock(torch, mx, ops, cus):
+    """The shader clock and the cycles per MFMA during the same loop, on the weight's own
+    operand bytes and on constant bytes (every E2M1 code 1.0): each wave's core-clock ticks
+    over its loop against the 100 MHz counter. It runs right after the rate calibration on
+    the same loop; of four launches per operand set the last one's waves are read, and the
+    median wave is reported."""
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(8 * cus, dtype=torch.int64, device="cuda")
+    const = torch.full((16384,), 0x22, dtype=torch.uint8, device="cuda")
+    iters, out = 4096, {}
+    for name, src in (("data", ops), ("constant", const)):
+        for _ in range(4):
+            mx.mx_calib_mfma_operands_clock(src, cus, iters, sink, clocks)
+        torch.cuda.synchronize()
+        c = clocks.view(-1, 2).double().cpu()
+        ghz = (c[:, 0] / (c[:, 1] / 100e6) / 1e9).median().item()
+        cyc = (c[:, 0] / (iters * 64)).median().item()
+        out[f"mfma_clock_GHz_{name}"] = round(ghz, 3)
+        out[f"mfma_cycles_per_op_{name}"] = round(cyc, 2)
+    return out
+
+
 def point_record(name, N, K, M, cold, us_warm, kernel=None):
     """cold: (median, min, max) us per launch over the replays."""
     us_cold = cold[0]
@@ -451,10 +473,14 @@ def main():
     torch.cuda.synchronize()
     log(f"headline {HEADLINE}: prepared weight {wp.numel()} B")
     calib["mfma_fp4_data_TFLOPs"] = calibrate_mfma_data(torch, mx, timer, wp[: N * K // 2], calib["cus"])
+    calib.update(calibrate_mfma_clock(torch, mx, wp[: N * K // 2], calib["cus"]))
     calib["mfma_data"] = ("16x16x128 block-scaled FP4 MFMA on the prepared %dx%d weight's own operand bytes, "
                           "one wave per SIMD, 64 accumulators per wave (the register tile of a 128 x 128 wave), "
                           "unit scales" % (N, K))
     log(f"calibration: {calib['mfma_fp4_data_TFLOPs']:.0f} TFLOP/s FP4 MFMA on the weight's own operands")
+    log(f"calibration: MFMA loop clock {calib['mfma_clock_GHz_data']:.2f} GHz on the weight's operands "
+        f"({calib['mfma_cycles_per_op_data']:.1f} cycles per MFMA), {calib['mfma_clock_GHz_constant']:.2f} GHz "
+        f"on constant operands ({calib['mfma_cycles_per_op_constant']:.1f})")
 
     # rotating sets for the whole step, one graph per set (each holds one step: a call per M)
     per_step = wp.numel() + sum(2 * m * K + 2 * m * N for m in ms)

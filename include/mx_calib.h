@@ -62,6 +62,18 @@ mx_status mx_calib_mfma_operands(const void* ops, size_t bytes, int64_t ctas, in
 /* Floating-point operations of one mx_calib_mfma_operands launch (64 MFMAs per wave and round). */
 double mx_calib_mfma_operands_flops(int64_t ctas, int64_t iters);
 
+/*
+ * mx_calib_mfma_operands that also reports the shader clock it ran at: lane 0 of wave w
+ * (w = 4 * CTA + wave in CTA) writes two uint64 values to `clocks` (device memory of
+ * 8 * ctas uint64, 8-byte aligned): clocks[2 w] = ticks of the core-clock counter
+ * (s_memtime) over its MFMA loop, clocks[2 w + 1] = ticks of the constant 100 MHz counter
+ * (s_memrealtime) over the same loop. Their ratio times 100 MHz is the wave's mean clock;
+ * the MFMA count over core-clock ticks gives the cycles each MFMA held the pipe. Arguments
+ * and errors otherwise as mx_calib_mfma_operands.
+ */
+mx_status mx_calib_mfma_operands_clock(const void* ops, size_t bytes, int64_t ctas, int64_t iters, void* sink,
+                                       void* clocks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

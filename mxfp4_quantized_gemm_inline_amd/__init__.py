@@ -47,6 +47,7 @@ SIGNATURES = {
     "mx_calib_mfma_flops": (ctypes.c_double, [_c_i64, _c_i64]),
     "mx_calib_mfma_operands": (_c_int, [_vp, _c_sz, _c_i64, _c_i64, _vp, _vp]),
     "mx_calib_mfma_operands_flops": (ctypes.c_double, [_c_i64, _c_i64]),
+    "mx_calib_mfma_operands_clock": (_c_int, [_vp, _c_sz, _c_i64, _c_i64, _vp, _vp, _vp]),
 }
 
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DEVICE, MX_ERR_WORKSPACE, MX_ERR_HIP = range(7)
@@ -453,6 +454,21 @@ def mx_calib_mfma_operands_flops(ctas: int, iters: int) -> float:
     return float(lib().mx_calib_mfma_operands_flops(int(ctas), int(iters)))
 
 
+def mx_calib_mfma_operands_clock(ops, ctas: int, iters: int, sink, clocks, stream=None) -> None:
+    """mx_calib_mfma_operands that writes each wave's core-clock and 100 MHz counter ticks over
+    its MFMA loop to `clocks` (an int64 device tensor of at least 8 * ctas elements)."""
+    _dev(ops, None, "ops")
+    _dev(sink, None, "sink")
+    _dev(clocks, None, "clocks")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    if clocks.numel() * clocks.element_size() < 64 * int(ctas):
+        raise ValueError("clocks must hold 8 * ctas uint64 values")
+    _check(lib().mx_calib_mfma_operands_clock(ops.data_ptr(), ops.numel() * ops.element_size(), int(ctas),
+                                              int(iters), sink.data_ptr(), clocks.data_ptr(), _stream_ptr(stream)),
+           "mx_calib_mfma_operands_clock")
+
+
 __all__ = [
     "LIB_PATH", "MxError", "lib", "status_string", "mx_prepared_layout_version",
     "mx_prepared_weight_bytes", "mx_a4w4_gemm_workspace_bytes", "mx_prepare_weight",
@@ -461,4 +477,5 @@ __all__ = [
     "mx_a4w4_gemm_grouped_act_quant_plan", "mx_a4w4_gemm_grouped_mx", "mx_a4w4_gemm_grouped_mx_plan",
     "mx_moe_combine", "mx_a16w4_gemm", "MX_ACT_SILU", "MX_ACT_SWIGLU", "mx_calib_read", "mx_calib_mfma",
     "mx_calib_mfma_flops", "mx_calib_mfma_operands", "mx_calib_mfma_operands_flops",
+    "mx_calib_mfma_operands_clock",
 ]

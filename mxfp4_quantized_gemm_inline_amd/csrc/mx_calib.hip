@@ -62,9 +62,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_calib_mfma(int iters, float* __
 // per side, in the prepared layout's lane order, and issues `iters` rounds of the 8 x 8 block
 // products a 128 x 128 wave tile of the register-direct GEMM issues per K step: 64
 // accumulators in the AGPRs, one wave per SIMD, unit scales.
+// With CLK, lane 0 of each wave also writes the core-clock counter (s_memtime) and the
+// constant 100 MHz counter (s_memrealtime) ticks over its MFMA loop to clocks[2 gw], [2 gw + 1].
 constexpr int kOpWindow = 16384;
+template <bool CLK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_calib_mfma_ops(const u32x4* __restrict__ ops, int64_t windows, int iters, float* __restrict__ sink) {
+void k_calib_mfma_ops(const u32x4* __restrict__ ops, int64_t windows, int iters, float* __restrict__ sink,
+                      uint64_t* __restrict__ clocks) {
   const uint32_t l = threadIdx.x & 63;
   const int64_t gw = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const u32x4* base = ops + (gw % windows) * (kOpWindow / 16);
@@ -79,6 +83,11 @@ void k_calib_mfma_ops(const u32x4* __restrict__ ops, int64_t windows, int iters,
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
   const uint32_t unit = 0x7F7F7F7Fu;
+  uint64_t c0 = 0, r0 = 0;
+  if constexpr (CLK) {
+    c0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -86,6 +95,13 @@ void k_calib_mfma_ops(const u32x4* __restrict__ ops, int64_t windows, int iters,
       for (int i = 0; i < 8; ++i) mx::mfma_fp4_tied<0, 0>(acc[j][i], b[j], a[i], unit, unit);
   }
   mx::mfma_drain();
+  if constexpr (CLK) {
+    const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (l == 0) {
+      clocks[2 * gw] = c1 - c0;
+      clocks[2 * gw + 1] = r1 - r0;
+    }
+  }
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -129,8 +145,24 @@ extern "C" mx_status mx_calib_mfma_operands(const void* ops, size_t bytes, int64
   if (reinterpret_cast<uintptr_t>(ops) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0) return MX_ERR_ALIGN;
   const mx_status d = mx::check_device();
   if (d != MX_OK) return d;
-  hipLaunchKernelGGL(k_calib_mfma_ops, dim3((unsigned)ctas), dim3(kThreads), 0, stream, static_cast<const u32x4*>(ops),
-                     (int64_t)(bytes / kOpWindow), (int)iters, static_cast<float*>(sink));
+  hipLaunchKernelGGL(k_calib_mfma_ops<false>, dim3((unsigned)ctas), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(ops), (int64_t)(bytes / kOpWindow), (int)iters, static_cast<float*>(sink),
+                     nullptr);
+  return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_HIP;
+}
+
+extern "C" mx_status mx_calib_mfma_operands_clock(const void* ops, size_t bytes, int64_t ctas, int64_t iters,
+                                                  void* sink, void* clocks, hipStream_t stream) {
+  if (!ops || !sink || !clocks) return MX_ERR_NULL;
+  if (bytes < (size_t)kOpWindow || ctas < 1 || ctas > kMaxCtas || iters < 1 || iters > kMaxIters) return MX_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(ops) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(clocks) % 8 != 0)
+    return MX_ERR_ALIGN;
+  const mx_status d = mx::check_device();
+  if (d != MX_OK) return d;
+  hipLaunchKernelGGL(k_calib_mfma_ops<true>, dim3((unsigned)ctas), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(ops), (int64_t)(bytes / kOpWindow), (int)iters, static_cast<float*>(sink),
+                     static_cast<uint64_t*>(clocks));
   return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_HIP;
 }
 

@@ -490,19 +490,20 @@ __global__ __launch_bounds__(2 * BN) void k_qr_tail_reduce(const float* __restri
 // The register-direct wave of k_gemm_qr, four to a CTA (one per SIMD) on the same
 // 16 MT x 16 NG tile, each over its own quarter of the CTA's K range: for calls with too few
 // tiles to give every SIMD one (1536 x 2048: 192 tiles of 128 x 128, one CTA per CU). The
-// four partial tiles are added through LDS in wave order, half a tile at a time (4 x 64 rows
-// of FP32, rows padded by 4 floats so the 16 rows a wave's float4 store covers fall in
-// distinct banks), and written once. With slices > 1 a CTA covers one of `slices` K ranges of
+// four partial tiles are added through LDS in wave order, 64 rows at a time (4 x 64 rows of
+// FP32, rows padded by 4 floats so the 16 rows a wave's float4 store covers fall in distinct
+// banks), and written once. With slices > 1 a CTA covers one of `slices` K ranges of
 // its tile and writes FP32 partials P[slice][M][N], which k_splitk_reduce adds in slice order.
 
 template <int MT, int NG>
 struct QKShape {
   static constexpr int BM = 16 * MT, BN = 16 * NG;
-  static constexpr int HR = BM / 2;           // rows per reduction half
+  static constexpr int HR = 64;               // rows per reduction pass
+  static constexpr int NP = BM / HR;          // passes
   static constexpr int PROW = BN + 4;         // padded FP32 row
   static constexpr int SMEM = 4 * HR * PROW * 4;
-  static_assert(HR == 64 && BN % 8 == 0, "a wave sums 16 rows of each half, 8 columns a chunk");
-  static_assert(SMEM <= 160 * 1024, "the four partial half tiles fit the LDS");
+  static_assert(BM % HR == 0 && BN % 8 == 0, "a wave sums 16 rows of each pass, 8 columns a chunk");
+  static_assert(SMEM <= 160 * 1024, "the four partial 64-row tiles fit the LDS");
 };
 
 template <int MT, int NG, int D>
@@ -530,18 +531,18 @@ void k_gemm_qk(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
 
   float* red = reinterpret_cast<float*>(smem);  // [4 waves][64 rows][PROW]
   const int m0 = bm * S_::BM, n0 = bn * S_::BN;
-  static_for<2>([&](auto h_c) {
+  static_for<S_::NP>([&](auto h_c) {
     constexpr int h = decltype(h_c)::value;
-    if constexpr (h == 1) __syncthreads();  // every wave has summed the first half
+    if constexpr (h > 0) __syncthreads();  // every wave has summed the previous pass
 #pragma unroll
     for (int j = 0; j < NG; ++j)
 #pragma unroll
-      for (int i = h * MT / 2; i < (h + 1) * MT / 2; ++i) {
-        const int r = 16 * (i - h * MT / 2) + (lane & 15), cl = 16 * j + 4 * (lane >> 4);
+      for (int i = 4 * h; i < 4 * h + 4; ++i) {
+        const int r = 16 * (i - 4 * h) + (lane & 15), cl = 16 * j + 4 * (lane >> 4);
         *reinterpret_cast<v4f*>(red + (w * S_::HR + r) * S_::PROW + cl) = acc[j][i];
       }
     __syncthreads();
-    // wave w adds rows 16 w .. 16 w + 15 of this half over the four waves, 8 columns a chunk
+    // wave w adds rows 16 w .. 16 w + 15 of this pass over the four waves, 8 columns a chunk
     constexpr int CPR = S_::BN / 8;
 #pragma unroll
     for (int c = 0; c < (16 * CPR + 63) / 64; ++c) {
@@ -629,8 +630,8 @@ hipError_t run_qr(const void* ap, const void* wp, void* c, float* P, int M, int 
 }
 
 // Four-wave configurations (MT, NG, D): tiles 128 x 96 .. 128 x 144 (the widest holds its four
-// partial half tiles in 148 KiB of LDS).
-#define MX_QK_CONFIGS(X) X(8, 8, 2) X(8, 9, 1) X(8, 7, 2) X(8, 6, 2)
+// partial 64-row tiles in 148 KiB of LDS), and 128 x 48 four steps ahead for a single row tile.
+#define MX_QK_CONFIGS(X) X(8, 8, 2) X(8, 9, 1) X(8, 7, 2) X(8, 6, 2) X(8, 3, 4)
 
 std::atomic<uint64_t> g_qk_lds[8];
 

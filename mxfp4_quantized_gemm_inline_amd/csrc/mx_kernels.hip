@@ -1543,6 +1543,14 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   // 8448 x 7168 M=512: 236 tiles of 128 x 144, 34.3 -> 28.7 us (128 x 128: 264 tiles, two
   // rounds, 40.0 us). At K = 4224 (7168 x 4224 M=512, 256 tiles of 128 x 112) it only ties
   // the LDS kernel.
+  // One 128-row tile at long K (8448 x 7168 M=128): 128 x 48 tiles, four K quarters per CTA,
+  // four steps ahead, no K slices across CTAs (176 CTAs there: 23.2 -> 19.2 us against the
+  // inline 64 x 256 tile over three K slices; 128 x 32 tiles, 264 CTAs: 27.6 us).
+  const int64_t t48 = (N + 47) / 48;
+  if (M > 96 && M <= 128 && T >= 48 && t48 >= 150 && t48 <= 256 && qk_workspace_bytes(M, N, K, 1) <= ws_bytes) {
+    c.qo = true; c.qk = true; c.MT = 8; c.NG = 3; c.NBUF = 4; c.GM = 1; c.S = 1;
+    return c;
+  }
   if (M >= 512 && T >= 48 && qk_workspace_bytes(M, N, K, 1) <= ws_bytes) {
     for (int ng = 6; ng <= 9; ++ng) {
       const int64_t tiles = tm128 * ((N + 16 * ng - 1) / (16 * ng));

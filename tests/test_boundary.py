@@ -156,7 +156,10 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     # mid M: 64 x 64 tiles while the activation re-reads stay modest, K slices beyond
     assert mx.mx_a4w4_gemm_plan(128, 7168, 768) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
     assert mx.mx_a4w4_gemm_plan(100, 7168, 4224) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
-    assert "k_splitk_reduce" in mx.mx_a4w4_gemm_plan(128, 8448, 7168)
+    assert "k_splitk_reduce" in mx.mx_a4w4_gemm_plan(64, 8448, 7168)
+    # one 128-row tile at long K: 176 CTAs of 128 x 48, four waves over K quarters
+    assert mx.mx_a4w4_gemm_plan(128, 8448, 7168) == "k_prepare + k_gemm_qk<8, 3, 4> GM=1"
+    assert mx.mx_a4w4_gemm_plan(128, 8448, 7168, workspace_bytes=0).startswith("k_gemm_tile<")
     # split K only with a workspace; the streaming kernels never need one otherwise
     with_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168)
     no_ws = mx.mx_a4w4_gemm_plan(32, 1536, 7168, workspace_bytes=0)
@@ -258,6 +261,16 @@ def test_calibration_argument_errors():
     assert L.mx_calib_mfma_operands(MIS, 16384, 8, 16, sink, None) == mx.MX_ERR_ALIGN
     # 256 CTAs x 4 waves x 100 rounds x 64 MFMAs x 65,536 flop
     assert mx.mx_calib_mfma_operands_flops(256, 100) == 256 * 4 * 100 * 64 * 65536
+    clk = 0x80000
+    f = L.mx_calib_mfma_operands_clock
+    assert f(None, 16384, 8, 16, sink, clk, None) == mx.MX_ERR_NULL
+    assert f(A, 16384, 8, 16, None, clk, None) == mx.MX_ERR_NULL
+    assert f(A, 16384, 8, 16, sink, None, None) == mx.MX_ERR_NULL
+    assert f(A, 16383, 8, 16, sink, clk, None) == mx.MX_ERR_SHAPE
+    assert f(A, 16384, 0, 16, sink, clk, None) == mx.MX_ERR_SHAPE
+    assert f(A, 16384, 8, 0, sink, clk, None) == mx.MX_ERR_SHAPE
+    assert f(MIS, 16384, 8, 16, sink, clk, None) == mx.MX_ERR_ALIGN
+    assert f(A, 16384, 8, 16, sink, clk + 4, None) == mx.MX_ERR_ALIGN  # clocks hold uint64
 
 
 def test_gemm2_plan_picks_the_sweep_for_long_segments_at_short_k(monkeypatch):

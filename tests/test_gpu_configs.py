@@ -28,7 +28,7 @@ TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8,
 QO = [(2, 4, 8, 4, 4, 2), (2, 2, 4, 4, 4, 2), (2, 2, 4, 4, 5, 2), (1, 4, 8, 4, 3, 2)]
 # mirrors MX_QR_CONFIGS / MX_QK_CONFIGS in mx_gemm_qo.hip: (MT, NG, D)
 QR = [(8, 8, 2), (8, 9, 1)]
-QK = [(8, 8, 2), (8, 9, 1), (8, 7, 2), (8, 6, 2)]
+QK = [(8, 8, 2), (8, 9, 1), (8, 7, 2), (8, 6, 2), (8, 3, 4)]
 SWEEP_K = (256, 512, 768, 1024)  # the short-K sweep kernel's compiled step counts 2, 4, 6, 8
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
 K_TESTS = (4224, 768)  # 33 and 6 steps of 128
@@ -175,8 +175,8 @@ def test_four_wave_config(cfg, K, slices):
     range (T = 4, 5 (one wave with no step), 6, 33, 56 steps), added through LDS in wave order,
     with and without K slices across CTAs (FP32 partials added by the split-K reduce); on a
     ragged last row tile, a tile of fewer rows than one 64-row quad, several tile orders and
-    canary rows past M. Tile widths 96, 112 and 144 start at every byte offset within a weight
-    scale word, and at N = 768 the last 112- and 144-wide tiles are partial. Compared with the
+    canary rows past M. Tile widths 48, 96, 112 and 144 start at every byte offset within a
+    weight scale word, and at N = 768 the last 112- and 144-wide tiles are partial. Compared with the
     oracle (the sum order differs from the inline kernel's)."""
     torch = torch_or_skip()
     mx = lib_or_fail()

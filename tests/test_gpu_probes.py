@@ -42,6 +42,7 @@ DENSE = [
     ("x,8,9,1,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
     ("x,8,7,2,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
     ("x,8,6,2,8", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
+    ("x,8,3,4,1", 4224, (37, 300), lambda M, K: (M + 63) // 64 * 64 * K * 17 // 32),
     ("x,8,8,2,8,3", 7168, (37, 300),
      lambda M, K: ((M + 63) // 64 * 64 * K * 17 // 32 + 255) // 256 * 256 + 3 * M * N_P * 4),
 ]
