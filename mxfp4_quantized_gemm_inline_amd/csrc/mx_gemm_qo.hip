@@ -281,12 +281,14 @@ void k_gemm_qo(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
 template <int MT, int NG>
 struct RDWave {
   static constexpr int BM = 16 * MT, BN = 16 * NG;
-  static constexpr int MQ = MT / 4;                               // activation scale words
+  static constexpr bool AAL = MT % 4 == 0;                         // first row group % 4 == 0
+  static constexpr int MQL = AAL ? MT / 4 : (MT + 2) / 4 + 1;      // activation scale words loaded
+  static constexpr int MQ = (MT + 3) / 4;                          // ... after realignment
   static constexpr bool WAL = NG % 4 == 0;                         // g0 % 4 == 0 for every tile
   static constexpr int NQL = WAL ? NG / 4 : (NG + 2) / 4 + 1;      // weight scale words loaded
   static constexpr int NQ = (NG + 3) / 4;                          // ... after realignment
   static constexpr int JA = 64 / MT;                               // accumulator rows in the AGPRs
-  static_assert(MT % 4 == 0 && MT <= 16 && NG >= 1, "whole activation scale words");
+  static_assert(MT >= 1 && MT <= 16 && NG >= 1, "tile of 1..16 row groups");
 };
 
 // One wave's K steps t0 .. t1 - 1 of output tile (bm, bn) into acc (zeroed here). Ap holds the
@@ -300,19 +302,19 @@ __device__ __forceinline__ void rd_steps(v4f (&acc)[NG][MT], const uint8_t* __re
   const int T = steps_of(K);
   const int Mp = (M + 63) / 64 * 64;
   const int GAall = Mp / 16, GW = N / 16;
-  const int g0 = bn * NG;
-  const uint32_t vsh = (uint32_t)(g0 & 3);
+  const int g0 = bn * NG, a0 = bm * MT;
+  const uint32_t vsh = (uint32_t)(g0 & 3), vsha = (uint32_t)(a0 & 3);
   const uint8_t* pa[MT];
   const uint8_t* pw[NG];
-  const uint8_t* psa[R::MQ];
+  const uint8_t* psa[R::MQL];
   const uint8_t* psw[R::NQL];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) pa[i] = Ap + (size_t)min(bm * MT + i, GAall - 1) * T * 1024;
+  for (int i = 0; i < MT; ++i) pa[i] = Ap + (size_t)min(a0 + i, GAall - 1) * T * 1024;
 #pragma unroll
   for (int j = 0; j < NG; ++j) pw[j] = Wp + (size_t)min(g0 + j, GW - 1) * T * 1024;
 #pragma unroll
-  for (int q = 0; q < R::MQ; ++q)
-    psa[q] = Ap + payload_bytes(Mp, K) + (size_t)min(bm * R::MQ + q, GAall / 4 - 1) * T * 256;
+  for (int q = 0; q < R::MQL; ++q)
+    psa[q] = Ap + payload_bytes(Mp, K) + (size_t)min((a0 >> 2) + q, GAall / 4 - 1) * T * 256;
 #pragma unroll
   for (int q = 0; q < R::NQL; ++q)
     psw[q] = Wp + payload_bytes(N, K) + (size_t)min((g0 >> 2) + q, GW / 4 - 1) * T * 256;
@@ -320,7 +322,7 @@ __device__ __forceinline__ void rd_steps(v4f (&acc)[NG][MT], const uint8_t* __re
   // ring set s holds step t's operands for (t - t0) % S == s; steps past the last load the
   // last step again (never used)
   u32x4 a[S][MT], b[S][NG];
-  uint32_t sa[S][R::MQ], sb[S][R::NQL];
+  uint32_t sa[S][R::MQL], sb[S][R::NQL];
   const int tlast = max(t1 - 1, 0);
   auto load = [&](int t, auto s_c) {
     constexpr int s = decltype(s_c)::value;
@@ -331,7 +333,7 @@ __device__ __forceinline__ void rd_steps(v4f (&acc)[NG][MT], const uint8_t* __re
 #pragma unroll
     for (int j = 0; j < NG; ++j) b[s][j] = *reinterpret_cast<const u32x4*>(pw[j] + o);
 #pragma unroll
-    for (int q = 0; q < R::MQ; ++q) sa[s][q] = *reinterpret_cast<const uint32_t*>(psa[q] + os);
+    for (int q = 0; q < R::MQL; ++q) sa[s][q] = *reinterpret_cast<const uint32_t*>(psa[q] + os);
 #pragma unroll
     for (int q = 0; q < R::NQL; ++q) sb[s][q] = *reinterpret_cast<const uint32_t*>(psw[q] + os);
   };
@@ -341,7 +343,7 @@ __device__ __forceinline__ void rd_steps(v4f (&acc)[NG][MT], const uint8_t* __re
     for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.f, 0.f, 0.f, 0.f};
   auto mfmas = [&](auto s_c) {
     constexpr int s = decltype(s_c)::value;
-    uint32_t sw[R::NQ];
+    uint32_t sw[R::NQ], sv[R::MQ];
     static_for<R::NQ>([&](auto q_c) {
       constexpr int q = decltype(q_c)::value;
       if constexpr (R::WAL)
@@ -349,11 +351,18 @@ __device__ __forceinline__ void rd_steps(v4f (&acc)[NG][MT], const uint8_t* __re
       else  // bytes g0 % 4 + 4 q .. + 3 of the loaded words
         sw[q] = __builtin_amdgcn_alignbyte(sb[s][q + 1 < R::NQL ? q + 1 : R::NQL - 1], sb[s][q], vsh);
     });
+    static_for<R::MQ>([&](auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      if constexpr (R::AAL)
+        sv[q] = sa[s][q];
+      else  // the same for the activation row groups a0 ..
+        sv[q] = __builtin_amdgcn_alignbyte(sa[s][q + 1 < R::MQL ? q + 1 : R::MQL - 1], sa[s][q], vsha);
+    });
     static_for<NG>([&](auto j_c) {
       constexpr int j = decltype(j_c)::value;
       static_for<MT>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
-        mfma_fp4_tied<j & 3, i & 3, (j >= R::JA)>(acc[j][i], b[s][j], a[s][i], sw[j >> 2], sa[s][i >> 2]);
+        mfma_fp4_tied<j & 3, i & 3, (j >= R::JA)>(acc[j][i], b[s][j], a[s][i], sw[j >> 2], sv[i >> 2]);
       });
     });
   };
@@ -611,7 +620,7 @@ hipError_t run_qo(int id, const void* ap, const void* wp, void* c, int M, int N,
 // (72 accumulators, the ninth row of 16 columns in VGPRs) one step ahead, since two steps of
 // its operands leave too few registers for the rest. Measured at 8448 x 7168 M=2048: 128 x 144
 // two steps ahead 77.6 against 75.3 us one step ahead; 128 x 160 (80 accumulators) 114.9 us.
-#define MX_QR_CONFIGS(X) X(8, 8, 2) X(8, 9, 1)
+#define MX_QR_CONFIGS(X) X(8, 8, 2) X(8, 9, 1) X(9, 8, 1)
 
 template <int MT, int NG, int D>
 hipError_t run_qr(const void* ap, const void* wp, void* c, float* P, int M, int N, int K, int GM, int tail,

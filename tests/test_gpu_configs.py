@@ -27,7 +27,7 @@ TILE = [(1, 4, 4, 4, 2, 1), (2, 4, 4, 4, 2, 1), (1, 4, 8, 4, 1, 1), (2, 2, 4, 8,
 # mirrors MX_QO_CONFIGS in mx_gemm_qo.hip: (WM, WN, MT, NG, NBUF, OCC)
 QO = [(2, 4, 8, 4, 4, 2), (2, 2, 4, 4, 4, 2), (2, 2, 4, 4, 5, 2), (1, 4, 8, 4, 3, 2)]
 # mirrors MX_QR_CONFIGS / MX_QK_CONFIGS in mx_gemm_qo.hip: (MT, NG, D)
-QR = [(8, 8, 2), (8, 9, 1)]
+QR = [(8, 8, 2), (8, 9, 1), (9, 8, 1)]
 QK = [(8, 8, 2), (8, 9, 1), (8, 7, 2), (8, 6, 2), (8, 3, 4)]
 SWEEP_K = (256, 512, 768, 1024)  # the short-K sweep kernel's compiled step counts 2, 4, 6, 8
 N_TEST = 768          # 3 x 256: tail tiles for BN = 512
@@ -40,7 +40,7 @@ _cache = {}
 def _case(K):
     if K not in _cache:
         mx = lib_or_fail()
-        a = W.dense_activation(300, K, "plain", seed=21)
+        a = W.dense_activation(600, K, "plain", seed=21)
         w = W.dense_weight(N_TEST, K, seed=22)
         qw, sw = O.quantize_mx(w)
         qa, sa = O.quantize_mx(a)
@@ -146,12 +146,13 @@ def test_register_direct_config(cfg, K):
     4, 6, 33, 56 steps), on a ragged last row tile, a tile of fewer rows than one 64-row quad,
     several tile orders and canary rows past M. At N = 768 the 128 x 144 tiles start at every
     byte of a weight scale word (first groups 0, 9, 18, 27, ...) and the last one holds 48
-    columns. Compared with the oracle and bit for bit with the inline kernel (same
-    per-element K order)."""
+    columns; at M = 600 the 144 x 128 tiles start at every byte of an activation scale word
+    and the last one holds 24 rows. Compared with the oracle and bit for bit with the inline
+    kernel (same per-element K order)."""
     torch = torch_or_skip()
     mx = lib_or_fail()
     a, wp, exact = _case(K)
-    for M, gm in ((300, 8), (37, 1), (256, 3)):
+    for M, gm in ((300, 8), (37, 1), (256, 3), (600, 2)):
         full = torch.full((M + 5, N_TEST), -7.0, dtype=torch.bfloat16, device="cuda")
         ws = torch.empty((M + 63) // 64 * 64 * K * 17 // 32, dtype=torch.uint8, device="cuda")
         os.environ["MX_GEMM_CONFIG"] = "r," + ",".join(map(str, cfg)) + f",{gm}"
