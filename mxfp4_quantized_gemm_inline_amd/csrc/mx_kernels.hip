@@ -17,6 +17,8 @@
 #include <utility>
 
 #include "mx_device.h"
+
+#include <type_traits>
 #include "mx_internal.h"
 
 namespace mx {
@@ -171,7 +173,8 @@ struct StreamCTA {
   __device__ __forceinline__ void load_w(int tb) {
 #pragma unroll
     for (int i = 0; i < PD; ++i) {
-      // without the guard a wave with no step loads step 0 (unused)
+      // t1 - 1 >= 0 whenever K has a step, also for a wave with no step (t1 = t0 >= 1 then);
+      // the clamp at 0 only keeps the unguarded form's register allocation as measured
       const int t = kGuarded ? min(tb + i, t1 - 1) : max(0, min(tb + i, t1 - 1));
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -183,9 +186,11 @@ struct StreamCTA {
   }
 
   // Quantize rows [0, Mc) of this wave's blocks 4*t0 .. 4*t1-1 into LDS. `after_first`
-  // runs once, right after the first batch's loads are issued.
-  template <class Rows, class F>
-  __device__ __forceinline__ void quant(const Rows& rows, int Mc, F&& after_first) {
+  // runs once, right after the first batch's loads are issued. With several blocks per lane
+  // and a `weights_always` call (the weight loads issued on every path), a wave whose blocks
+  // fit one batch takes the single-batch form below.
+  template <class Rows, class F, class G = std::nullptr_t>
+  __device__ __forceinline__ void quant(const Rows& rows, int Mc, F&& after_first, G&& weights_always = nullptr) {
     const int nbw = 4 * S, nb = Mc * nbw;
     if (nb <= 0) {
       after_first();
@@ -193,6 +198,49 @@ struct StreamCTA {
     }
     const int q64 = 64 / nbw, r64 = 64 % nbw;
     int m = lane / nbw, r = lane % nbw;  // coordinates of block b = lane
+    if constexpr (kGuarded && !std::is_same_v<std::decay_t<G>, std::nullptr_t>) {
+      if (nb <= 64 * QB) {
+        // one batch: every load of it first (block coordinates computed branch-free), then
+        // the weight loads, and no branch around the stores, so the quantization waits for
+        // the activation loads alone; lanes past the last block write into the 16 spare
+        // bytes that end row Mc - 1 (never read)
+        uint32_t x[QB][16];
+        int mm[QB], rr[QB];
+        bool val[QB], spare[QB];
+        const uint16_t* src[QB];
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          const bool ok = j * 64 + lane < nb;
+          mm[j] = ok ? m : Mc - 1;
+          rr[j] = ok ? r : nbw - 1;
+          spare[j] = !ok;
+          src[j] = rows.ptr(mm[j], val[j]) + (size_t)(4 * t0 + rr[j]) * kBlock;
+          m += q64;
+          r += r64;
+          const int wrap = r >= nbw ? 1 : 0;
+          r -= wrap * nbw;
+          m += wrap;
+        }
+#pragma unroll
+        for (int j = 0; j < QB; ++j) load_block(src[j], x[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        weights_always();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) {
+          uint32_t q[4];
+          uint32_t sc = quant_block(x[j], q);
+          if (!val[j]) { q[0] = q[1] = q[2] = q[3] = 0u; sc = 0u; }
+          const int kbl = 4 * (t0 - ks0) + rr[j];  // block index within the slice
+          uint8_t* const row = aq + (size_t)mm[j] * RS;
+          uint8_t* const pq = spare[j] ? row + RS - 16 : row + kbl * 16;
+          uint8_t* const ps = spare[j] ? row + RS - 1 : as + (size_t)mm[j] * SB + kbl;
+          *reinterpret_cast<uint4*>(pq) = make_uint4(q[0], q[1], q[2], q[3]);
+          *ps = (uint8_t)sc;
+        }
+        return;
+      }
+    }
     bool first = true;
     for (int base = 0; base < nb; base += 64 * QB) {
       uint32_t x[QB][16];
@@ -317,11 +365,12 @@ __global__ __launch_bounds__(64 * WK) void k_gemm_stream(const uint16_t* __restr
   StreamCTA<MT, NG, WK, PD, QB> cta;
   cta.init(Wp, N, K, cg * NG, ks0, ks1, TS, min(M, 16 * MT), smem);
   const DenseRows rows{A, K};
-  // with one activation block per lane, unconditional, so that the quantization's wait covers
-  // the activation load alone (a load issued on one branch only makes the compiler wait for
-  // every load at the join)
+  // unconditional where the quantization should wait for the activation loads alone (a load
+  // issued on one branch only makes the compiler wait for every load at the join); a wave
+  // with no step then loads its last step's neighbour, never used
   using CTA = StreamCTA<MT, NG, WK, PD, QB>;
-  cta.quant(rows, M, [&] { if (!CTA::kGuarded || cta.S > 0) cta.load_w(cta.t0); });
+  cta.quant(rows, M, [&] { if (!CTA::kGuarded || cta.S > 0) cta.load_w(cta.t0); },
+            [&] { cta.load_w(cta.t0); });
   __syncthreads();
   v4f acc[NG][MT];
   cta.mma(M, false, acc);
