@@ -388,6 +388,7 @@ __device__ __forceinline__ void rd_steps(v4f (&acc)[NG][MT], const uint8_t* __re
 template <int MT, int NG>
 struct QRShape {
   static constexpr int BM = 16 * MT, BN = 16 * NG;
+  static constexpr bool kTail = MT == 8 && NG == 8;  // the shape that runs tail K slices
   static constexpr int CROW = BN * 2 + 16;  // bf16 staging row, padded by 16 bytes
   static constexpr int SMEM = BM * CROW;
 };
@@ -408,7 +409,9 @@ void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
   const int tiles_m = (M + S_::BM - 1) / S_::BM, tiles_n = (N + S_::BN - 1) / S_::BN;
   const int full = tiles_m * tiles_n - tail;
   int bm, bn, t0 = 0, t1 = T;
-  const bool part = (int)blockIdx.x >= full;
+  // only the 128 x 128 form runs tail slices; without that branch the others keep their
+  // accumulators in registers through the epilogue
+  const bool part = QRShape<MT, NG>::kTail && (int)blockIdx.x >= full;
   if (!part) {
     tile_coords(blockIdx.x, full, tiles_m, tiles_n, GM, bm, bn);
   } else {
@@ -421,17 +424,19 @@ void k_gemm_qr(const uint8_t* __restrict__ Ap, const uint8_t* __restrict__ Wp, u
   v4f acc[NG][MT];
   rd_steps<MT, NG, D>(acc, Ap, Wp, M, N, K, bm, bn, t0, t1, lane);
 
-  if (part) {
-    // FP32 partial tile, row-major: lane l holds rows 16 i + l % 16, columns 16 j + 4 (l / 16) + 0..3
-    float* Pt = P + (size_t)(blockIdx.x - full) * S_::BM * S_::BN;
+  if constexpr (S_::kTail) {
+    if (part) {
+      // FP32 partial tile, row-major: lane l holds rows 16 i + l % 16, columns 16 j + 4 (l / 16) + 0..3
+      float* Pt = P + (size_t)(blockIdx.x - full) * S_::BM * S_::BN;
 #pragma unroll
-    for (int j = 0; j < NG; ++j)
+      for (int j = 0; j < NG; ++j)
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int r = 16 * i + (lane & 15), cl = 16 * j + 4 * (lane >> 4);
-        *reinterpret_cast<v4f*>(Pt + r * S_::BN + cl) = acc[j][i];
-      }
-    return;
+        for (int i = 0; i < MT; ++i) {
+          const int r = 16 * i + (lane & 15), cl = 16 * j + 4 * (lane >> 4);
+          *reinterpret_cast<v4f*>(Pt + r * S_::BN + cl) = acc[j][i];
+        }
+      return;
+    }
   }
   // epilogue: stage the bf16 tile in this wave's LDS, then store whole rows, 16 bytes a lane
 #pragma unroll
@@ -718,6 +723,7 @@ hipError_t launch_gemm_qr(int MT, int NG, int D, int slices, const void* a, cons
   if (!qr_supported(MT, NG, D) || N % 64 != 0 || slices < 1) return hipErrorInvalidValue;
   const int64_t Mp = (M + 63) / 64 * 64;
   const int tail = slices > 1 ? qr_tail_tiles(M, N, MT, NG) : 0;
+  if (tail > 0 && !(MT == 8 && NG == 8)) return hipErrorInvalidValue;  // only 128 x 128 runs tail slices
   float* P = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (qo_act_bytes(M, K) + 255) / 256 * 256);
   hipError_t e = launch_prepare_rows(a, M, Mp, K, ws, st);
   if (e != hipSuccess) return e;

@@ -1603,19 +1603,18 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   const int64_t t256 = ((int64_t)M + 255) / 256 * ((N + 255) / 256);
   const int64_t t128 = ((int64_t)M + 127) / 128 * ((N + 127) / 128);
   // Slightly more 128 x 128 tiles than one wave per SIMD of the chip (8448 x 7168 at M=2048:
-  // 1056): the register-direct kernel on 72-accumulator tiles that fit one round: 144 x 128
-  // (990 tiles there: 75.0 -> 72.9 us; their 256-byte output rows are whole lines), else
-  // 128 x 144 (944 tiles there: 80.0 -> 75.0 us against 128 x 128 with the tail); else
-  // 128 x 128 with the tiles past one round in four K slices (90 -> 86 us there; with the
-  // whole last round 96 us, eight slices 93 us).
+  // 1056): the register-direct kernel on 72-accumulator tiles that fit one round: 128 x 144
+  // (944 tiles there: 80.0 -> 68.8 us against 128 x 128 with the tail), else 144 x 128
+  // (990 tiles there: 75.8 us); else 128 x 128 with the tiles past one round in four K
+  // slices (90 -> 86 us there; with the whole last round 96 us, eight slices 93 us).
   const int64_t tm128 = ((int64_t)M + 127) / 128;
+  if (T >= 16 && t128 > 1024 && tm128 * ((N + 143) / 144) <= 1024 && qr_workspace_bytes(M, N, K, 8, 9, 1) <= ws_bytes) {
+    c.qo = true; c.qr = true; c.MT = 8; c.NG = 9; c.NBUF = 1; c.GM = 8; c.S = 1;
+    return c;
+  }
   if (T >= 16 && t128 > 1024 && ((int64_t)M + 143) / 144 * ((N + 127) / 128) <= 1024 &&
       qr_workspace_bytes(M, N, K, 9, 8, 1) <= ws_bytes) {
     c.qo = true; c.qr = true; c.MT = 9; c.NG = 8; c.NBUF = 1; c.GM = 8; c.S = 1;
-    return c;
-  }
-  if (T >= 16 && t128 > 1024 && tm128 * ((N + 143) / 144) <= 1024 && qr_workspace_bytes(M, N, K, 8, 9, 1) <= ws_bytes) {
-    c.qo = true; c.qr = true; c.MT = 8; c.NG = 9; c.NBUF = 1; c.GM = 8; c.S = 1;
     return c;
   }
   if (T >= 16 && qr_tail_tiles(M, N, 8, 8) > 0 && qr_workspace_bytes(M, N, K, 8, 8, 4) <= ws_bytes) {
@@ -1775,6 +1774,9 @@ bool resolve_config(int M, int N, int K, size_t ws_bytes, GemmConfig& cfg) {
   if (ov > 0 && cfg.sweep && (!sweep_supported(steps_of(K), cfg.J) || N % 128 != 0)) return false;
   if (ov > 0 && cfg.qo && config_workspace(cfg, M, N, K) > ws_bytes) return false;
   if (ov > 0 && cfg.qr && cfg.S > steps_of(K)) return false;
+  // tail K slices run only on 128 x 128 tiles
+  if (ov > 0 && cfg.qr && cfg.S > 1 && !(cfg.MT == 8 && cfg.NG == 8) && qr_tail_tiles(M, N, cfg.MT, cfg.NG) > 0)
+    return false;
   if (ov > 0 && cfg.qk && 4 * cfg.S > steps_of(K)) return false;
   if (ov > 0 && cfg.tile && !cfg.qo && cfg.S > 1) {
     const int T = steps_of(K);

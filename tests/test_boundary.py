@@ -128,12 +128,12 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     # inline kernels run
     assert mx.mx_a4w4_gemm_plan(2048, 7168, 4224) == "k_prepare + k_gemm_qo<2, 4, 8, 4, 4, 2> GM=8"
     # 1056 tiles of 128 x 128, a little over one wave per SIMD: the register-direct kernel on
-    # 990 tiles of 144 x 128; 128 x 144 tiles when 144 x 128 ones do not fit one round (N =
-    # 8960: 1050 of 144 x 128, 1008 of 128 x 144); at 1188 tiles (M = 2304 at N = 8448) both
-    # still exceed it (1056, 1062), so 128 x 128 tiles run with the 164 past the first round
-    # in four K slices
-    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_prepare + k_gemm_qr<9, 8, 1> GM=8"
-    assert mx.mx_a4w4_gemm_plan(2048, 8960, 7168) == "k_prepare + k_gemm_qr<8, 9, 1> GM=8"
+    # 944 tiles of 128 x 144; 144 x 128 tiles when only those fit one round (M = 2304 at N =
+    # 8192: 1026 of 128 x 144, 1024 of 144 x 128); at 1188 tiles (M = 2304 at N = 8448) both
+    # still exceed it (1062, 1056), so 128 x 128 tiles run with the 164 past the first round in
+    # four K slices
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168) == "k_prepare + k_gemm_qr<8, 9, 1> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2304, 8192, 7168) == "k_prepare + k_gemm_qr<9, 8, 1> GM=8"
     assert mx.mx_a4w4_gemm_plan(2304, 8448, 7168) == \
         "k_prepare + k_gemm_qr<8, 8, 2> GM=8 tail=164x4 + k_qr_tail_reduce"
     # one CTA of four register-direct waves per tile, the narrowest tile that fits one round
@@ -149,7 +149,7 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     act_t = (2304 * 7168 * 17 // 32 + 255) // 256 * 256
     assert mx.mx_a4w4_gemm_workspace_bytes(2304, 8448, 7168) == act_t + 164 * 4 * 128 * 128 * 4
     assert mx.mx_a4w4_gemm_workspace_bytes(520, 8448, 7168) == 576 * 7168 * 17 // 32
-    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act) == "k_prepare + k_gemm_qr<9, 8, 1> GM=8"
+    assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act) == "k_prepare + k_gemm_qr<8, 9, 1> GM=8"
     assert mx.mx_a4w4_gemm_plan(2048, 8448, 7168, workspace_bytes=act - 1).startswith("k_gemm_tile<")
     # no room for the tail partials: the LDS quantize-once kernel
     assert mx.mx_a4w4_gemm_plan(2304, 8448, 7168, workspace_bytes=act_t) == \

@@ -71,14 +71,14 @@ def test_noalloc_rejects_plans_beyond_the_scratch():
 
 
 def test_noalloc_register_direct_plans():
-    """The register-direct plans through the scratch array: 2048 x 8448 at K = 2048 (990 tiles
-    of 144 x 128, one wave each), then 2048 x 1536 at K = 7168 (the four-wave kernel) over the
+    """The register-direct plans through the scratch array: 2048 x 8448 at K = 2048 (944 tiles
+    of 128 x 144, one wave each), then 2048 x 1536 at K = 7168 (the four-wave kernel) over the
     same bytes; bit for bit against mx_a4w4_gemm with its own workspace, and against the
     oracle. (The register-direct plan with tail K slices needs at least 129 x 4 FP32 partial
     tiles of 64 KiB, more than the array holds, so that plan is refused here.)"""
     torch = torch_or_skip()
     mx = lib_or_fail()
-    for M, N, K, kern in ((2048, 8448, 2048, "k_gemm_qr<9, 8, 1>"), (2048, 1536, 7168, "k_gemm_qk")):
+    for M, N, K, kern in ((2048, 8448, 2048, "k_gemm_qr<8, 9, 1>"), (2048, 1536, 7168, "k_gemm_qk")):
         need = mx.mx_a4w4_gemm_workspace_bytes(M, N, K)
         assert 0 < need <= mx.mx_noalloc_scratch_bytes()
         plan = mx.mx_a4w4_gemm_plan(M, N, K, need)
