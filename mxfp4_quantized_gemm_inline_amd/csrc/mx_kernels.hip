@@ -1628,12 +1628,15 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   // 8448 x 7168 M=512: 236 tiles of 128 x 144, 34.3 -> 28.7 us (128 x 128: 264 tiles, two
   // rounds, 40.0 us). At K = 4224 (7168 x 4224 M=512, 256 tiles of 128 x 112) it only ties
   // the LDS kernel.
-  // One 128-row tile at long K (8448 x 7168 M=128): 128 x 48 tiles, four K quarters per CTA,
-  // four steps ahead, no K slices across CTAs (176 CTAs there: 23.2 -> 19.2 us against the
-  // inline 64 x 256 tile over three K slices; 128 x 32 tiles, 264 CTAs: 27.6 us).
-  const int64_t t48 = (N + 47) / 48;
-  if (M > 96 && M <= 128 && T >= 48 && t48 >= 150 && t48 <= 256 && qk_workspace_bytes(M, N, K, 1) <= ws_bytes) {
-    c.qo = true; c.qk = true; c.MT = 8; c.NG = 3; c.NBUF = 4; c.GM = 1; c.S = 1;
+  // Few 128-row tiles at long K: 128 x 48 tiles, four K quarters per CTA, four steps ahead,
+  // no K slices across CTAs, when they number 128 .. 256 (one CTA per CU at most). 8448 x 7168
+  // M=128 (176 CTAs): 23.2 -> 19.2 us against the inline 64 x 256 tile over three K slices
+  // (128 x 32 tiles, 264 CTAs: 27.6 us); 7168 x 4224 M=128 (150): 16.3 -> 14.9 us against the
+  // inline 64 x 64 tile; 1536 x 7168 M=512 (128): 20.0 -> 19.4 us against the inline tile over
+  // four K slices. At K = 768 (7168 x 768 M=128 and 512) the inline kernels stay well ahead.
+  const int64_t t48 = tm128 * ((N + 47) / 48);
+  if (M > 96 && T >= 32 && t48 >= 128 && t48 <= 256 && qk_workspace_bytes(M, N, K, 1) <= ws_bytes) {
+    c.qo = true; c.qk = true; c.MT = 8; c.NG = 3; c.NBUF = 4; c.GM = (int)(tm128 < 4 ? tm128 : 4); c.S = 1;
     return c;
   }
   if (M >= 512 && T >= 48 && qk_workspace_bytes(M, N, K, 1) <= ws_bytes) {

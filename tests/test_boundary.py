@@ -154,11 +154,16 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     # no room for the tail partials: the LDS quantize-once kernel
     assert mx.mx_a4w4_gemm_plan(2304, 8448, 7168, workspace_bytes=act_t) == \
         "k_prepare + k_gemm_qo<2, 2, 4, 4, 4, 2> GM=8"
-    # N = 1536 at M = 512 gives 48 tiles of 128 x 128: too few, K slices keep it inline
-    assert "k_gemm_qo" not in mx.mx_a4w4_gemm_plan(512, 1536, 7168)
+    # N = 1536 at M = 512 gives 48 tiles of 128 x 128, too few for the LDS kernel; 128 tiles of
+    # 128 x 48 run four waves each over K quarters
+    assert mx.mx_a4w4_gemm_plan(512, 1536, 7168) == "k_prepare + k_gemm_qk<8, 3, 4> GM=4"
+    assert mx.mx_a4w4_gemm_plan(384, 1536, 7168).startswith("k_gemm_tile<")   # 96 such tiles
     # mid M: 64 x 64 tiles while the activation re-reads stay modest, K slices beyond
     assert mx.mx_a4w4_gemm_plan(128, 7168, 768) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
-    assert mx.mx_a4w4_gemm_plan(100, 7168, 4224) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(100, 7168, 4224) == "k_prepare + k_gemm_qk<8, 3, 4> GM=1"
+    assert mx.mx_a4w4_gemm_plan(100, 7168, 4224, workspace_bytes=0) == "k_gemm_tile<1, 4, 4, 1, 2, 2> GM=8"
+    assert mx.mx_a4w4_gemm_plan(96, 7168, 4224).startswith("k_gemm_")   # not the four-wave kernel
+    assert "k_gemm_qk" not in mx.mx_a4w4_gemm_plan(96, 7168, 4224)
     assert "k_splitk_reduce" in mx.mx_a4w4_gemm_plan(64, 8448, 7168)
     # one 128-row tile at long K: 176 CTAs of 128 x 48, four waves over K quarters
     assert mx.mx_a4w4_gemm_plan(128, 8448, 7168) == "k_prepare + k_gemm_qk<8, 3, 4> GM=1"
