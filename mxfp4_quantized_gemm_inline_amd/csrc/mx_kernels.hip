@@ -1548,12 +1548,20 @@ GemmConfig select_config(int M, int N, int K, size_t ws_bytes) {
   };
   // long K: the tiled kernel with K slices when the caller offers room for the partials
   const bool split_ok = T >= 16 && (size_t)2 * M * N * 4 <= ws_bytes;
-  // 17..32 rows against many column groups and long K (8448 x 7168): 64 x 256 tiles over four
-  // K slices beat the streaming kernel, whose 132 CTAs leave half the chip idle (16.4 against
-  // 19.5 us, cold)
-  if (M > 16 && M <= 32 && G >= 512 && T >= 32 && (size_t)4 * M * N * 4 <= ws_bytes) {
-    c.tile = true; c.WM = 1; c.WN = 4; c.MT = 4; c.NG = 4; c.PF = 2; c.GM = 8; c.OCC = 2; c.S = 4;
-    return c;
+  // 17..32 rows against many column groups and long K (8448 x 7168): 64 x 256 tiles over K
+  // slices beat the streaming kernel, whose 132 CTAs leave half the chip idle (16.4 against
+  // 19.5 us, cold). The most slices (4 .. 8) whose CTAs still fit one per CU: at 8448 x 7168
+  // M=32, 33 tiles x 7 slices of 8 steps, 16.1 -> 14.2 us against four slices (five: 15.7,
+  // six: 15.0; eight, 264 CTAs: 18.7 us).
+  if (M > 16 && M <= 32 && G >= 512 && T >= 32) {
+    const int64_t tiles = (N + 255) / 256;
+    int sk = (int)std::max<int64_t>(4, std::min<int64_t>(8, 256 / tiles));
+    sk = std::min(sk, T / 6);
+    while (sk > 4 && (size_t)sk * M * N * 4 > ws_bytes) --sk;
+    if ((size_t)sk * M * N * 4 <= ws_bytes) {
+      c.tile = true; c.WM = 1; c.WN = 4; c.MT = 4; c.NG = 4; c.PF = 2; c.GM = 8; c.OCC = 2; c.S = sk;
+      return c;
+    }
   }
   if (M <= 32 || (M <= 128 && G <= 96 && !split_ok)) {
     // weight-streaming kernel: the weight is read once, straight into registers

@@ -165,6 +165,13 @@ def test_gemm_plan_names_the_selected_kernel(monkeypatch):
     assert mx.mx_a4w4_gemm_plan(96, 7168, 4224).startswith("k_gemm_")   # not the four-wave kernel
     assert "k_gemm_qk" not in mx.mx_a4w4_gemm_plan(96, 7168, 4224)
     assert "k_splitk_reduce" in mx.mx_a4w4_gemm_plan(64, 8448, 7168)
+    # 17..32 rows at 8448 x 7168: 64 x 256 tiles in as many K slices as fit one CTA per CU (33 x 7)
+    assert mx.mx_a4w4_gemm_plan(32, 8448, 7168) == "k_gemm_tile<1, 4, 4, 4, 2, 2> GM=8 S=7 + k_splitk_reduce"
+    assert mx.mx_a4w4_gemm_plan(17, 8448, 7168) == "k_gemm_tile<1, 4, 4, 4, 2, 2> GM=8 S=7 + k_splitk_reduce"
+    assert mx.mx_a4w4_gemm_plan(32, 8448, 7168, workspace_bytes=4 * 32 * 8448 * 4) == \
+        "k_gemm_tile<1, 4, 4, 4, 2, 2> GM=8 S=4 + k_splitk_reduce"
+    assert mx.mx_a4w4_gemm_plan(32, 16384, 7168) == "k_gemm_tile<1, 4, 4, 4, 2, 2> GM=8 S=4 + k_splitk_reduce"
+    assert mx.mx_a4w4_gemm_plan(32, 8448, 7168, workspace_bytes=0).startswith("k_gemm_stream<")
     # one 128-row tile at long K: 176 CTAs of 128 x 48, four waves over K quarters
     assert mx.mx_a4w4_gemm_plan(128, 8448, 7168) == "k_prepare + k_gemm_qk<8, 3, 4> GM=1"
     assert mx.mx_a4w4_gemm_plan(128, 8448, 7168, workspace_bytes=0).startswith("k_gemm_tile<")
