@@ -152,3 +152,28 @@ def test_all_zero_and_negative_zero_blocks():
     c = host_bits(mx.mx_a4w4_gemm(dev_bf16(a), prepared(name), N))
     torch.cuda.synchronize()
     assert np.all(O.bf16_to_f64(c) == 0.0)
+
+
+# Shapes off the benchmark sweep that take the size-dependent choices: 17..32 rows against many
+# column groups at a K whose slices are uneven (N=8192, K=4096: five slices of 7, 7, 7, 7 and
+# 4 steps), and the four-wave 128 x 48 tiles over two and three row tiles.
+OFF_SWEEP = [
+    (24, 8192, 4096, "k_gemm_tile<1, 4, 4, 4, 2, 2> GM=8 S=5 + k_splitk_reduce"),
+    (200, 4096, 4224, "k_prepare + k_gemm_qk<8, 3, 4> GM=2"),
+    (384, 2048, 7168, "k_prepare + k_gemm_qk<8, 3, 4> GM=3"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,plan", OFF_SWEEP, ids=[f"{m}x{n}x{k}" for m, n, k, _ in OFF_SWEEP])
+def test_size_dependent_plans_match_oracle(M, N, K, plan):
+    torch = torch_or_skip()
+    mx = lib_or_fail()
+    assert mx.mx_a4w4_gemm_plan(M, N, K) == plan
+    w = W.dense_weight(N, K)
+    a = W.dense_activation(M, K, "zero_blocks")
+    c = host_bits(mx.mx_a4w4_gemm(dev_bf16(a), mx.mx_prepare_weight(dev_bf16(w)), N))
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    qa, sa = O.quantize_mx(a[rows])
+    qw, sw = O.quantize_mx(w)
+    check_gemm(c[rows], O.gemm_from_mx(qa, sa, qw, sw), what=f"{M}x{N}x{K}")
